@@ -1,0 +1,204 @@
+/*
+ * kvshare.h — C ABI of the shared-KV attention library (libkvshare.so), gfx950.
+ *
+ * Several task-specific decoders attend over ONE paged KV cache that a frozen
+ * base model wrote once.  In the notation of "ICaRus: Identical Cache Reuse for
+ * Efficient Multi-Model Inference" (Method / overall framework), a logical
+ * encoder E_base produces K_{1:i}, V_{1:i} and every task decoder D_task
+ * computes x_{i+1} = D(x_i, K_{1:i}, V_{1:i}) over that same cache; Key design 3
+ * of that page concatenates the query heads of all parties that read the same
+ * KV so the KV is read once.  "PrefillShare: A Shared Prefill Module for KV Reuse
+ * in Multi-LLM Disaggregated Serving" (sections 3.3 and 7) extends a cached
+ * prefix by a partial prefill over the new tokens only, and keeps the KV in
+ * fixed-size blocks (pages).
+ *
+ * Three operations:
+ *   kv_pool_append         write new K/V rows into pages        (the cache "store")
+ *   shared_kv_decode       N decoders x G GQA heads, one KV read (decode attention)
+ *   partial_prefill_extend append a chunk, then causal attention of the chunk
+ *                          over cached prefix + chunk           (partial prefill)
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions common to every entry point
+ * ---------------------------------------------------------------------------
+ *  - Element type of K, V, q and out is bfloat16 (raw 16-bit storage).  Softmax
+ *    and accumulation are done in fp32; outputs are rounded to bf16
+ *    round-to-nearest-even.
+ *  - Every pointer argument except `pool` and the `*_out`-less scalars is a
+ *    DEVICE pointer.  `pool` points to a host struct whose `data` member is a
+ *    device pointer.  The caller allocates and owns every buffer; the library
+ *    never allocates, frees or synchronizes, and keeps no per-call state.
+ *    All work is enqueued asynchronously on `stream` (NULL = null stream).
+ *  - Return value: KVS_OK (0) or a negative status.  On a negative status other
+ *    than KVS_EHIP nothing was enqueued.  kvs_last_error() returns a
+ *    thread-local message describing the last non-zero status.
+ *  - Host-side checks: null pointers, page_size == 16, head_dim in {64, 128},
+ *    num_q_heads % num_kv_heads == 0, layer in range, positive sizes,
+ *    max_seq_len <= bt_stride * 16, workspace size.
+ *  - Device-resident values (page ids, seq_lens, cu_new) are not visible to the
+ *    host without a sync.  The kernels check them: a page id outside
+ *    [0, num_pages), a length above the host-given bound, or an inconsistent
+ *    cu_new never leads to an out-of-bounds access.  The offending
+ *    page/session is skipped (its output is unspecified) and, when `dev_status`
+ *    is non-NULL, the bits below are OR-ed into *dev_status (a device int32 the
+ *    caller zeroes; read it after the stream completes).
+ *
+ * ---------------------------------------------------------------------------
+ * Paged pool layout (bf16 elements, page size 16, head dim D in {64, 128})
+ * ---------------------------------------------------------------------------
+ *  The pool holds `num_layers` independent layer slices of `num_pages` physical
+ *  pages; each page holds 16 consecutive token slots for all KV heads.  One
+ *  (layer, page, head) TILE is 2*16*D elements, K part first, then V part:
+ *
+ *    tile(layer, page, head) = ((layer*num_pages + page)*num_kv_heads + head) * 32*D
+ *    K(t, d) = tile + ((d/32)*64 + ((d%32)/8)*16 + t) * 8 + d%8
+ *    V(t, d) = tile + 16*D + ((d/32)*64 + (t/4)*16 + d%16) * 8 + ((d/16)%2)*4 + t%4
+ *
+ *  t is the slot in the page (0..15), d the head-dim index.  Each 1 KiB group
+ *  (fixed d/32) is exactly the set of 64 16-byte lane operands of one gfx950
+ *  16x16 bf16 matrix-core step, so a wave reads a K or V tile with fully
+ *  contiguous 16-byte loads and needs no transpose.  A tile is 8 KiB at D=128.
+ *
+ *  Logical token position p of session b lives in page block_table[b*bt_stride
+ *  + p/16], slot p%16.  Block table entries past ceil(len/16) are never read
+ *  (-1 is allowed there).  The block table is shared by all layers and by all
+ *  decoders of a session: the cache is stored once per session whatever the
+ *  number of decoders (PrefillShare, section 4, memory model Eqs. 8-9, shared
+ *  term not multiplied by N).  Slots past a session's length are never read
+ *  with non-zero weight, whatever they hold (NaN included).
+ */
+#ifndef KVSHARE_H
+#define KVSHARE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  KVS_OK = 0,
+  KVS_EINVAL = -1,       /* null pointer, non-positive size, bad enum value   */
+  KVS_ERANGE = -2,       /* a bound exceeds the block table / pool capacity   */
+  KVS_EWORKSPACE = -3,   /* workspace missing or smaller than required        */
+  KVS_EUNSUPPORTED = -4, /* page_size != 16, head_dim not in {64,128}, ...    */
+  KVS_EHIP = -5          /* a HIP launch failed; see kvs_last_error()         */
+};
+
+/* Bits OR-ed into *dev_status by the kernels. */
+enum {
+  KVS_DEV_BAD_PAGE = 1,  /* block-table entry outside [0, num_pages)          */
+  KVS_DEV_BAD_LEN = 2,   /* seq_lens / cu_new beyond the host-given bounds    */
+};
+
+typedef struct kvs_pool {
+  void* data;            /* device pointer to kvs_pool_bytes(...) bytes       */
+  int32_t num_layers;
+  int32_t num_pages;     /* physical pages per layer                          */
+  int32_t num_kv_heads;
+  int32_t head_dim;      /* 64 or 128                                          */
+  int32_t page_size;     /* must be 16                                         */
+} kvs_pool;
+
+/* Bytes needed by a pool of the given shape (0 if a size is non-positive). */
+size_t kvs_pool_bytes(int32_t num_layers, int32_t num_pages, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t page_size);
+
+/*
+ * kv_pool_append — write the K/V rows of new tokens into their page slots.
+ *
+ * The cache-store step of the base prefill: PrefillShare (section 4, base
+ * prefill produces C_base; section 3.3, partial prefill appends the new tokens'
+ * KV) and ICaRus (overall framework: E_base writes the KV that all decoders
+ * read).  Pure data movement: the result is bit-exact.
+ *
+ *  k_new, v_new  bf16 [total_new][num_kv_heads][head_dim], sessions' rows
+ *                concatenated; session b owns rows cu_new[b] .. cu_new[b+1]-1.
+ *  cu_new        int32 [batch+1], cu_new[0] = 0, non-decreasing,
+ *                cu_new[batch] = total_new.
+ *  block_table   int32 [batch][bt_stride] physical page ids.
+ *  seq_lens      int32 [batch]: tokens already resident BEFORE this call; new
+ *                row j of session b goes to logical position seq_lens[b] + j.
+ *  max_new       host bound on cu_new[b+1]-cu_new[b] (>= 1).
+ *  max_seq_len   host bound on seq_lens[b] + new tokens of b (<= bt_stride*16).
+ *  Only the destination slots are written; every other pool byte is unchanged.
+ *  Two new rows must never map to the same physical slot (caller's duty).
+ */
+int kv_pool_append(const kvs_pool* pool, int32_t layer, const void* k_new, const void* v_new,
+                   const int32_t* cu_new, const int32_t* block_table, int32_t bt_stride,
+                   const int32_t* seq_lens, int32_t batch, int32_t total_new, int32_t max_new,
+                   int32_t max_seq_len, int32_t* dev_status, hipStream_t stream);
+
+/* Workspace bytes needed by shared_kv_decode for these bounds. */
+size_t shared_kv_decode_workspace_bytes(int32_t batch, int32_t num_decoders, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_seq_len);
+
+/*
+ * shared_kv_decode — one decode step of N decoders over one shared cache.
+ *
+ * ICaRus, Method / overall framework (x_{i+1} = D(x_i, K_{1:i}, V_{1:i}) with
+ * the KV written by E_base) and Key design 3 (query heads of every party that
+ * reads the same KV are concatenated along the head dimension, so the KV is
+ * read once).  For session b, decoder n, query head h (KV head g = h / G,
+ * G = num_q_heads / num_kv_heads):
+ *     out[b,n,h,:] = sum_t softmax_t(scale * q[b,n,h,:] . K_g[t,:]) V_g[t,:],
+ *     t = 0 .. seq_lens[b]-1;   out = 0 when seq_lens[b] == 0.
+ * All N*G query rows of a KV head are processed together, so every page is read
+ * from memory once per call, independent of N.  Decode only reads the pool.
+ *
+ *  q, out        bf16 [batch][num_decoders][num_q_heads][head_dim].
+ *  seq_lens      int32 [batch], tokens attended (the current token's KV is
+ *                appended with kv_pool_append before the call).
+ *  max_seq_len   host bound on seq_lens[b]; sizes the launch.
+ *  scale         softmax scale (1/sqrt(head_dim) for the usual attention).
+ *  workspace     device buffer of >= shared_kv_decode_workspace_bytes(...)
+ *                bytes, ZERO-FILLED before its first use.  Every call leaves its
+ *                counters at zero again, so a workspace may be reused by later
+ *                calls on the same stream; calls that overlap in time must use
+ *                different workspaces.
+ */
+int shared_kv_decode(const kvs_pool* pool, int32_t layer, const void* q, void* out,
+                     const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                     int32_t batch, int32_t num_decoders, int32_t num_q_heads,
+                     int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
+                     int32_t* dev_status, hipStream_t stream);
+
+/*
+ * partial_prefill_extend — cached-prefix extension over the new tokens only.
+ *
+ * PrefillShare, sections 3.3 and 7: on a cache hit only the new tokens are
+ * prefilled against the cached prefix; section 4: prefill
+ * (y_1, C_n) = F(X, empty) is the case with an empty prefix.  First appends the
+ * chunk's K/V exactly as kv_pool_append does, then for new row i of session b
+ * (absolute position p = seq_lens[b] + i) and query head h:
+ *     out[cu_new[b]+i, h, :] = sum_{t<=p} softmax_t(scale * q . K_g[t,:]) V_g[t,:]
+ * i.e. full attention to the prefix and causal (diagonal included) within the
+ * chunk.
+ *
+ *  q, out        bf16 [total_new][num_q_heads][head_dim].
+ *  k_new, v_new  bf16 [total_new][num_kv_heads][head_dim].
+ *  cu_new        int32 [batch+1] as for kv_pool_append.
+ *  seq_lens      int32 [batch], prefix length of each session before the call.
+ *  max_new       host bound on any session's new-token count (>= 1).
+ *  max_seq_len   host bound on seq_lens[b] + new tokens of b (<= bt_stride*16).
+ */
+int partial_prefill_extend(const kvs_pool* pool, int32_t layer, const void* q, const void* k_new,
+                           const void* v_new, void* out, const int32_t* cu_new,
+                           const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                           int32_t batch, int32_t num_q_heads, int32_t total_new, int32_t max_new,
+                           int32_t max_seq_len, float scale, int32_t* dev_status,
+                           hipStream_t stream);
+
+/* Thread-local description of the last non-zero status returned on this thread. */
+const char* kvs_last_error(void);
+
+/* Library version string. */
+const char* kvs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVSHARE_H */

@@ -1,0 +1,384 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each check ties the oracle to a fact fixed outside it: IEEE bf16 decoding, a
+brute-force attention over the logical sequence (no pages), the library routine
+the special case reduces to (torch's scaled_dot_product_attention in float64 on
+the CPU), closed forms of softmax attention, and the invariants the pages imply
+(ICaRus, Key designs 2-3: every decoder reads the same bit-identical KV, so its
+output depends only on its own query and that KV; PrefillShare, section 3.3:
+extending a cached prefix by the new tokens gives what a full prefill of the
+whole sequence gives).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from cross_model_shared_amd import workload as wlmod
+
+RNG = np.random.default_rng
+
+
+def bits(rng, shape, std=1.0):
+    return wlmod.draw_bf16(rng, shape, std)
+
+
+def poison_pool(shape):
+    # 1024.0 in bf16: any slot read by mistake dominates the result
+    return np.full(shape.elems, 0x4480, dtype=np.uint16)
+
+
+def build_session_pool(lens, Hkv, D, seed, layers=1, layer=0):
+    """Pool + block table holding logical K/V of each session (via oracle.append)."""
+    bt, num_pages = wlmod.build_block_table(lens, seed)
+    shape = oracle.PoolShape(layers, num_pages, Hkv, D)
+    rng = RNG(seed)
+    K = [bits(rng, (L, Hkv, D)) for L in lens]
+    V = [bits(rng, (L, Hkv, D)) for L in lens]
+    kk, cu = wlmod.concat_rows(K)
+    vv, _ = wlmod.concat_rows(V)
+    pool = oracle.append(poison_pool(shape), shape, layer, kk, vv, cu, bt,
+                         np.zeros(len(lens), np.int32))
+    return shape, pool, bt, K, V
+
+
+def brute_attention(q, K, V, scale):
+    """Textbook softmax attention with Python floats (one row)."""
+    L, D = len(K), len(q)
+    if L == 0:
+        return [0.0] * D
+    s = [scale * math.fsum(q[d] * K[t][d] for d in range(D)) for t in range(L)]
+    mx = max(s)
+    w = [math.exp(x - mx) for x in s]
+    z = math.fsum(w)
+    return [math.fsum(w[t] * V[t][d] for t in range(L)) / z for d in range(D)]
+
+
+def sdpa(q, K, V, scale, mask=None):
+    """torch SDPA in float64 on the CPU. q [R, Hq, D]; K, V [L, Hq, D]."""
+    qt = torch.from_numpy(q).permute(1, 0, 2).unsqueeze(0)
+    kt = torch.from_numpy(K).permute(1, 0, 2).unsqueeze(0)
+    vt = torch.from_numpy(V).permute(1, 0, 2).unsqueeze(0)
+    m = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
+    return o.squeeze(0).permute(1, 0, 2).numpy()
+
+
+# ---------------------------------------------------------------------------
+# bf16 decoding (IEEE-754 binary32 with the low 16 bits zero)
+# ---------------------------------------------------------------------------
+def test_bf16_decoding_known_patterns():
+    pats = np.array([0x3F80, 0xC000, 0x3E80, 0x0000, 0x8000, 0x7F80, 0xFF80, 0x0001, 0x4049],
+                    dtype=np.uint16)
+    got = oracle.bf16_to_f64(pats)
+    want = [1.0, -2.0, 0.25, 0.0, -0.0, math.inf, -math.inf, 2.0 ** -133, 3.140625]
+    assert list(got) == want
+    assert math.copysign(1.0, got[4]) == -1.0
+    assert np.isnan(oracle.bf16_to_f64(np.array([0x7FC0], np.uint16)))[0]
+
+
+def test_input_rounding_is_nearest_even():
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa (1.0) wins
+    x = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -9), 1.0 + 2 ** -8 + 2 ** -20],
+                 dtype=np.float32)
+    got = oracle.bf16_to_f64(wlmod.f32_to_bf16_bits(x))
+    assert list(got) == [1.0, 1.0 + 2 ** -6, -1.0, 1.0 + 2 ** -7]
+
+
+# ---------------------------------------------------------------------------
+# Pool index map: documented properties
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("D", [64, 128])
+def test_layout_is_a_bijection_per_tile(D):
+    ks = sorted(oracle.k_offset(t, d) for t in range(16) for d in range(D))
+    vs = sorted(oracle.v_offset(t, d) for t in range(16) for d in range(D))
+    assert ks == list(range(16 * D))
+    assert vs == list(range(16 * D))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_layout_lane_operand_runs(D):
+    # K: a run of 8 head-dim values of one slot is 16 contiguous bytes
+    for t in range(16):
+        for d0 in range(0, D, 8):
+            offs = [oracle.k_offset(t, d0 + c) for c in range(8)]
+            assert offs == list(range(offs[0], offs[0] + 8)) and offs[0] % 8 == 0
+    # V: 4 consecutive slots of one head-dim value are 8 contiguous bytes
+    for d in range(D):
+        for t0 in range(0, 16, 4):
+            offs = [oracle.v_offset(t0 + c, d) for c in range(4)]
+            assert offs == list(range(offs[0], offs[0] + 4)) and offs[0] % 4 == 0
+    # each 32-wide slab of the head dim occupies its own 1 KiB (512 elements)
+    for t in range(16):
+        for d in range(D):
+            assert oracle.k_offset(t, d) // 512 == d // 32
+            assert oracle.v_offset(t, d) // 512 == d // 32
+
+
+def test_tiles_do_not_overlap():
+    shape = oracle.PoolShape(2, 3, 2, 64)
+    starts = [oracle.tile_start(l, p, h, 3, 2, 64) for l in range(2) for p in range(3)
+              for h in range(2)]
+    assert starts == [i * 2 * 16 * 64 for i in range(12)]
+    assert shape.elems == 12 * 2 * 16 * 64
+
+
+# ---------------------------------------------------------------------------
+# Append / gather
+# ---------------------------------------------------------------------------
+def test_append_then_gather_roundtrip():
+    lens = [37, 16, 1, 50]
+    shape, pool, bt, K, V = build_session_pool(lens, 2, 64, seed=5)
+    for b, L in enumerate(lens):
+        Kg, Vg = oracle.gather(pool, shape, 0, bt[b], L)
+        assert np.array_equal(Kg, oracle.bf16_to_f64(K[b]))
+        assert np.array_equal(Vg, oracle.bf16_to_f64(V[b]))
+
+
+def test_append_split_equals_one_shot_and_touches_only_its_slots():
+    rng = RNG(11)
+    lens = [40, 23]
+    Hkv, D = 2, 64
+    bt, num_pages = wlmod.build_block_table(lens, 7)
+    shape = oracle.PoolShape(2, num_pages, Hkv, D)
+    base = bits(rng, (shape.elems,))           # arbitrary prior contents
+    K = [bits(rng, (L, Hkv, D)) for L in lens]
+    V = [bits(rng, (L, Hkv, D)) for L in lens]
+    kk, cu = wlmod.concat_rows(K)
+    vv, _ = wlmod.concat_rows(V)
+    one = oracle.append(base, shape, 1, kk, vv, cu, bt, np.zeros(2, np.int32))
+    # same rows in two calls: first 17 / 5 rows, then the rest
+    cut = [17, 5]
+    ka, cua = wlmod.concat_rows([K[b][:cut[b]] for b in range(2)])
+    va, _ = wlmod.concat_rows([V[b][:cut[b]] for b in range(2)])
+    kb, cub = wlmod.concat_rows([K[b][cut[b]:] for b in range(2)])
+    vb, _ = wlmod.concat_rows([V[b][cut[b]:] for b in range(2)])
+    two = oracle.append(base, shape, 1, ka, va, cua, bt, np.zeros(2, np.int32))
+    two = oracle.append(two, shape, 1, kb, vb, cub, bt, np.array(cut, np.int32))
+    assert np.array_equal(one, two)
+    # exactly the destination elements changed (layer 0 untouched, spares untouched)
+    written = np.zeros(shape.elems, bool)
+    for b, L in enumerate(lens):
+        for p in range(L):
+            for h in range(Hkv):
+                for d in range(D):
+                    for which in (0, 1):
+                        written[shape.slot_index(1, bt[b, p // 16], h, p % 16, d, which)] = True
+    assert written.sum() == 2 * sum(lens) * Hkv * D
+    assert np.array_equal(one[~written], base[~written])
+
+
+# ---------------------------------------------------------------------------
+# Decode: brute force, library routine, closed forms, invariants
+# ---------------------------------------------------------------------------
+def test_tiny_decode_matches_brute_force_over_logical_sequence():
+    wl = wlmod.make_workload("tiny")
+    shape, pool, bt, K, V = build_session_pool(wl.lens, wl.num_kv_heads, wl.head_dim, seed=0)
+    q = wlmod.decode_q(wl)
+    got = oracle.decode(pool, shape, 0, q, bt, np.array(wl.lens), wl.scale)
+    qf = oracle.bf16_to_f64(q)
+    G = wl.group
+    for b in range(wl.batch):
+        Kf = oracle.bf16_to_f64(K[b]).tolist()
+        Vf = oracle.bf16_to_f64(V[b]).tolist()
+        for n in range(wl.num_decoders):
+            for h in range(wl.num_q_heads):
+                g = h // G
+                want = brute_attention(qf[b, n, h].tolist(), [r[g] for r in Kf],
+                                       [r[g] for r in Vf], wl.scale)
+                assert np.max(np.abs(got[b, n, h] - want)) < 1e-12
+
+
+@pytest.mark.parametrize("lens,N,Hkv,G,D", [([200, 256], 2, 2, 4, 64), ([1, 17, 33], 3, 2, 5, 128),
+                                             ([64], 1, 1, 1, 64)])
+def test_decode_matches_torch_sdpa(lens, N, Hkv, G, D):
+    shape, pool, bt, K, V = build_session_pool(lens, Hkv, D, seed=len(lens) + D)
+    rng = RNG(3)
+    q = bits(rng, (len(lens), N, Hkv * G, D))
+    scale = 1.0 / math.sqrt(D)
+    got = oracle.decode(pool, shape, 0, q, bt, np.array(lens), scale)
+    qf = oracle.bf16_to_f64(q)
+    for b, L in enumerate(lens):
+        Kr = np.repeat(oracle.bf16_to_f64(K[b]), G, axis=1)   # head h reads KV head h // G
+        Vr = np.repeat(oracle.bf16_to_f64(V[b]), G, axis=1)
+        for n in range(N):
+            want = sdpa(qf[b, n][None], Kr, Vr, scale)[0]
+            assert np.max(np.abs(got[b, n] - want)) < 1e-12
+
+
+def _single(K, V, q, scale):
+    return oracle.attend(oracle.bf16_to_f64(q), oracle.bf16_to_f64(K), oracle.bf16_to_f64(V), scale)
+
+
+def test_closed_form_single_token_returns_v():
+    rng = RNG(1)
+    K, V, q = bits(rng, (1, 64)), bits(rng, (1, 64)), bits(rng, (64,))
+    assert np.array_equal(_single(K, V, q, 0.125), oracle.bf16_to_f64(V[0]))
+
+
+def test_closed_form_zero_query_gives_mean_of_v():
+    rng = RNG(2)
+    K, V = bits(rng, (37, 64)), bits(rng, (37, 64))
+    q = np.zeros(64, np.uint16)
+    want = oracle.bf16_to_f64(V).mean(axis=0)
+    assert np.max(np.abs(_single(K, V, q, 0.125) - want)) < 1e-14
+
+
+def test_closed_form_two_tokens_is_sigmoid_interpolation():
+    rng = RNG(3)
+    K, V, q = bits(rng, (2, 64)), bits(rng, (2, 64)), bits(rng, (64,))
+    Kf, Vf, qf = (oracle.bf16_to_f64(x) for x in (K, V, q))
+    s0, s1 = 0.125 * (Kf[0] @ qf), 0.125 * (Kf[1] @ qf)
+    sig = 1.0 / (1.0 + math.exp(-(s1 - s0)))
+    want = Vf[0] + sig * (Vf[1] - Vf[0])
+    assert np.max(np.abs(_single(K, V, q, 0.125) - want)) < 1e-14
+
+
+def test_closed_form_powers_of_two_weights():
+    # scores 0, ln2, 2 ln2 -> weights 1:2:4, exactly (V0 + 2 V1 + 4 V2) / 7
+    K = wlmod.f32_to_bf16_bits(np.array([[0.0, 5.0], [1.0, 5.0], [2.0, 5.0]], np.float32))
+    V = wlmod.f32_to_bf16_bits(np.array([[7.0, 0.0], [0.0, 7.0], [14.0, -7.0]], np.float32))
+    q = wlmod.f32_to_bf16_bits(np.array([1.0, 0.0], np.float32))
+    got = _single(K, V, q, math.log(2.0))
+    assert np.allclose(got, [(7 + 0 + 56) / 7, (0 + 14 - 28) / 7], atol=1e-14, rtol=0)
+
+
+def test_shift_invariances():
+    rng = RNG(4)
+    Kf = oracle.bf16_to_f64(bits(rng, (29, 64)))
+    Vf = oracle.bf16_to_f64(bits(rng, (29, 64)))
+    qf = oracle.bf16_to_f64(bits(rng, (64,)))
+    base = oracle.attend(qf, Kf, Vf, 0.125)
+    c = rng.standard_normal(64)
+    assert np.max(np.abs(oracle.attend(qf, Kf, Vf + c, 0.125) - (base + c))) < 1e-13
+    u = rng.standard_normal(64)
+    assert np.max(np.abs(oracle.attend(qf, Kf + u, Vf, 0.125) - base)) < 1e-13
+
+
+def test_empty_context_is_zero():
+    shape = oracle.PoolShape(1, 4, 2, 64)
+    pool = poison_pool(shape)
+    bt = np.full((1, 2), -1, np.int32)
+    q = bits(RNG(0), (1, 2, 4, 64))
+    assert not oracle.decode(pool, shape, 0, q, bt, [0], 0.125).any()
+
+
+def test_decoders_read_one_cache_independently():
+    """ICaRus Key designs 2-3: N decoders' concatenated call = each decoder alone."""
+    lens = [45, 16]
+    shape, pool, bt, _, _ = build_session_pool(lens, 2, 64, seed=9)
+    q = bits(RNG(9), (2, 4, 6, 64))
+    full = oracle.decode(pool, shape, 0, q, bt, lens, 0.125)
+    for n in range(4):
+        alone = oracle.decode(pool, shape, 0, q[:, n:n + 1].copy(), bt, lens, 0.125)
+        assert np.array_equal(full[:, n:n + 1], alone)
+    perm = [2, 0, 3, 1]
+    permuted = oracle.decode(pool, shape, 0, q[:, perm].copy(), bt, lens, 0.125)
+    assert np.array_equal(permuted, full[:, perm])
+
+
+def test_page_permutation_invariance():
+    lens = [70, 33]
+    shape, pool, bt, _, _ = build_session_pool(lens, 2, 64, seed=12)
+    q = bits(RNG(12), (2, 2, 4, 64))
+    base = oracle.decode(pool, shape, 0, q, bt, lens, 0.125)
+    perm = RNG(5).permutation(shape.num_pages)        # new id of old page i
+    tile = oracle.tile_elems(64) * shape.num_kv_heads
+    moved = np.empty_like(pool)
+    for old in range(shape.num_pages):
+        moved[perm[old] * tile:(perm[old] + 1) * tile] = pool[old * tile:(old + 1) * tile]
+    bt2 = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1).astype(np.int32)
+    assert np.array_equal(oracle.decode(moved, shape, 0, q, bt2, lens, 0.125), base)
+
+
+# ---------------------------------------------------------------------------
+# Extend
+# ---------------------------------------------------------------------------
+def _extend_case(prefix, new, Hkv, G, D, seed):
+    """Pool holding the prefixes, chunk inputs, and the full logical sequences."""
+    rng = RNG(seed)
+    full_k = [bits(rng, (p + c, Hkv, D)) for p, c in zip(prefix, new)]
+    full_v = [bits(rng, (p + c, Hkv, D)) for p, c in zip(prefix, new)]
+    bt, num_pages = wlmod.build_block_table([p + c for p, c in zip(prefix, new)], seed)
+    shape = oracle.PoolShape(1, num_pages, Hkv, D)
+    kp, cup = wlmod.concat_rows([k[:p] for k, p in zip(full_k, prefix)])
+    vp, _ = wlmod.concat_rows([v[:p] for v, p in zip(full_v, prefix)])
+    pool = oracle.append(poison_pool(shape), shape, 0, kp, vp, cup, bt, np.zeros(len(prefix), np.int32))
+    kn, cu = wlmod.concat_rows([k[p:] for k, p in zip(full_k, prefix)])
+    vn, _ = wlmod.concat_rows([v[p:] for v, p in zip(full_v, prefix)])
+    q = bits(rng, (int(cu[-1]), Hkv * G, D))
+    return shape, pool, bt, q, kn, vn, cu, full_k, full_v
+
+
+@pytest.mark.parametrize("prefix,new", [([40, 0, 16], [9, 20, 1]), ([0], [33])])
+def test_extend_equals_causal_sdpa_over_whole_sequence(prefix, new):
+    Hkv, G, D = 2, 3, 64
+    shape, pool, bt, q, kn, vn, cu, fk, fv = _extend_case(prefix, new, Hkv, G, D, seed=21)
+    out, pool2 = oracle.extend(pool, shape, 0, q, kn, vn, cu, bt, prefix, 0.125)
+    qf = oracle.bf16_to_f64(q)
+    for b, (P, C) in enumerate(zip(prefix, new)):
+        Kr = np.repeat(oracle.bf16_to_f64(fk[b]), G, axis=1)
+        Vr = np.repeat(oracle.bf16_to_f64(fv[b]), G, axis=1)
+        mask = np.arange(P + C)[None, :] <= (P + np.arange(C))[:, None]   # diagonal included
+        want = sdpa(qf[cu[b]:cu[b + 1]], Kr, Vr, 0.125, mask)
+        assert np.max(np.abs(out[cu[b]:cu[b + 1]] - want)) < 1e-12
+        Kg, _ = oracle.gather(pool2, shape, 0, bt[b], P + C)
+        assert np.array_equal(Kg, oracle.bf16_to_f64(fk[b]))
+
+
+def test_chunked_extend_equals_one_shot():
+    Hkv, G, D = 1, 2, 64
+    prefix, new = [21], [40]
+    shape, pool, bt, q, kn, vn, cu, _, _ = _extend_case(prefix, new, Hkv, G, D, seed=8)
+    one, pool_one = oracle.extend(pool, shape, 0, q, kn, vn, cu, bt, prefix, 0.125)
+    a, pool_a = oracle.extend(pool, shape, 0, q[:15], kn[:15], vn[:15], np.array([0, 15]), bt,
+                              prefix, 0.125)
+    b, pool_b = oracle.extend(pool_a, shape, 0, q[15:], kn[15:], vn[15:], np.array([0, 25]), bt,
+                              [36], 0.125)
+    assert np.array_equal(np.concatenate([a, b]), one)
+    assert np.array_equal(pool_b, pool_one)
+
+
+def test_decode_equals_single_row_extend():
+    Hkv, G, D = 2, 2, 64
+    prefix, new = [50], [1]
+    shape, pool, bt, q, kn, vn, cu, _, _ = _extend_case(prefix, new, Hkv, G, D, seed=4)
+    ext, pool2 = oracle.extend(pool, shape, 0, q, kn, vn, cu, bt, prefix, 0.125)
+    dec = oracle.decode(pool2, shape, 0, q[None], bt, [51], 0.125)
+    assert np.array_equal(dec[0, 0], ext[0])
+
+
+def test_logical_helpers_match_pool_path():
+    Hkv, G, D = 2, 2, 64
+    prefix, new = [30, 5], [7, 12]
+    shape, pool, bt, q, kn, vn, cu, fk, fv = _extend_case(prefix, new, Hkv, G, D, seed=2)
+    out, pool2 = oracle.extend(pool, shape, 0, q, kn, vn, cu, bt, prefix, 0.125)
+    for b in range(2):
+        rows = list(range(new[b]))
+        got = oracle.extend_from_logical(q[cu[b]:cu[b + 1]], fk[b], fv[b], prefix[b], rows, 0.125)
+        assert np.array_equal(got, out[cu[b]:cu[b + 1]])
+    qd = bits(RNG(1), (2, 3, Hkv * G, D))
+    lens = [37, 17]
+    dec = oracle.decode(pool2, shape, 0, qd, bt, lens, 0.125)
+    log = oracle.decode_from_logical(qd, [fk[b][:lens[b]] for b in range(2)],
+                                     [fv[b][:lens[b]] for b in range(2)], 0.125)
+    assert np.array_equal(dec, log)
+
+
+# ---------------------------------------------------------------------------
+# Workload recipes
+# ---------------------------------------------------------------------------
+def test_workload_recipes():
+    wl = wlmod.make_workload("qwen3_14b_long")
+    assert all(4096 <= L <= 131072 for L in wl.lens)
+    ls = wlmod.truncated_lognormal(wlmod._rng(99, 0), 20000, 9.7869, 1.0, 4096, 131072)
+    assert abs(np.mean(ls) / 27000 - 1) < 0.03    # the recipe's analytic truncated mean
+    w2 = wlmod.make_workload("llama8b_n4")
+    assert all(1024 <= L <= 8192 for L in w2.lens)
+    w3 = wlmod.make_workload("qwen3_8b_n8")
+    assert all(4096 <= L <= 16384 for L in w3.lens) and w3.num_layers == 36
+    bt, npages = wlmod.build_block_table(w3.lens, 2)
+    used = bt[bt >= 0]
+    assert len(np.unique(used)) == len(used) == sum((L + 15) // 16 for L in w3.lens) < npages
