@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark of the shared-KV attention path on one MI355X.
+
+A step is one decode step of the 8-decoder Qwen3-8B-shaped agentic workload
+over all 36 layers: for every layer, kv_pool_append writes the step's token
+K/V of every session (the frozen base model's cache store), then
+shared_kv_decode runs the N=8 decoders x 4 GQA heads of every KV head over the
+shared pages.  `value` is the decode's algorithmic bytes per second over whole
+steps.  Extend (partial prefill of 512 new tokens on 8K cached prefixes,
+16 sessions) is timed alongside and reported as TFLOP/s under "extend".
+
+Prints ONE JSON line.  Inputs are seeded synthetic tensors already resident in
+HBM when timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
+DECODE_WORKLOAD = "qwen3_8b_n8"
+EXTEND_WORKLOAD = "extend_8k_512"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--extend-calls", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=None, help=argparse.SUPPRESS)
+    return ap.parse_args()
+
+
+def decode_bytes(lens, B, N, Hq, Hkv, D):
+    """Algorithmic bytes of one decode call: valid KV + q + out + block table + lengths."""
+    kv = sum(lens) * Hkv * D * 2 * 2
+    qo = 2 * B * N * Hq * D * 2
+    bt = 4 * sum((L + 15) // 16 for L in lens)
+    return kv + qo + bt + 4 * B
+
+
+def append_bytes(tokens, Hkv, D):
+    return tokens * Hkv * D * 2 * 2 * 2     # read k/v rows, write them
+
+
+def extend_flops(prefix, new, Hq, D):
+    return 4 * D * Hq * sum(c * p + c * (c + 1) // 2 for p, c in zip(prefix, new))
+
+
+class EventTimer:
+    """Sums HIP-event durations of the bracketed calls on the current stream."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self):
+        import torch
+
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, e0):
+        import torch
+
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+
+    def all_ms(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
+
+def setup_decode(wl, layers):
+    import torch
+
+    from cross_model_shared_amd import binding
+    from cross_model_shared_amd import workload as W
+
+    B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    lens = wl.lens
+    bt, num_pages = W.build_block_table(lens, wl.seed)
+    pool = binding.Pool(layers, num_pages, Hkv, D)
+    dev = dict(bt=torch.from_numpy(bt).cuda(), lens=torch.tensor(lens, dtype=torch.int32, device="cuda"),
+               before=torch.tensor([L - 1 for L in lens], dtype=torch.int32, device="cuda"),
+               zeros=torch.zeros(B, dtype=torch.int32, device="cuda"))
+    cu = np.zeros(B + 1, np.int64)
+    cu[1:] = np.cumsum(lens)
+    dev["cu_all"] = torch.from_numpy(cu.astype(np.int32)).cuda()
+    dev["cu_one"] = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    total = int(cu[-1])
+    maxL = max(lens)
+    t0 = time.perf_counter()
+    for layer in range(layers):
+        k = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 10, layer)).view(total, Hkv, D)
+        v = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 11, layer)).view(total, Hkv, D)
+        binding.append(pool, layer, k, v, dev["cu_all"], dev["bt"], dev["zeros"], max_new=maxL,
+                       max_seq_len=maxL)
+        del k, v
+    torch.cuda.synchronize()
+    log(f"[bench] pool filled: {layers} layers x {num_pages} pages = {pool.nbytes / 1e9:.1f} GB "
+        f"in {time.perf_counter() - t0:.1f}s")
+    q = [W.device_normal_bf16(B * N * Hq * D, wl.std, W.mix_seed(wl.seed, 12, l)).view(B, N, Hq, D)
+         for l in range(layers)]
+    tok_k = [W.device_normal_bf16(B * Hkv * D, wl.std, W.mix_seed(wl.seed, 13, l)).view(B, Hkv, D)
+             for l in range(layers)]
+    tok_v = [W.device_normal_bf16(B * Hkv * D, wl.std, W.mix_seed(wl.seed, 14, l)).view(B, Hkv, D)
+             for l in range(layers)]
+    out = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(binding.decode_workspace_bytes(B, N, Hq, Hkv, D, maxL), dtype=torch.uint8, device="cuda")
+    return dict(pool=pool, dev=dev, q=q, tok_k=tok_k, tok_v=tok_v, out=out, ws=ws, maxL=maxL,
+                num_pages=num_pages, bt=bt)
+
+
+def decode_step(wl, st, layers, timer=None):
+    from cross_model_shared_amd import binding
+
+    d = st["dev"]
+    for layer in range(layers):
+        binding.append(st["pool"], layer, st["tok_k"][layer], st["tok_v"][layer], d["cu_one"], d["bt"],
+                       d["before"], max_new=1, max_seq_len=st["maxL"])
+        e0 = timer.start() if timer else None
+        binding.decode(st["pool"], layer, st["q"][layer], st["out"], d["bt"], d["lens"], st["maxL"],
+                       wl.scale, st["ws"])
+        if timer:
+            timer.stop(e0)
+
+
+def setup_extend(wl):
+    import torch
+
+    from cross_model_shared_amd import binding
+    from cross_model_shared_amd import workload as W
+
+    B, Hq, Hkv, D = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    full = wl.total_lens()
+    bt, num_pages = W.build_block_table(full, wl.seed)
+    pool = binding.Pool(1, num_pages, Hkv, D)
+    btd = torch.from_numpy(bt).cuda()
+    P = sum(wl.prefix)
+    cu_p = torch.tensor(np.concatenate([[0], np.cumsum(wl.prefix)]), dtype=torch.int32, device="cuda")
+    kp = W.device_normal_bf16(P * Hkv * D, wl.std, W.mix_seed(wl.seed, 20)).view(P, Hkv, D)
+    vp = W.device_normal_bf16(P * Hkv * D, wl.std, W.mix_seed(wl.seed, 21)).view(P, Hkv, D)
+    binding.append(pool, 0, kp, vp, cu_p, btd, torch.zeros(B, dtype=torch.int32, device="cuda"),
+                   max_new=max(wl.prefix), max_seq_len=max(full))
+    T = sum(wl.new)
+    q = W.device_normal_bf16(T * Hq * D, wl.std, W.mix_seed(wl.seed, 22)).view(T, Hq, D)
+    kn = W.device_normal_bf16(T * Hkv * D, wl.std, W.mix_seed(wl.seed, 23)).view(T, Hkv, D)
+    vn = W.device_normal_bf16(T * Hkv * D, wl.std, W.mix_seed(wl.seed, 24)).view(T, Hkv, D)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(wl.new)]), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    pre = torch.tensor(wl.prefix, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    return dict(pool=pool, bt=btd, q=q, kn=kn, vn=vn, cu=cu, out=out, pre=pre, max_new=max(wl.new),
+                msl=max(full))
+
+
+def extend_call(wl, st):
+    from cross_model_shared_amd import binding
+
+    binding.extend(st["pool"], 0, st["q"], st["kn"], st["vn"], st["out"], st["cu"], st["bt"], st["pre"],
+                   st["max_new"], st["msl"], wl.scale)
+
+
+def cpu_baseline(wl, st, target_s):
+    """Time the CPU oracle's decode on a bounded sample of sessions of layer 0."""
+    import torch
+
+    import oracle
+    from cross_model_shared_amd import workload as W
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    lens = wl.lens
+    order = sorted(range(B), key=lambda b: lens[b])[:: max(1, B // 16)]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    total = int(cu[-1])
+    k = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 10, 0)).view(total, Hkv, D)
+    v = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 11, 0)).view(total, Hkv, D)
+    q = st["q"][0].view(torch.int16).cpu().numpy().view(np.uint16)
+    spent, done_bytes, done = 0.0, 0, []
+    for b in order:
+        L = lens[b]
+        kb = k[cu[b]:cu[b + 1]].view(torch.int16).cpu().numpy().view(np.uint16)
+        vb = v[cu[b]:cu[b + 1]].view(torch.int16).cpu().numpy().view(np.uint16)
+        npg = (L + 15) // 16
+        shape = oracle.PoolShape(1, npg, Hkv, D)
+        bt = np.arange(npg, dtype=np.int32)[None]
+        img = oracle.append(np.zeros(shape.elems, np.uint16), shape, 0, kb, vb, [0, L], bt, [0])
+        t0 = time.perf_counter()
+        oracle.decode(img, shape, 0, q[b:b + 1], bt, [L], wl.scale)
+        spent += time.perf_counter() - t0
+        done_bytes += decode_bytes([L], 1, N, Hq, Hkv, D)
+        done.append(L)
+        if spent >= target_s:
+            break
+    del k, v
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+            "blas_threads": blas_threads, "kind": "oracle",
+            "sample": f"float64 oracle decode (gather + softmax) of {len(done)} of {B} sessions of layer 0 "
+                      f"(lengths {done}), all {N} decoders x {Hq} heads; {spent:.1f}s CPU time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path runs on a "
+              f"single MI355X; see the sharding notes in the design document)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from cross_model_shared_amd import binding
+    from cross_model_shared_amd import workload as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    wl = W.make_workload(DECODE_WORKLOAD)
+    layers = args.layers or wl.num_layers
+    B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    st = setup_decode(wl, layers)
+    per_call = decode_bytes(wl.lens, B, N, Hq, Hkv, D)
+    step_bytes = layers * per_call
+    step_total_bytes = step_bytes + layers * append_bytes(B, Hkv, D)
+
+    for _ in range(args.warmup):
+        decode_step(wl, st, layers)
+    torch.cuda.synchronize()
+    timer = EventTimer()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        decode_step(wl, st, layers, timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    value = step_bytes / (wall / args.steps) / 1e9
+    call_ms = timer.mean_ms()
+    achieved = per_call / (call_ms * 1e-3) / 1e9
+    log(f"[bench] decode step {ms_step:.3f} ms ({layers} layers), decode call {call_ms * 1e3:.1f} us, "
+        f"{achieved:.0f} GB/s")
+
+    # time(N) / time(1) at fixed KV: one decoder's queries only (ICaRus Key design 3 claim)
+    q1 = st["q"][0][:, :1].contiguous()
+    out1 = torch.empty_like(q1)
+    ws1 = torch.zeros(binding.decode_workspace_bytes(B, 1, Hq, Hkv, D, st["maxL"]), dtype=torch.uint8,
+                      device="cuda")
+    t1, tN = EventTimer(), EventTimer()
+    for i in range(12):
+        e = t1.start()
+        binding.decode(st["pool"], i % layers, q1, out1, st["dev"]["bt"], st["dev"]["lens"], st["maxL"],
+                       wl.scale, ws1)
+        t1.stop(e)
+        e = tN.start()
+        binding.decode(st["pool"], (i + 5) % layers, st["q"][0], st["out"], st["dev"]["bt"], st["dev"]["lens"],
+                       st["maxL"], wl.scale, st["ws"])
+        tN.stop(e)
+    torch.cuda.synchronize()
+    n1_ms = float(np.median(t1.all_ms()[2:]))
+    nN_ms = float(np.median(tN.all_ms()[2:]))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, st, args.cpu_seconds)
+        log(f"[bench] cpu baseline {cpu['value']} GB/s")
+    pool_gb = st["pool"].nbytes / 1e9
+    del st
+    torch.cuda.empty_cache()
+
+    # ---- extend ----
+    ew = W.make_workload(EXTEND_WORKLOAD)
+    es = setup_extend(ew)
+    for _ in range(3):
+        extend_call(ew, es)
+    torch.cuda.synchronize()
+    et = EventTimer()
+    for _ in range(args.extend_calls):
+        e = et.start()
+        extend_call(ew, es)
+        et.stop(e)
+    torch.cuda.synchronize()
+    ext_ms = float(np.median(et.all_ms()))
+    flops = extend_flops(ew.prefix, ew.new, ew.num_q_heads, ew.head_dim)
+    ext_tflops = flops / (ext_ms * 1e-3) / 1e12
+    log(f"[bench] extend call {ext_ms:.3f} ms, {ext_tflops:.1f} TFLOP/s")
+
+    res = {
+        "metric": "shared-KV decode attn KV GB/s (% HBM peak) at N=8 decoders; extend TFLOP/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{DECODE_WORKLOAD}: Qwen3-8B-shaped 8-decoder agentic decode step, {layers} layers "
+                        f"(append 1 token/session + shared_kv_decode per layer), B={B} sessions, N={N}, "
+                        f"32 q / 8 KV heads, D=128, page 16, lengths U[4096,16384] (sum {sum(wl.lens)})",
+            "batch": B, "num_decoders": N, "layers": layers, "context_tokens": sum(wl.lens),
+            "step_algorithmic_bytes": step_total_bytes, "decode_bytes_per_layer": per_call,
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "shared_kv_decode (per-layer call)",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "launch_ms": round(call_ms, 5),
+        },
+        "cpu_baseline": cpu,
+        "decoder_concat": {"time_N8_over_N1": round(nN_ms / n1_ms, 3), "ms_N8": round(nN_ms, 4),
+                           "ms_N1": round(n1_ms, 4)},
+        "footprint": {"pool_GB": round(pool_gb, 2), "n_private_copies_GB": round(pool_gb * N, 2),
+                      "ratio": N},
+        "extend": {
+            "workload": f"{EXTEND_WORKLOAD}: B=16, cached prefix 8192 + 512 new tokens, 32 q / 8 KV heads, "
+                        f"D=128 (partial_prefill_extend = append chunk + causal attention)",
+            "value": round(ext_tflops, 2), "unit": "TFLOP/s", "ms_per_call": round(ext_ms, 4),
+            "flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(ext_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ext_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+        },
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+"""ctypes binding of libkvshare.so: argument marshalling only.
+
+Every function here checks that tensors live on the GPU with the dtype and
+shape the C ABI expects, then passes raw device pointers and the current HIP
+stream.  All arithmetic runs in the library's HIP kernels; there is no CPU
+path, and a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvshare.so")
+
+KVS_OK, KVS_EINVAL, KVS_ERANGE, KVS_EWORKSPACE, KVS_EUNSUPPORTED, KVS_EHIP = 0, -1, -2, -3, -4, -5
+DEV_BAD_PAGE, DEV_BAD_LEN = 1, 2
+PAGE = 16
+
+
+class KvsError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"kvshare status {status}: {message}")
+        self.status = status
+
+
+class KvsPool(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("num_layers", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32)]
+
+
+_i32, _sz, _vp, _f = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+_pool_p = ctypes.POINTER(KvsPool)
+
+_SIGNATURES = {
+    "kvs_pool_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "kv_pool_append": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                                      _i32, _vp, _vp]),
+    "shared_kv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "shared_kv_decode": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                        _f, _vp, _sz, _vp, _vp]),
+    "partial_prefill_extend": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                                              _i32, _i32, _i32, _i32, _i32, _f, _vp, _vp]),
+    "kvs_last_error": (ctypes.c_char_p, []),
+    "kvs_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (building it in-tree first if it is not there)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        from . import build_lib
+
+        build_lib.build()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libkvshare.so not found at {path}; the HIP path is required")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().kvs_last_error().decode()
+
+
+def _check(status: int):
+    if status != KVS_OK:
+        raise KvsError(status, last_error())
+
+
+# ---------------------------------------------------------------------------
+# tensor helpers (torch is only the device allocator and stream provider)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t, name, dtype=None, numel=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Pool:
+    """A paged KV pool in device memory (bf16 payload, page size 16)."""
+
+    def __init__(self, num_layers, num_pages, num_kv_heads, head_dim, device="cuda", fill=None):
+        torch = _torch()
+        lib = load()
+        nbytes = lib.kvs_pool_bytes(num_layers, num_pages, num_kv_heads, head_dim, PAGE)
+        if nbytes == 0:
+            raise ValueError("invalid pool shape")
+        if fill is None:
+            self.data = torch.empty(nbytes // 2, dtype=torch.int16, device=device)
+        else:
+            self.data = torch.full((nbytes // 2,), int(fill), dtype=torch.int16, device=device)
+        self.num_layers, self.num_pages = int(num_layers), int(num_pages)
+        self.num_kv_heads, self.head_dim = int(num_kv_heads), int(head_dim)
+        self._struct = KvsPool(self.data.data_ptr(), self.num_layers, self.num_pages,
+                               self.num_kv_heads, self.head_dim, PAGE)
+
+    @property
+    def struct(self):
+        return ctypes.byref(self._struct)
+
+    @property
+    def nbytes(self) -> int:
+        return self.data.numel() * 2
+
+
+def append(pool: Pool, layer, k_new, v_new, cu_new, block_table, seq_lens, max_new, max_seq_len,
+           dev_status=None, stream=None):
+    torch = _torch()
+    batch = seq_lens.numel()
+    total = k_new.shape[0]
+    row = pool.num_kv_heads * pool.head_dim
+    _check(load().kv_pool_append(
+        pool.struct, layer, _ptr(k_new, "k_new", torch.bfloat16, total * row),
+        _ptr(v_new, "v_new", torch.bfloat16, total * row), _ptr(cu_new, "cu_new", torch.int32, batch + 1),
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
+        _ptr(seq_lens, "seq_lens", torch.int32), batch, total, max_new, max_seq_len,
+        _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True), _stream(stream)))
+
+
+def decode_workspace_bytes(batch, num_decoders, num_q_heads, num_kv_heads, head_dim, max_seq_len) -> int:
+    return load().shared_kv_decode_workspace_bytes(batch, num_decoders, num_q_heads, num_kv_heads,
+                                                   head_dim, max_seq_len)
+
+
+def decode(pool: Pool, layer, q, out, block_table, seq_lens, max_seq_len, scale, workspace,
+           dev_status=None, stream=None):
+    """q, out: bf16 [B, N, H_q, D]; workspace: a zero-filled uint8 device tensor."""
+    torch = _torch()
+    B, N, Hq, D = q.shape
+    if D != pool.head_dim or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q/out shape does not match the pool")
+    _check(load().shared_kv_decode(
+        pool.struct, layer, _ptr(q, "q", torch.bfloat16), _ptr(out, "out", torch.bfloat16),
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
+        _ptr(seq_lens, "seq_lens", torch.int32, B), B, N, Hq, max_seq_len, float(scale),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True), _stream(stream)))
+
+
+def extend(pool: Pool, layer, q, k_new, v_new, out, cu_new, block_table, seq_lens, max_new,
+           max_seq_len, scale, dev_status=None, stream=None):
+    """q, out: bf16 [T, H_q, D]; k_new, v_new: bf16 [T, H_kv, D]."""
+    torch = _torch()
+    T, Hq, D = q.shape
+    batch = seq_lens.numel()
+    row = pool.num_kv_heads * pool.head_dim
+    if D != pool.head_dim or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q/out shape does not match the pool")
+    _check(load().partial_prefill_extend(
+        pool.struct, layer, _ptr(q, "q", torch.bfloat16), _ptr(k_new, "k_new", torch.bfloat16, T * row),
+        _ptr(v_new, "v_new", torch.bfloat16, T * row), _ptr(out, "out", torch.bfloat16),
+        _ptr(cu_new, "cu_new", torch.int32, batch + 1), _ptr(block_table, "block_table", torch.int32),
+        block_table.shape[1], _ptr(seq_lens, "seq_lens", torch.int32), batch, Hq, T, max_new,
+        max_seq_len, float(scale), _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True),
+        _stream(stream)))

@@ -1,0 +1,92 @@
+// kv_pool_append on gfx950: copy new K/V rows into their page slots, bit for bit.
+//
+// The cache store of the base prefill (PrefillShare, section 3.3: the KV lives
+// in fixed-size blocks; ICaRus, overall framework: E_base writes the KV all
+// decoders read).  One workgroup per (window of up to 16 new tokens that share a
+// page, KV head, session).  K rows are moved as 16-byte runs; the V part of a
+// tile is stored with 4 slots of one head-dim value side by side, so a thread
+// gathers those 4 slots and writes them as one 8-byte word when all 4 are new,
+// and slot by slot otherwise (slots not being appended are never touched).
+#include "kvs_device.h"
+#include "kvs_internal.h"
+
+namespace kvs {
+
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int w = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int Hkv = a.pool.num_kv_heads;
+  const int P = a.seq_lens[b];
+  const int c0 = a.cu_new[b], c1 = a.cu_new[b + 1];
+  const int n = c1 - c0;
+  if (P < 0 || n < 0 || n > a.max_new || P + n > a.max_seq_len || c0 < 0 || c1 > a.total_new) {
+    if (threadIdx.x == 0 && w == 0 && h == 0) flag_error(a.dev_status, 2);
+    return;
+  }
+  if (n == 0) return;
+  const int lp = P / kPage + w;  // logical page written by this workgroup
+  const int t0 = max(lp * kPage, P), t1 = min(lp * kPage + kPage, P + n);
+  if (t0 >= t1) return;
+  const int pid = a.bt[int64_t(b) * a.bt_stride + lp];
+  if (pid < 0 || pid >= a.pool.num_pages) {
+    if (threadIdx.x == 0) flag_error(a.dev_status, 1);
+    return;
+  }
+  uint16_t* tile = a.pool.data + tile_offset(a.layer, pid, h, a.pool.num_pages, Hkv, D);
+  const int64_t row_stride = int64_t(Hkv) * D;
+  // new row of logical position t is c0 + (t - P)
+  const uint16_t* ksrc = a.k_new + int64_t(h) * D;
+  const uint16_t* vsrc = a.v_new + int64_t(h) * D;
+
+  // K: one thread per (slot, 8-value run)
+  for (int e = threadIdx.x; e < kPage * (D / 8); e += 256) {
+    const int slot = e / (D / 8), run = e % (D / 8);
+    const int t = lp * kPage + slot;
+    if (t < t0 || t >= t1) continue;
+    const int d0 = run * 8;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ksrc + int64_t(c0 + t - P) * row_stride + d0);
+    *reinterpret_cast<u32x4*>(tile + ((d0 / 32) * 64 + ((d0 % 32) / 8) * 16 + slot) * 8) = v;
+  }
+  // V: one thread per (group of 4 slots, head-dim value)
+  uint16_t* vt = tile + kPage * D;
+  for (int e = threadIdx.x; e < 4 * D; e += 256) {
+    const int quad = e / D, d = e % D;
+    const int base = lp * kPage + 4 * quad;
+    uint16_t* dst = vt + ((d / 32) * 64 + quad * 16 + d % 16) * 8 + ((d / 16) % 2) * 4;
+    if (base >= t0 && base + 3 < t1) {
+      uint16_t x[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[c] = vsrc[int64_t(c0 + base + c - P) * row_stride + d];
+      *reinterpret_cast<u32x2*>(dst) =
+          u32x2{uint32_t(x[0]) | (uint32_t(x[1]) << 16), uint32_t(x[2]) | (uint32_t(x[3]) << 16)};
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int t = base + c;
+        if (t >= t0 && t < t1) dst[c] = vsrc[int64_t(c0 + t - P) * row_stride + d];
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_append_t(const AppendArgs& a, hipStream_t stream) {
+  // a window of new tokens starting mid-page can touch one page more
+  const int windows = (a.max_new + kPage - 1) / kPage + 1;
+  dim3 grid(windows, a.pool.num_kv_heads, a.batch);
+  hipLaunchKernelGGL((append_kernel<D>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+  if (a.pool.head_dim == 128) return launch_append_t<128>(a, stream);
+  return launch_append_t<64>(a, stream);
+}
+
+}  // namespace kvs

@@ -1,0 +1,91 @@
+// Device-side building blocks shared by the gfx950 kernels: vector types, the
+// pool tile addressing, matrix-core steps and the online-softmax update.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPage = 16;
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Element offset of the (layer, page, head) tile: K part (16*D) then V part (16*D).
+__device__ __forceinline__ int64_t tile_offset(int layer, int page, int head, int num_pages,
+                                               int num_kv_heads, int D) {
+  return ((int64_t(layer) * num_pages + page) * num_kv_heads + head) * int64_t(32 * D);
+}
+
+// One lane's 16-byte operand of K slab `i` (head dims 32i..32i+31): slot lane%16,
+// head dims 32i + 8*(lane/16) .. +7.  As an A operand of the 16x16x32 step this is
+// row (slot) lane%16, k = 8*(lane/16)+c — the K tile is stored in exactly this order.
+__device__ __forceinline__ u32x4 load_k_slab(const uint16_t* tile, int i, int lane) {
+  return reinterpret_cast<const u32x4*>(tile)[i * kWave + lane];
+}
+// One lane's 16 bytes of V slab `i`: head dims 32i + 16*half + lane%16 (half = 0, 1),
+// slots 4*(lane/16) .. +3 for each half.
+__device__ __forceinline__ u32x4 load_v_slab(const uint16_t* tile, int D, int i, int lane) {
+  return reinterpret_cast<const u32x4*>(tile + 16 * D)[i * kWave + lane];
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ i16x4 as_i16x4(u32x2 v) { return __builtin_bit_cast(i16x4, v); }
+
+// C += A(16x32) * B(32x16), bf16 in, fp32 accumulate.
+__device__ __forceinline__ f32x4 mma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+// C += A(16x16) * B(16x16), bf16 in, fp32 accumulate.
+__device__ __forceinline__ f32x4 mma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(a), as_i16x4(b), c, 0, 0, 0);
+}
+
+// Pack four fp32 into four bf16 (round to nearest even) as two dwords.
+__device__ __forceinline__ u32x2 pack_bf16x4(float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  v[2] = (__bf16)c;
+  v[3] = (__bf16)d;
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ float wave_max_across_quads(float x) {
+  // lanes l, l^16, l^32, l^48 hold the same row
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_across_quads(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Zero the V operand entries (both halves) of slots >= nvalid.  Slots past a
+// session's end may hold anything, NaN included, and 0 * NaN would poison PV.
+__device__ __forceinline__ u32x4 mask_v_slab(u32x4 v, int lane, int nvalid) {
+  const int s0 = 4 * (lane >> 4);
+  // dword j of each half holds slots s0+2j (low 16 bits) and s0+2j+1 (high)
+  uint32_t m0 = (s0 + 0 < nvalid ? 0x0000FFFFu : 0u) | (s0 + 1 < nvalid ? 0xFFFF0000u : 0u);
+  uint32_t m1 = (s0 + 2 < nvalid ? 0x0000FFFFu : 0u) | (s0 + 3 < nvalid ? 0xFFFF0000u : 0u);
+  v[0] &= m0;
+  v[1] &= m1;
+  v[2] &= m0;
+  v[3] &= m1;
+  return v;
+}
+
+__device__ __forceinline__ void flag_error(int32_t* dev_status, int bits) {
+  if (dev_status) atomicOr(dev_status, bits);
+}
+
+}  // namespace kvs

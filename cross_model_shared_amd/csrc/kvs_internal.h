@@ -1,0 +1,78 @@
+// Host-side launch arguments and launchers shared by the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvs {
+
+struct PoolView {
+  uint16_t* data;
+  int num_layers, num_pages, num_kv_heads, head_dim;
+};
+
+struct AppendArgs {
+  PoolView pool;
+  int layer;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* cu_new;
+  const int32_t* bt;
+  int bt_stride;
+  const int32_t* seq_lens;
+  int batch, total_new, max_new, max_seq_len;
+  int32_t* dev_status;
+};
+
+// How a decode call is cut into work: query rows per KV head are taken in row
+// groups of 16*nb (one wave holds them all), and each session's pages in splits
+// of split_pages pages (one workgroup each).
+struct DecodePlan {
+  int rows;         // N * G query rows per KV head
+  int nb;           // 16-row column blocks per wave (1, 2 or 4)
+  int rg_rows;      // 16 * nb
+  int rowgroups;    // ceil(rows / rg_rows)
+  int split_pages;  // pages per workgroup (multiple of 4: one share per wave)
+  int max_splits;   // ceil(ceil(max_seq_len/16) / split_pages)
+  size_t ml_offset, acc_offset, bytes;
+};
+
+DecodePlan plan_decode(int batch, int num_decoders, int num_q_heads, int num_kv_heads, int head_dim,
+                       int max_seq_len);
+
+struct DecodeArgs {
+  PoolView pool;
+  int layer;
+  const uint16_t* q;
+  uint16_t* out;
+  const int32_t* bt;
+  int bt_stride;
+  const int32_t* seq_lens;
+  int batch, num_decoders, num_q_heads, max_seq_len;
+  float scale_log2;
+  float* ws_ml;
+  float* ws_acc;
+  DecodePlan plan;
+  int32_t* dev_status;
+};
+
+struct ExtendArgs {
+  PoolView pool;
+  int layer;
+  const uint16_t* q;
+  uint16_t* out;
+  const int32_t* cu_new;
+  const int32_t* bt;
+  int bt_stride;
+  const int32_t* seq_lens;
+  int batch, num_q_heads, total_new, max_new, max_seq_len;
+  float scale_log2;
+  int32_t* dev_status;
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream);
+
+}  // namespace kvs

@@ -1,0 +1,206 @@
+// C ABI of libkvshare: argument checks, launch planning, status reporting.
+// Every check runs before anything is enqueued; the library never allocates,
+// frees or synchronizes.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <string>
+
+#include "../../include/kvshare.h"
+#include "kvs_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int check_pool(const kvs_pool* pool, int32_t layer) {
+  if (!pool) return fail(KVS_EINVAL, "pool is NULL");
+  if (!pool->data) return fail(KVS_EINVAL, "pool->data is NULL");
+  if (pool->page_size != 16)
+    return fail(KVS_EUNSUPPORTED, "page_size %d unsupported (must be 16)", pool->page_size);
+  if (pool->head_dim != 64 && pool->head_dim != 128)
+    return fail(KVS_EUNSUPPORTED, "head_dim %d unsupported (64 or 128)", pool->head_dim);
+  if (pool->num_layers <= 0 || pool->num_pages <= 0 || pool->num_kv_heads <= 0)
+    return fail(KVS_EINVAL, "pool sizes must be positive (layers %d, pages %d, kv heads %d)",
+                pool->num_layers, pool->num_pages, pool->num_kv_heads);
+  if (layer < 0 || layer >= pool->num_layers)
+    return fail(KVS_ERANGE, "layer %d outside [0, %d)", layer, pool->num_layers);
+  return KVS_OK;
+}
+
+int check_table(int32_t batch, int32_t bt_stride, int32_t max_seq_len) {
+  if (batch <= 0) return fail(KVS_EINVAL, "batch %d must be positive", batch);
+  if (bt_stride <= 0) return fail(KVS_EINVAL, "bt_stride %d must be positive", bt_stride);
+  if (max_seq_len < 0) return fail(KVS_EINVAL, "max_seq_len %d is negative", max_seq_len);
+  if (int64_t(max_seq_len) > int64_t(bt_stride) * 16)
+    return fail(KVS_ERANGE, "max_seq_len %d exceeds block-table capacity %lld (bt_stride %d * 16)",
+                max_seq_len, (long long)bt_stride * 16, bt_stride);
+  return KVS_OK;
+}
+
+kvs::PoolView view(const kvs_pool* p) {
+  return kvs::PoolView{static_cast<uint16_t*>(p->data), p->num_layers, p->num_pages, p->num_kv_heads,
+                       p->head_dim};
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KVS_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return KVS_OK;
+}
+
+// Pages per decode workgroup.  Sized so that an upper bound of the work
+// (every session at max_seq_len) makes about kTargetBlocks workgroups: enough
+// to keep 256 CUs busy when real lengths are ragged, few enough that split
+// partials stay a small fraction of the KV bytes.  KVS_DECODE_SPLIT_PAGES
+// overrides it (tuning only; rounded up to a multiple of 4).
+int decode_split_pages(int64_t units, int max_pages) {
+  const char* env = getenv("KVS_DECODE_SPLIT_PAGES");
+  if (env && atoi(env) > 0) return (atoi(env) + 3) / 4 * 4;
+  constexpr int64_t kTargetBlocks = 8192;
+  int64_t sp = (units * max_pages + kTargetBlocks - 1) / kTargetBlocks;
+  if (sp < 16) sp = 16;
+  if (sp > 1024) sp = 1024;
+  return int((sp + 3) / 4 * 4);
+}
+
+}  // namespace
+
+namespace kvs {
+
+DecodePlan plan_decode(int batch, int num_decoders, int num_q_heads, int num_kv_heads, int head_dim,
+                       int max_seq_len) {
+  DecodePlan p{};
+  p.rows = num_decoders * (num_q_heads / num_kv_heads);
+  p.nb = p.rows <= 16 ? 1 : (p.rows <= 32 ? 2 : 4);
+  p.rg_rows = 16 * p.nb;
+  p.rowgroups = (p.rows + p.rg_rows - 1) / p.rg_rows;
+  const int max_pages = (max_seq_len + 15) / 16;
+  const int64_t units = int64_t(batch) * num_kv_heads * p.rowgroups;
+  p.split_pages = decode_split_pages(units, max_pages < 1 ? 1 : max_pages);
+  p.max_splits = max_pages < 1 ? 1 : (max_pages + p.split_pages - 1) / p.split_pages;
+  const size_t slots = size_t(units) * p.max_splits;
+  p.ml_offset = 0;
+  size_t ml_bytes = slots * p.rg_rows * 2 * sizeof(float);
+  p.acc_offset = (ml_bytes + 255) / 256 * 256;
+  p.bytes = p.acc_offset + slots * p.rg_rows * head_dim * sizeof(float);
+  return p;
+}
+
+}  // namespace kvs
+
+extern "C" {
+
+const char* kvs_last_error(void) { return g_last_error.c_str(); }
+
+const char* kvs_version(void) { return "kvshare 0.1 gfx950"; }
+
+size_t kvs_pool_bytes(int32_t num_layers, int32_t num_pages, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t page_size) {
+  if (num_layers <= 0 || num_pages <= 0 || num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0)
+    return 0;
+  return size_t(num_layers) * num_pages * num_kv_heads * 2 * size_t(page_size) * head_dim * 2;
+}
+
+int kv_pool_append(const kvs_pool* pool, int32_t layer, const void* k_new, const void* v_new,
+                   const int32_t* cu_new, const int32_t* block_table, int32_t bt_stride,
+                   const int32_t* seq_lens, int32_t batch, int32_t total_new, int32_t max_new,
+                   int32_t max_seq_len, int32_t* dev_status, hipStream_t stream) {
+  int s = check_pool(pool, layer);
+  if (s) return s;
+  if (!k_new || !v_new || !cu_new || !block_table || !seq_lens)
+    return fail(KVS_EINVAL, "kv_pool_append: a required pointer is NULL");
+  if ((s = check_table(batch, bt_stride, max_seq_len))) return s;
+  if (max_new <= 0 || total_new < 0)
+    return fail(KVS_EINVAL, "kv_pool_append: max_new %d must be >= 1, total_new %d >= 0", max_new,
+                total_new);
+  if (max_new > max_seq_len)
+    return fail(KVS_ERANGE, "kv_pool_append: max_new %d exceeds max_seq_len %d", max_new, max_seq_len);
+  kvs::AppendArgs a{view(pool), layer, static_cast<const uint16_t*>(k_new),
+                    static_cast<const uint16_t*>(v_new), cu_new, block_table, bt_stride, seq_lens,
+                    batch, total_new, max_new, max_seq_len, dev_status};
+  return launched(kvs::launch_append(a, stream), "kv_pool_append");
+}
+
+size_t shared_kv_decode_workspace_bytes(int32_t batch, int32_t num_decoders, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_seq_len) {
+  if (batch <= 0 || num_decoders <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_seq_len < 0 || num_q_heads % num_kv_heads)
+    return 0;
+  return kvs::plan_decode(batch, num_decoders, num_q_heads, num_kv_heads, head_dim, max_seq_len).bytes;
+}
+
+int shared_kv_decode(const kvs_pool* pool, int32_t layer, const void* q, void* out,
+                     const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                     int32_t batch, int32_t num_decoders, int32_t num_q_heads, int32_t max_seq_len,
+                     float scale, void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                     hipStream_t stream) {
+  int s = check_pool(pool, layer);
+  if (s) return s;
+  if (!q || !out || !block_table || !seq_lens)
+    return fail(KVS_EINVAL, "shared_kv_decode: a required pointer is NULL");
+  if ((s = check_table(batch, bt_stride, max_seq_len))) return s;
+  if (num_decoders <= 0 || num_q_heads <= 0)
+    return fail(KVS_EINVAL, "shared_kv_decode: num_decoders %d and num_q_heads %d must be positive",
+                num_decoders, num_q_heads);
+  if (num_q_heads % pool->num_kv_heads)
+    return fail(KVS_EUNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                pool->num_kv_heads);
+  if (!(scale > 0.f) || scale != scale)
+    return fail(KVS_EINVAL, "shared_kv_decode: scale must be a positive number");
+  kvs::DecodePlan plan = kvs::plan_decode(batch, num_decoders, num_q_heads, pool->num_kv_heads,
+                                          pool->head_dim, max_seq_len);
+  if (!workspace || workspace_bytes < plan.bytes)
+    return fail(KVS_EWORKSPACE, "shared_kv_decode: workspace %zu bytes < required %zu",
+                workspace ? workspace_bytes : size_t(0), plan.bytes);
+  char* ws = static_cast<char*>(workspace);
+  kvs::DecodeArgs a{view(pool), layer, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+                    block_table, bt_stride, seq_lens, batch, num_decoders, num_q_heads, max_seq_len,
+                    scale * 1.4426950408889634f, reinterpret_cast<float*>(ws + plan.ml_offset),
+                    reinterpret_cast<float*>(ws + plan.acc_offset), plan, dev_status};
+  return launched(kvs::launch_decode(a, stream), "shared_kv_decode");
+}
+
+int partial_prefill_extend(const kvs_pool* pool, int32_t layer, const void* q, const void* k_new,
+                           const void* v_new, void* out, const int32_t* cu_new,
+                           const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                           int32_t batch, int32_t num_q_heads, int32_t total_new, int32_t max_new,
+                           int32_t max_seq_len, float scale, int32_t* dev_status, hipStream_t stream) {
+  int s = check_pool(pool, layer);
+  if (s) return s;
+  if (!q || !k_new || !v_new || !out || !cu_new || !block_table || !seq_lens)
+    return fail(KVS_EINVAL, "partial_prefill_extend: a required pointer is NULL");
+  if ((s = check_table(batch, bt_stride, max_seq_len))) return s;
+  if (num_q_heads <= 0 || max_new <= 0 || total_new < 0)
+    return fail(KVS_EINVAL, "partial_prefill_extend: num_q_heads %d, max_new %d must be >= 1",
+                num_q_heads, max_new);
+  if (max_new > max_seq_len)
+    return fail(KVS_ERANGE, "partial_prefill_extend: max_new %d exceeds max_seq_len %d", max_new,
+                max_seq_len);
+  if (num_q_heads % pool->num_kv_heads)
+    return fail(KVS_EUNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                pool->num_kv_heads);
+  if (!(scale > 0.f) || scale != scale)
+    return fail(KVS_EINVAL, "partial_prefill_extend: scale must be a positive number");
+  kvs::AppendArgs ap{view(pool), layer, static_cast<const uint16_t*>(k_new),
+                     static_cast<const uint16_t*>(v_new), cu_new, block_table, bt_stride, seq_lens,
+                     batch, total_new, max_new, max_seq_len, dev_status};
+  if ((s = launched(kvs::launch_append(ap, stream), "partial_prefill_extend (append)"))) return s;
+  kvs::ExtendArgs a{view(pool), layer, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+                    cu_new, block_table, bt_stride, seq_lens, batch, num_q_heads, total_new, max_new,
+                    max_seq_len, scale * 1.4426950408889634f, dev_status};
+  return launched(kvs::launch_extend(a, stream), "partial_prefill_extend");
+}
+
+}  // extern "C"

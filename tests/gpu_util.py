@@ -1,0 +1,90 @@
+"""Helpers for the GPU parity tests: host arrays <-> device tensors, pool setup."""
+import numpy as np
+
+from cross_model_shared_amd import binding
+from cross_model_shared_amd import workload as wlmod
+
+POISON_BIG = 0x4480   # bf16 1024.0: a wrongly read slot dominates any score/value
+POISON_NAN = 0x7FC0   # bf16 quiet NaN: a wrongly read slot poisons the output
+
+
+def dev_bf16(bits: np.ndarray):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16)).cuda().view(
+        torch.bfloat16)
+
+
+def dev_i32(x):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+
+def host_bits(t) -> np.ndarray:
+    import torch
+
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host_f64(t) -> np.ndarray:
+    import torch
+
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def pool_bits(pool: binding.Pool) -> np.ndarray:
+    return pool.data.cpu().numpy().view(np.uint16)
+
+
+def status_tensor():
+    import torch
+
+    return torch.zeros(1, dtype=torch.int32, device="cuda")
+
+
+def sync():
+    import torch
+
+    torch.cuda.synchronize()
+
+
+def make_decode_case(lens, N, Hkv, G, D, seed, std=1.0, layers=1, layer=0, poison=POISON_BIG,
+                     spare_frac=0.05):
+    """Pool (GPU, via kv_pool_append) holding each session's logical K/V, plus queries.
+
+    Returns a dict with host arrays (bits) for the oracle and device tensors.
+    """
+    rng = np.random.default_rng(seed)
+    bt, num_pages = wlmod.build_block_table(lens, seed, spare_frac=spare_frac)
+    K = [wlmod.draw_bf16(rng, (L, Hkv, D), std) for L in lens]
+    V = [wlmod.draw_bf16(rng, (L, Hkv, D), std) for L in lens]
+    q = wlmod.draw_bf16(rng, (len(lens), N, Hkv * G, D), std)
+    kk, cu = wlmod.concat_rows(K)
+    vv, _ = wlmod.concat_rows(V)
+    pool = binding.Pool(layers, num_pages, Hkv, D, fill=np.int16(np.uint16(poison).view(np.int16)))
+    st = status_tensor()
+    max_len = max(max(lens), 1)
+    if kk.shape[0]:
+        binding.append(pool, layer, dev_bf16(kk), dev_bf16(vv), dev_i32(cu), dev_i32(bt),
+                       dev_i32(np.zeros(len(lens))), max_new=max_len, max_seq_len=max_len, dev_status=st)
+    return dict(lens=list(lens), N=N, Hkv=Hkv, G=G, D=D, bt=bt, num_pages=num_pages, K=K, V=V, q=q,
+                kk=kk, vv=vv, cu=cu, pool=pool, status=st, layers=layers, layer=layer, poison=poison)
+
+
+def run_decode(case, q_bits=None, lens=None, bt=None, max_seq_len=None, scale=None):
+    import torch
+
+    q_bits = case["q"] if q_bits is None else q_bits
+    lens = case["lens"] if lens is None else lens
+    bt = case["bt"] if bt is None else bt
+    B, N, Hq, D = q_bits.shape
+    msl = max(max(lens), 1) if max_seq_len is None else max_seq_len
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    ws = torch.zeros(binding.decode_workspace_bytes(B, N, Hq, case["Hkv"], D, msl), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device="cuda")
+    binding.decode(case["pool"], case["layer"], dev_bf16(q_bits), out, dev_i32(bt), dev_i32(lens), msl,
+                   scale, ws, dev_status=case["status"])
+    sync()
+    return out

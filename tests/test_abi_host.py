@@ -1,0 +1,140 @@
+"""The C ABI on the host: symbols, sizes, and argument checks (no GPU needed).
+
+Every call below fails a host-side check, so nothing is ever enqueued; the
+pointers are placeholders that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from cross_model_shared_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.load()
+
+
+def header_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert {"kv_pool_append", "shared_kv_decode", "partial_prefill_extend", "kvs_pool_bytes",
+            "shared_kv_decode_workspace_bytes", "kvs_last_error", "kvs_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert b"gfx950" in L.kvs_version()
+
+
+def test_pool_bytes(L):
+    assert L.kvs_pool_bytes(36, 1000, 8, 128, 16) == 36 * 1000 * 8 * 2 * 16 * 128 * 2
+    assert L.kvs_pool_bytes(1, 0, 8, 128, 16) == 0
+    assert L.kvs_pool_bytes(-1, 10, 8, 128, 16) == 0
+
+
+def test_workspace_bytes_depend_on_bounds_not_device(L):
+    a = L.shared_kv_decode_workspace_bytes(64, 8, 32, 8, 128, 16384)
+    b = L.shared_kv_decode_workspace_bytes(64, 8, 32, 8, 128, 16384)
+    assert a == b > 0
+    # partials: (m, l) and a D-vector per row and split; at least one split per unit
+    assert a >= 64 * 8 * 32 * (128 + 2) * 4
+    assert L.shared_kv_decode_workspace_bytes(2, 2, 8, 3, 64, 100) == 0   # 8 % 3 != 0
+    assert L.shared_kv_decode_workspace_bytes(0, 2, 8, 2, 64, 100) == 0
+
+
+def pool(data=FAKE, layers=1, pages=8, heads=2, dim=64, page=16):
+    return binding.KvsPool(data.value if data is not None else None, layers, pages, heads, dim, page)
+
+
+def call_decode(L, p, layer=0, q=FAKE, out=FAKE, bt=FAKE, stride=4, lens=FAKE, batch=2, N=2, Hq=8,
+                msl=64, scale=0.125, ws=FAKE, wsb=1 << 30):
+    return L.shared_kv_decode(ctypes.byref(p), layer, q, out, bt, stride, lens, batch, N, Hq, msl, scale, ws,
+                              wsb, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=pool(data=None)), binding.KVS_EINVAL),
+    (dict(p=pool(page=32)), binding.KVS_EUNSUPPORTED),
+    (dict(p=pool(dim=96)), binding.KVS_EUNSUPPORTED),
+    (dict(p=pool(), layer=1), binding.KVS_ERANGE),
+    (dict(p=pool(), layer=-1), binding.KVS_ERANGE),
+    (dict(p=pool(), q=None), binding.KVS_EINVAL),
+    (dict(p=pool(), out=None), binding.KVS_EINVAL),
+    (dict(p=pool(), bt=None), binding.KVS_EINVAL),
+    (dict(p=pool(), lens=None), binding.KVS_EINVAL),
+    (dict(p=pool(), batch=0), binding.KVS_EINVAL),
+    (dict(p=pool(), N=0), binding.KVS_EINVAL),
+    (dict(p=pool(), Hq=7), binding.KVS_EUNSUPPORTED),
+    (dict(p=pool(), msl=65), binding.KVS_ERANGE),          # > bt_stride * 16
+    (dict(p=pool(), scale=0.0), binding.KVS_EINVAL),
+    (dict(p=pool(), ws=None), binding.KVS_EWORKSPACE),
+    (dict(p=pool(), wsb=16), binding.KVS_EWORKSPACE),
+])
+def test_decode_host_checks(L, kw, status):
+    p = kw.pop("p")
+    assert call_decode(L, p, **kw) == status
+    assert binding.last_error()
+
+
+def call_append(L, p, layer=0, k=FAKE, v=FAKE, cu=FAKE, bt=FAKE, stride=4, lens=FAKE, batch=2, total=10,
+                max_new=8, msl=64):
+    return L.kv_pool_append(ctypes.byref(p), layer, k, v, cu, bt, stride, lens, batch, total, max_new, msl,
+                            None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=pool(page=8)), binding.KVS_EUNSUPPORTED),
+    (dict(p=pool(heads=0)), binding.KVS_EINVAL),
+    (dict(p=pool(), k=None), binding.KVS_EINVAL),
+    (dict(p=pool(), cu=None), binding.KVS_EINVAL),
+    (dict(p=pool(), max_new=0), binding.KVS_EINVAL),
+    (dict(p=pool(), total=-1), binding.KVS_EINVAL),
+    (dict(p=pool(), max_new=65), binding.KVS_ERANGE),
+    (dict(p=pool(), msl=100), binding.KVS_ERANGE),
+    (dict(p=pool(), stride=0), binding.KVS_EINVAL),
+    (dict(p=pool(layers=2), layer=2), binding.KVS_ERANGE),
+])
+def test_append_host_checks(L, kw, status):
+    p = kw.pop("p")
+    assert call_append(L, p, **kw) == status
+
+
+def call_extend(L, p, q=FAKE, k=FAKE, v=FAKE, out=FAKE, cu=FAKE, bt=FAKE, stride=4, lens=FAKE, batch=2,
+                Hq=8, total=10, max_new=8, msl=64, scale=0.125):
+    return L.partial_prefill_extend(ctypes.byref(p), 0, q, k, v, out, cu, bt, stride, lens, batch, Hq, total,
+                                    max_new, msl, scale, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=pool(dim=256)), binding.KVS_EUNSUPPORTED),
+    (dict(p=pool(), q=None), binding.KVS_EINVAL),
+    (dict(p=pool(), out=None), binding.KVS_EINVAL),
+    (dict(p=pool(), Hq=5), binding.KVS_EUNSUPPORTED),
+    (dict(p=pool(), max_new=0), binding.KVS_EINVAL),
+    (dict(p=pool(), msl=1000), binding.KVS_ERANGE),
+    (dict(p=pool(), scale=float("nan")), binding.KVS_EINVAL),
+    (dict(p=pool(), batch=-3), binding.KVS_EINVAL),
+])
+def test_extend_host_checks(L, kw, status):
+    p = kw.pop("p")
+    assert call_extend(L, p, **kw) == status
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    with pytest.raises(ValueError, match="GPU tensor"):
+        binding._ptr(torch.zeros(4), "x")
