@@ -6,16 +6,23 @@
 // P V into O^T.  The QK^T result layout (lane l holds tokens 4*(l/16)+j of row
 // l%16) is exactly the B-operand layout of the 16x16x16 PV step, so the
 // probabilities go from one matrix-core step to the next without a shuffle.
+//
+// The running maximum is only moved when a page's maximum exceeds it by more
+// than 2^kLazyLog2 (in the log2 domain): probabilities then stay below 2^8 in
+// fp32, and the accumulators are rescaled only on the rare pages that move it.
+// Any reference point gives the same softmax, as long as acc and l share it.
 #pragma once
 
 #include "kvs_device.h"
 
 namespace kvs {
 
+constexpr float kLazyLog2 = 8.0f;
+
 template <int D, int NB>
 struct RowState {
   f32x4 acc[NB][D / 16];  // O^T: acc[cb][dblk][j] = O[row 16cb + lane%16][16 dblk + 4(lane/16) + j]
-  float m[NB];            // running max of scaled scores (log2 domain), per row
+  float m[NB];            // reference max of scaled scores (log2 domain), per row
   float l[NB];            // running sum of exp2(s - m) over this lane's slots
   __device__ __forceinline__ void init() {
 #pragma unroll
@@ -50,35 +57,52 @@ __device__ __forceinline__ void attend_page(RowState<D, NB>& st, const QFrag<D, 
     for (int i = 0; i < D / 32; ++i) vf[i] = mask_v_slab(vf[i], lane, nvalid);
   }
   const int s0 = 4 * (lane >> 4);
+  f32x4 s[NB];
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    s[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) s = mma_16x16x32(kf[i], qf.q[cb][i], s);
+    for (int i = 0; i < D / 32; ++i) s[cb] = mma_16x16x32(kf[i], qf.q[cb][i], s[cb]);
+  }
+  float alpha[NB];
+  bool any_move = false;
+  u32x2 pb[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
     float x[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      x[j] = s[j] * scale_log2;
+      x[j] = s[cb][j] * scale_log2;
       if (masked) x[j] = (s0 + j < lim[cb]) ? x[j] : -INFINITY;
     }
     float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     tmax = wave_max_across_quads(tmax);
-    const float m_new = fmaxf(st.m[cb], tmax);
-    // m_new is -inf only when the row has seen no key yet and none here: keep zeros
+    const float m_old = st.m[cb];
+    // move the reference only when the page max exceeds it by more than 2^kLazyLog2
+    const bool move = tmax > m_old + kLazyLog2;   // also true for the first seen key
+    const float m_new = move ? tmax : m_old;
+    any_move |= move;
+    alpha[cb] = move ? exp2f(m_old - m_new) : 1.f;  // exp2(-inf) = 0 on the first move
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(st.m[cb] - m_use);
     float p[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) p[j] = exp2f(x[j] - m_use);
-    st.l[cb] = st.l[cb] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    st.l[cb] = st.l[cb] * alpha[cb] + ((p[0] + p[1]) + (p[2] + p[3]));
     st.m[cb] = m_new;
+    pb[cb] = pack_bf16x4(p[0], p[1], p[2], p[3]);
+  }
+  if (__builtin_amdgcn_ballot_w64(any_move)) {
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) st.acc[cb][i] *= alpha;
-    const u32x2 pb = pack_bf16x4(p[0], p[1], p[2], p[3]);
+    for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      st.acc[cb][2 * i] = mma_16x16x16(u32x2{vf[i][0], vf[i][1]}, pb, st.acc[cb][2 * i]);
-      st.acc[cb][2 * i + 1] = mma_16x16x16(u32x2{vf[i][2], vf[i][3]}, pb, st.acc[cb][2 * i + 1]);
+      for (int i = 0; i < D / 16; ++i) st.acc[cb][i] *= alpha[cb];
+  }
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      st.acc[cb][2 * i] = mma_16x16x16(u32x2{vf[i][0], vf[i][1]}, pb[cb], st.acc[cb][2 * i]);
+      st.acc[cb][2 * i + 1] = mma_16x16x16(u32x2{vf[i][2], vf[i][3]}, pb[cb], st.acc[cb][2 * i + 1]);
     }
   }
 }

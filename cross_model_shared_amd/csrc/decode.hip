@@ -2,15 +2,19 @@
 //
 // ICaRus (Key design 3) runs the queries of every party that reads the same KV
 // side by side along the head dimension so the KV is read once.  Here all
-// R = N*G query rows of a KV head sit in the N side of the matrix-core steps of
-// one wave, so each (page, head) tile is streamed from HBM exactly once per call
-// whatever N is.  Work split:
-//   grid (split, KV head x row group, session), 4 waves per workgroup;
-//   a workgroup takes split_pages consecutive logical pages of one session,
-//   wave w takes pages w, w+4, ... of them with its own online softmax;
-//   the 4 waves' partial softmax states are merged through LDS, then either the
-//   output is written (one split) or the partial (m, l, acc) goes to the
-//   workspace and decode_combine_kernel merges the splits.
+// R = N*G query rows of a KV head sit on the N side of the matrix-core steps of
+// one wave, so each (page, KV head) tile streams from HBM exactly once per call
+// whatever N is.
+//
+// Work split (stream-K over pages): the tiles of every (KV head, row group,
+// session) unit are laid end to end — unit order (KV head, row group) then
+// session, pages in logical order — and the resulting list is cut into one
+// contiguous, equal share per wave of a persistent grid (one 4-wave workgroup
+// per CU).  A wave streams its share through a per-wave LDS ring with direct
+// global->LDS 16-byte loads (S pages in flight, no registers held by loads),
+// runs the page step of attn_core.h, and at every unit boundary either writes
+// the final output (unit wholly inside its share) or its partial softmax state
+// (m, l, acc) for decode_combine_kernel (unit crossing a share boundary).
 #include "attn_core.h"
 #include "kvs_internal.h"
 
@@ -20,49 +24,86 @@ namespace {
 
 constexpr int kWaves = 4;
 
+// s_waitcnt with vmcnt = VM and the other counters left alone (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] in bits 15:14).
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until at most `pages_after` pages' worth of ring loads are outstanding.
+template <int SLABS, int S>
+__device__ __forceinline__ void wait_ring(int pages_after) {
+  static_assert(S <= 8 && SLABS * (S - 1) < 64, "ring depth vs vmcnt range");
+  switch (pages_after) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<SLABS * 1 < 64 ? SLABS * 1 : 0>(); break;
+    case 2: wait_vmcnt<SLABS * 2 < 64 ? SLABS * 2 : 0>(); break;
+    case 3: wait_vmcnt<SLABS * 3 < 64 ? SLABS * 3 : 0>(); break;
+    case 4: wait_vmcnt<SLABS * 4 < 64 ? SLABS * 4 : 0>(); break;
+    case 5: wait_vmcnt<SLABS * 5 < 64 ? SLABS * 5 : 0>(); break;
+    case 6: wait_vmcnt<SLABS * 6 < 64 ? SLABS * 6 : 0>(); break;
+    default: wait_vmcnt<SLABS * 7 < 64 ? SLABS * 7 : 0>(); break;
+  }
+}
+
+__device__ __forceinline__ int clamp_len(int L, int max_len) { return L < 0 ? 0 : (L > max_len ? max_len : L); }
+
+// Position in the tile list: unit (gr = KV head * rowgroups + row group, session b), page.
+struct Walker {
+  int gr, b, page, npg;
+};
+
+__device__ __forceinline__ int read_cum(const int* cum, int i) {
+  return __builtin_amdgcn_readfirstlane(cum[i]);
+}
+
+// First nonempty session at or after b (B if none).
+__device__ __forceinline__ int next_nonempty(const int* cum, int b, int B) {
+  while (b < B && read_cum(cum, b + 1) == read_cum(cum, b)) ++b;
+  return b;
+}
+
+__device__ __forceinline__ Walker seek(const int* cum, int B, int Ptot, int64_t tau) {
+  Walker w;
+  w.gr = int(tau / Ptot);
+  const int r = int(tau % Ptot);
+  int lo = 0, hi = B;  // largest b with cum[b] <= r, among b < B
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (read_cum(cum, mid) <= r) lo = mid;
+    else hi = mid;
+  }
+  lo = next_nonempty(cum, lo, B);  // cum[b] <= r < cum[b+1] skips empty sessions
+  w.b = lo;
+  w.page = r - read_cum(cum, lo);
+  w.npg = read_cum(cum, lo + 1) - read_cum(cum, lo);
+  return w;
+}
+
+__device__ __forceinline__ void advance(Walker& w, const int* cum, int B) {
+  if (++w.page < w.npg) return;
+  w.page = 0;
+  int b = next_nonempty(cum, w.b + 1, B);
+  if (b >= B) {
+    ++w.gr;
+    b = next_nonempty(cum, 0, B);
+  }
+  w.b = b;
+  w.npg = b < B ? read_cum(cum, b + 1) - read_cum(cum, b) : 0;
+}
+
+__device__ __forceinline__ int64_t share_start(int k, int64_t T, int W) { return int64_t(k) * T / W; }
+
 template <int D, int NB>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
-  constexpr int RG = 16 * NB;
-  const DecodePlan& pl = a.plan;
-  const int split = blockIdx.x;
-  const int Hkv = a.pool.num_kv_heads;
-  const int g = blockIdx.y % Hkv;
-  const int rg = blockIdx.y / Hkv;
-  const int b = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int G = a.num_q_heads / Hkv;
-
-  int L = a.seq_lens[b];
-  if (L < 0 || L > a.max_seq_len) {
-    if (threadIdx.x == 0 && split == 0 && blockIdx.y == 0) flag_error(a.dev_status, 2);
-    L = L < 0 ? 0 : a.max_seq_len;
-  }
-  const int npages = (L + kPage - 1) / kPage;
-  const int p_begin = split * pl.split_pages;
-  const int row0 = rg * RG;
-
-  if (L == 0) {  // softmax over nothing: zero output, written by split 0
-    if (split != 0) return;
-    for (int e = threadIdx.x; e < RG * (D / 8); e += 256) {
-      const int r = row0 + e / (D / 8);
-      if (r >= pl.rows) continue;
-      const int n = r / G, h = g * G + r % G;
-      uint16_t* o = a.out + ((int64_t(b) * a.num_decoders + n) * a.num_q_heads + h) * D;
-      reinterpret_cast<u32x4*>(o)[e % (D / 8)] = u32x4{0u, 0u, 0u, 0u};
-    }
-    return;
-  }
-  if (p_begin >= npages) return;
-  const int p_end = min(npages, p_begin + pl.split_pages);
-  const int nsplits = (npages + pl.split_pages - 1) / pl.split_pages;
-
-  // query operands of this row group (zero rows past R)
-  QFrag<D, NB> qf;
+__device__ __forceinline__ void load_q(QFrag<D, NB>& qf, const DecodeArgs& a, int b, int g, int rg,
+                                       int lane) {
+  const int G = a.num_q_heads / a.pool.num_kv_heads;
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
-    const int r = row0 + cb * 16 + (lane & 15);
-    const bool valid = r < pl.rows;
+    const int r = rg * 16 * NB + cb * 16 + (lane & 15);
+    const bool valid = r < a.plan.rows;
     const int n = valid ? r / G : 0, h = valid ? g * G + r % G : 0;
     const uint16_t* qrow = a.q + ((int64_t(b) * a.num_decoders + n) * a.num_q_heads + h) * D;
 #pragma unroll
@@ -70,171 +111,232 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       qf.q[cb][i] = valid ? *reinterpret_cast<const u32x4*>(qrow + 32 * i + 8 * (lane >> 4))
                           : u32x4{0u, 0u, 0u, 0u};
   }
+}
 
-  RowState<D, NB> st;
-  st.init();
-  const int32_t* btrow = a.bt + int64_t(b) * a.bt_stride;
-  const int num_pages = a.pool.num_pages;
-
-  u32x4 kf[D / 32], vf[D / 32], kn[D / 32], vn[D / 32];
-  int p = p_begin + wave;
-  int pid = p < p_end ? btrow[p] : -1;
-  bool ok = pid >= 0 && pid < num_pages;
-  if (p < p_end && !ok) flag_error(a.dev_status, 1);
-  if (ok) {
-    const uint16_t* tile = a.pool.data + tile_offset(a.layer, pid, g, num_pages, Hkv, D);
+template <int D, int NB>
+__device__ __forceinline__ void write_rows(const DecodeArgs& a, const RowState<D, NB>& st, int b, int g,
+                                           int rg, int lane) {
+  const int G = a.num_q_heads / a.pool.num_kv_heads;
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      kf[i] = load_k_slab(tile, i, lane);
-      vf[i] = load_v_slab(tile, D, i, lane);
+  for (int cb = 0; cb < NB; ++cb) {
+    const float l = wave_sum_across_quads(st.l[cb]);
+    const int r = rg * 16 * NB + cb * 16 + (lane & 15);
+    if (r >= a.plan.rows) continue;
+    const int n = r / G, h = g * G + r % G;
+    uint16_t* o = a.out + ((int64_t(b) * a.num_decoders + n) * a.num_q_heads + h) * D;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      const f32x4 v = st.acc[cb][i] * inv;
+      *reinterpret_cast<u32x2*>(o + 16 * i + 4 * (lane >> 4)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
     }
   }
-  while (p < p_end) {
-    // issue the next page's loads before computing this one
-    const int pn = p + kWaves;
-    const int pidn = pn < p_end ? btrow[pn] : -1;
-    const bool okn = pidn >= 0 && pidn < num_pages;
-    if (pn < p_end && !okn) flag_error(a.dev_status, 1);
-    if (okn) {
-      const uint16_t* tile = a.pool.data + tile_offset(a.layer, pidn, g, num_pages, Hkv, D);
+}
+
+template <int D, int NB>
+__device__ __forceinline__ void write_partial(const DecodeArgs& a, const RowState<D, NB>& st, int slot,
+                                              int lane) {
+  constexpr int RG = 16 * NB;
+  float* acc = a.ws_acc + int64_t(slot) * RG * D;
+  float* ml = a.ws_ml + int64_t(slot) * RG * 2;
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) {
-        kn[i] = load_k_slab(tile, i, lane);
-        vn[i] = load_v_slab(tile, D, i, lane);
+  for (int cb = 0; cb < NB; ++cb) {
+    const float l = wave_sum_across_quads(st.l[cb]);
+    const int r = cb * 16 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i)
+      *reinterpret_cast<f32x4*>(acc + r * D + 16 * i + 4 * (lane >> 4)) = st.acc[cb][i];
+    if (lane < 16) {
+      ml[r * 2 + 0] = st.m[cb];
+      ml[r * 2 + 1] = l;
+    }
+  }
+}
+
+template <int D, int NB, int S>
+__global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
+  constexpr int SLABS = D / 16;  // 1 KiB slabs per (page, head) tile: K slabs then V slabs
+  __shared__ u32x4 ring[kWaves][S][SLABS * 64];
+  __shared__ int cum_s[kDecodeMaxBatch + 1];
+  __shared__ int part_s[256];
+
+  const int lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: lets the compiler
+  const int B = a.batch, Hkv = a.pool.num_kv_heads, RGs = a.plan.rowgroups;  // use scalar loads
+
+  // ---- pages per session and their exclusive prefix sum (every workgroup) ----
+  const int chunk = (B + 255) / 256;
+  int local = 0;
+  for (int i = 0; i < chunk; ++i) {
+    const int b = tid * chunk + i;
+    if (b < B) {
+      const int L = a.seq_lens[b];
+      if ((L < 0 || L > a.max_seq_len) && blockIdx.x == 0) flag_error(a.dev_status, KVS_DEV_BAD_LEN_BIT);
+      local += (clamp_len(L, a.max_seq_len) + kPage - 1) / kPage;
+    }
+  }
+  part_s[tid] = local;
+  __syncthreads();
+  if (wave == 0) {
+    int v[4], s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = part_s[lane * 4 + i]; s += v[i]; }
+    int incl = s;  // inclusive scan over lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    int run = incl - s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { part_s[lane * 4 + i] = run; run += v[i]; }
+  }
+  __syncthreads();
+  {
+    int run = part_s[tid];
+    for (int i = 0; i < chunk; ++i) {
+      const int b = tid * chunk + i;
+      if (b < B) {
+        cum_s[b] = run;
+        run += (clamp_len(a.seq_lens[b], a.max_seq_len) + kPage - 1) / kPage;
       }
     }
-    if (ok) {
-      const int nvalid = min(kPage, L - p * kPage);
+    if (tid == 255) cum_s[B] = run;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int b = tid; b <= B; b += 256) a.ws_cum[b] = cum_s[b];
+  __builtin_amdgcn_s_waitcnt(0);  // nothing outstanding before the ring starts
+
+  const int Ptot = cum_s[B];
+  const int64_t T = int64_t(Ptot) * Hkv * RGs;
+  const int W = gridDim.x * kWaves;
+  const int k = blockIdx.x * kWaves + wave;
+  const int64_t tau0 = share_start(k, T, W), tau1 = share_start(k + 1, T, W);
+  if (tau0 >= tau1) return;  // no barriers follow
+  const int n = int(tau1 - tau0);
+
+  const int num_pages = a.pool.num_pages;
+  uint32_t bad = 0;  // ring slots whose page id was out of range
+
+  Walker iw = seek(cum_s, B, Ptot, tau0);
+  Walker cw = iw;
+  auto issue = [&](int slot) {
+    const int g = iw.gr / RGs;
+    int pid = load_uniform(a.bt + int64_t(iw.b) * a.bt_stride + iw.page);
+    const bool ok = pid >= 0 && pid < num_pages;
+    bad = ok ? (bad & ~(1u << slot)) : (bad | (1u << slot));
+    if (!ok) {
+      flag_error(a.dev_status, KVS_DEV_BAD_PAGE_BIT);
+      __builtin_amdgcn_s_waitcnt(0);
+      pid = 0;  // stream a harmless in-range page, skip it at compute time
+    }
+    const u32x4* tile = reinterpret_cast<const u32x4*>(a.pool.data + tile_offset(a.layer, pid, g, num_pages, Hkv, D));
+#pragma unroll
+    for (int s = 0; s < SLABS; ++s)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + s * 64 + lane),
+                                       (__attribute__((address_space(3))) void*)(&ring[wave][slot][s * 64]),
+                                       16, 0, 0);
+    advance(iw, cum_s, B);
+  };
+
+  QFrag<D, NB> qf;
+  RowState<D, NB> st;
+  st.init();
+  load_q<D, NB>(qf, a, cw.b, cw.gr / RGs, cw.gr % RGs, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  int64_t unit_begin = int64_t(cw.gr) * Ptot + cum_s[cw.b];  // first tile of the current unit
+
+#pragma unroll 1
+  for (int j = 0; j < S - 1 && j < n; ++j) issue(j);
+
+#pragma unroll 1
+  for (int j = 0; j < n; ++j) {
+    const int slot = j % S;
+    if (j + S - 1 < n) issue((j + S - 1) % S);
+    wait_ring<SLABS, S>(min(S - 1, n - 1 - j));
+    if (!((bad >> slot) & 1u)) {
+      u32x4 kf[D / 32], vf[D / 32];
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) {
+        kf[i] = ring[wave][slot][i * 64 + lane];
+        vf[i] = ring[wave][slot][(D / 32 + i) * 64 + lane];
+      }
+      const int L = clamp_len(load_uniform(a.seq_lens + cw.b), a.max_seq_len);
+      const int nvalid = min(kPage, L - cw.page * kPage);
       int lim[NB];
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) lim[cb] = nvalid;
       attend_page<D, NB>(st, qf, kf, vf, a.scale_log2, nvalid < kPage, lim, nvalid, lane);
     }
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      kf[i] = kn[i];
-      vf[i] = vn[i];
-    }
-    ok = okn;
-    p = pn;
-  }
-
-  // ---- merge the 4 waves' states (fixed order, so results are reproducible) ----
-  __shared__ float sm_m[kWaves][RG];
-  __shared__ float sm_l[kWaves][RG];
-  __shared__ f32x4 sm_acc[NB][D / 16][kWave];
-  float lrow[NB];
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb) lrow[cb] = wave_sum_across_quads(st.l[cb]);
-  if (lane < 16) {
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-      sm_m[wave][cb * 16 + lane] = st.m[cb];
-      sm_l[wave][cb * 16 + lane] = lrow[cb];
-    }
-  }
-  __syncthreads();
-  float mtot[NB], ltot[NB];
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb) {
-    const int r = cb * 16 + (lane & 15);
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][r]);
-    float lt = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm_m[w][r];
-      lt += (mw == -INFINITY) ? 0.f : sm_l[w][r] * exp2f(mw - M);
-    }
-    mtot[cb] = M;
-    ltot[cb] = lt;
-    const float f = (st.m[cb] == -INFINITY) ? 0.f : exp2f(st.m[cb] - M);
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) st.acc[cb][i] *= f;
-  }
-#pragma unroll
-  for (int w = 0; w < kWaves - 1; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-        for (int i = 0; i < D / 16; ++i)
-          sm_acc[cb][i][lane] = (w == 0) ? st.acc[cb][i] : sm_acc[cb][i][lane] + st.acc[cb][i];
-    }
-    __syncthreads();
-  }
-  if (wave != kWaves - 1) return;
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) st.acc[cb][i] += sm_acc[cb][i][lane];
-
-  if (nsplits == 1) {
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-      const int r = row0 + cb * 16 + (lane & 15);
-      if (r >= pl.rows) continue;
-      const int n = r / G, h = g * G + r % G;
-      uint16_t* o = a.out + ((int64_t(b) * a.num_decoders + n) * a.num_q_heads + h) * D;
-      const float inv = ltot[cb] > 0.f ? 1.f / ltot[cb] : 0.f;
-#pragma unroll
-      for (int i = 0; i < D / 16; ++i) {
-        const f32x4 v = st.acc[cb][i] * inv;
-        *reinterpret_cast<u32x2*>(o + 16 * i + 4 * (lane >> 4)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+    const int cur_gr = cw.gr, cur_b = cw.b;
+    advance(cw, cum_s, B);
+    const bool last = (j == n - 1);
+    if (last || cw.gr != cur_gr || cw.b != cur_b) {
+      // unit (cur_gr, cur_b) ends here for this wave
+      const int64_t unit_end = unit_begin + (cum_s[cur_b + 1] - cum_s[cur_b]);
+      const bool before = unit_begin < tau0, after = unit_end > tau1;
+      if (!before && !after) {
+        write_rows<D, NB>(a, st, cur_b, cur_gr / RGs, cur_gr % RGs, lane);
+      } else {
+        write_partial<D, NB>(a, st, k * 2 + (before ? 0 : 1), lane);
       }
-    }
-    return;
-  }
-  const int64_t unit = (int64_t(b) * Hkv + g) * pl.rowgroups + rg;
-  const int64_t slot = unit * pl.max_splits + split;
-  float* wacc = a.ws_acc + slot * RG * D;
-  float* wml = a.ws_ml + slot * RG * 2;
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb) {
-    const int r = cb * 16 + (lane & 15);
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i)
-      *reinterpret_cast<f32x4*>(wacc + r * D + 16 * i + 4 * (lane >> 4)) = st.acc[cb][i];
-    if (lane < 16) {
-      wml[r * 2 + 0] = mtot[cb];
-      wml[r * 2 + 1] = ltot[cb];
+      if (!last) {
+        st.init();
+        load_q<D, NB>(qf, a, cw.b, cw.gr / RGs, cw.gr % RGs, lane);
+        __builtin_amdgcn_s_waitcnt(0);  // stores and q loads drained before the ring resumes
+        unit_begin = int64_t(cw.gr) * Ptot + cum_s[cw.b];
+      }
     }
   }
 }
 
-// Merge the split partials (m_s, l_s, acc_s) of one (session, KV head, row group):
+// Merge the partial states of units that cross share boundaries:
 // m* = max m_s, out = sum_s 2^(m_s - m*) acc_s / sum_s 2^(m_s - m*) l_s.
+// Also writes zeros for empty sessions (softmax over nothing).
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  const DecodePlan& pl = a.plan;
-  const int Hkv = a.pool.num_kv_heads;
-  const int g = blockIdx.x % Hkv;
-  const int rg = blockIdx.x / Hkv;
-  const int b = blockIdx.y;
+  const int B = a.batch, Hkv = a.pool.num_kv_heads, RGs = a.plan.rowgroups;
+  const int unit = blockIdx.x;  // (gr, b) with b fastest
+  const int b = unit % B, gr = unit / B;
+  const int g = gr / RGs, rg = gr % RGs;
+  const int RG = a.plan.rg_rows;
   const int G = a.num_q_heads / Hkv;
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
-  const int npages = (L + kPage - 1) / kPage;
-  const int nsplits = (npages + pl.split_pages - 1) / pl.split_pages;
-  if (nsplits <= 1) return;
-  const int RG = pl.rg_rows;
-  const int64_t unit = (int64_t(b) * Hkv + g) * pl.rowgroups + rg;
-  const float* ml = a.ws_ml + unit * pl.max_splits * RG * 2;
-  const float* acc = a.ws_acc + unit * pl.max_splits * RG * D;
+  const int Ptot = a.ws_cum[B];
+  const int npg = a.ws_cum[b + 1] - a.ws_cum[b];
+  const int W = a.plan.blocks * kWaves;
+  if (npg == 0) {
+    for (int e = threadIdx.x; e < RG * (D / 8); e += 256) {
+      const int r = rg * RG + e / (D / 8);
+      if (r >= a.plan.rows) continue;
+      const int n = r / G, h = g * G + r % G;
+      uint16_t* o = a.out + ((int64_t(b) * a.num_decoders + n) * a.num_q_heads + h) * D;
+      reinterpret_cast<u32x4*>(o)[e % (D / 8)] = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
+  const int64_t T = int64_t(Ptot) * Hkv * RGs;
+  const int64_t s_u = int64_t(gr) * Ptot + a.ws_cum[b], e_u = s_u + npg;
+  // share of tile t: floor(((t + 1) W - 1) / T)
+  const int k0 = int(((s_u + 1) * W - 1) / T), k1 = int((e_u * W - 1) / T);
+  if (k0 == k1) return;  // written directly by its wave
   for (int e = threadIdx.x; e < RG * (D / 4); e += 256) {
     const int rl = e / (D / 4), d4 = e % (D / 4);
     const int r = rg * RG + rl;
-    if (r >= pl.rows) continue;
+    if (r >= a.plan.rows) continue;
     float M = -INFINITY;
-    for (int s = 0; s < nsplits; ++s) M = fmaxf(M, ml[(s * RG + rl) * 2]);
+    for (int k = k0; k <= k1; ++k) {
+      const int slot = k * 2 + (k == k0 ? 1 : 0);
+      M = fmaxf(M, a.ws_ml[(int64_t(slot) * RG + rl) * 2]);
+    }
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-    for (int s = 0; s < nsplits; ++s) {
-      const float ms = ml[(s * RG + rl) * 2];
+    for (int k = k0; k <= k1; ++k) {
+      const int slot = k * 2 + (k == k0 ? 1 : 0);
+      const float ms = a.ws_ml[(int64_t(slot) * RG + rl) * 2];
       const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      den += w * ml[(s * RG + rl) * 2 + 1];
-      num += w * reinterpret_cast<const f32x4*>(acc + (int64_t(s) * RG + rl) * D)[d4];
+      den += w * a.ws_ml[(int64_t(slot) * RG + rl) * 2 + 1];
+      num += w * reinterpret_cast<const f32x4*>(a.ws_acc + (int64_t(slot) * RG + rl) * D)[d4];
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     const int n = r / G, h = g * G + r % G;
@@ -245,13 +347,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 
 template <int D, int NB>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  const DecodePlan& pl = a.plan;
-  dim3 grid(pl.max_splits, a.pool.num_kv_heads * pl.rowgroups, a.batch);
-  hipLaunchKernelGGL((decode_split_kernel<D, NB>), grid, dim3(256), 0, stream, a);
+  constexpr int S = D == 128 ? 4 : 8;  // 32 KiB of ring per wave
+  hipLaunchKernelGGL((decode_stream_kernel<D, NB, S>), dim3(a.plan.blocks), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pl.max_splits <= 1) return e;
-  dim3 cgrid(a.pool.num_kv_heads * pl.rowgroups, a.batch);
-  hipLaunchKernelGGL((decode_combine_kernel<D>), cgrid, dim3(256), 0, stream, a);
+  if (e != hipSuccess) return e;
+  const int units = a.pool.num_kv_heads * a.plan.rowgroups * a.batch;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(units), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

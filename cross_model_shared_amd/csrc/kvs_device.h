@@ -17,6 +17,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kPage = 16;
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
+// bits OR-ed into the caller's device status word (values of the C ABI enum)
+constexpr int KVS_DEV_BAD_PAGE_BIT = 1;
+constexpr int KVS_DEV_BAD_LEN_BIT = 2;
 
 // Element offset of the (layer, page, head) tile: K part (16*D) then V part (16*D).
 __device__ __forceinline__ int64_t tile_offset(int layer, int page, int head, int num_pages,
@@ -82,6 +85,14 @@ __device__ __forceinline__ u32x4 mask_v_slab(u32x4 v, int lane, int nvalid) {
   v[2] &= m0;
   v[3] &= m1;
   return v;
+}
+
+// Load through the constant address space: with a wave-uniform address this is
+// a scalar load (lgkmcnt), which keeps it out of the vector-memory counter that
+// paces the LDS ring.  Only for data that no kernel of the call writes.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
 }
 
 __device__ __forceinline__ void flag_error(int32_t* dev_status, int bits) {

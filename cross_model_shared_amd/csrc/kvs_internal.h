@@ -25,17 +25,20 @@ struct AppendArgs {
   int32_t* dev_status;
 };
 
+// Largest batch a decode call accepts (the per-session page prefix sum lives in LDS).
+constexpr int kDecodeMaxBatch = 4096;
+
 // How a decode call is cut into work: query rows per KV head are taken in row
-// groups of 16*nb (one wave holds them all), and each session's pages in splits
-// of split_pages pages (one workgroup each).
+// groups of 16*nb (one wave holds them all); the (page, KV head, row group)
+// tiles of all sessions are shared out evenly among the 4*blocks waves of a
+// persistent grid.  Each wave has two partial-state slots in the workspace.
 struct DecodePlan {
-  int rows;         // N * G query rows per KV head
-  int nb;           // 16-row column blocks per wave (1, 2 or 4)
-  int rg_rows;      // 16 * nb
-  int rowgroups;    // ceil(rows / rg_rows)
-  int split_pages;  // pages per workgroup (multiple of 4: one share per wave)
-  int max_splits;   // ceil(ceil(max_seq_len/16) / split_pages)
-  size_t ml_offset, acc_offset, bytes;
+  int rows;       // N * G query rows per KV head
+  int nb;         // 16-row column blocks per wave (1, 2 or 4)
+  int rg_rows;    // 16 * nb
+  int rowgroups;  // ceil(rows / rg_rows)
+  int blocks;     // workgroups of the persistent grid (one per CU)
+  size_t cum_offset, ml_offset, acc_offset, bytes;
 };
 
 DecodePlan plan_decode(int batch, int num_decoders, int num_q_heads, int num_kv_heads, int head_dim,
@@ -51,8 +54,9 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   int batch, num_decoders, num_q_heads, max_seq_len;
   float scale_log2;
-  float* ws_ml;
-  float* ws_acc;
+  int* ws_cum;    // [batch+1] page prefix sum, written by the decode kernel
+  float* ws_ml;   // [4*blocks*2][rg_rows][2] partial (m, l)
+  float* ws_acc;  // [4*blocks*2][rg_rows][D] partial acc
   DecodePlan plan;
   int32_t* dev_status;
 };

@@ -59,20 +59,8 @@ int launched(hipError_t e, const char* what) {
   return KVS_OK;
 }
 
-// Pages per decode workgroup.  Sized so that an upper bound of the work
-// (every session at max_seq_len) makes about kTargetBlocks workgroups: enough
-// to keep 256 CUs busy when real lengths are ragged, few enough that split
-// partials stay a small fraction of the KV bytes.  KVS_DECODE_SPLIT_PAGES
-// overrides it (tuning only; rounded up to a multiple of 4).
-int decode_split_pages(int64_t units, int max_pages) {
-  const char* env = getenv("KVS_DECODE_SPLIT_PAGES");
-  if (env && atoi(env) > 0) return (atoi(env) + 3) / 4 * 4;
-  constexpr int64_t kTargetBlocks = 8192;
-  int64_t sp = (units * max_pages + kTargetBlocks - 1) / kTargetBlocks;
-  if (sp < 16) sp = 16;
-  if (sp > 1024) sp = 1024;
-  return int((sp + 3) / 4 * 4);
-}
+// Workgroups of the persistent decode grid: one per CU of an MI355X (256 CUs).
+constexpr int kDecodeBlocks = 256;
 
 }  // namespace
 
@@ -80,19 +68,18 @@ namespace kvs {
 
 DecodePlan plan_decode(int batch, int num_decoders, int num_q_heads, int num_kv_heads, int head_dim,
                        int max_seq_len) {
+  (void)max_seq_len;
   DecodePlan p{};
   p.rows = num_decoders * (num_q_heads / num_kv_heads);
   p.nb = p.rows <= 16 ? 1 : (p.rows <= 32 ? 2 : 4);
   p.rg_rows = 16 * p.nb;
   p.rowgroups = (p.rows + p.rg_rows - 1) / p.rg_rows;
-  const int max_pages = (max_seq_len + 15) / 16;
-  const int64_t units = int64_t(batch) * num_kv_heads * p.rowgroups;
-  p.split_pages = decode_split_pages(units, max_pages < 1 ? 1 : max_pages);
-  p.max_splits = max_pages < 1 ? 1 : (max_pages + p.split_pages - 1) / p.split_pages;
-  const size_t slots = size_t(units) * p.max_splits;
-  p.ml_offset = 0;
-  size_t ml_bytes = slots * p.rg_rows * 2 * sizeof(float);
-  p.acc_offset = (ml_bytes + 255) / 256 * 256;
+  p.blocks = kDecodeBlocks;
+  const size_t slots = size_t(p.blocks) * 4 * 2;
+  auto align = [](size_t x) { return (x + 255) / 256 * 256; };
+  p.cum_offset = 0;
+  p.ml_offset = align(size_t(batch + 1) * sizeof(int));
+  p.acc_offset = p.ml_offset + align(slots * p.rg_rows * 2 * sizeof(float));
   p.bytes = p.acc_offset + slots * p.rg_rows * head_dim * sizeof(float);
   return p;
 }
@@ -135,8 +122,8 @@ int kv_pool_append(const kvs_pool* pool, int32_t layer, const void* k_new, const
 size_t shared_kv_decode_workspace_bytes(int32_t batch, int32_t num_decoders, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t max_seq_len) {
-  if (batch <= 0 || num_decoders <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      max_seq_len < 0 || num_q_heads % num_kv_heads)
+  if (batch <= 0 || batch > kvs::kDecodeMaxBatch || num_decoders <= 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || num_q_heads % num_kv_heads)
     return 0;
   return kvs::plan_decode(batch, num_decoders, num_q_heads, num_kv_heads, head_dim, max_seq_len).bytes;
 }
@@ -159,6 +146,8 @@ int shared_kv_decode(const kvs_pool* pool, int32_t layer, const void* q, void* o
                 pool->num_kv_heads);
   if (!(scale > 0.f) || scale != scale)
     return fail(KVS_EINVAL, "shared_kv_decode: scale must be a positive number");
+  if (batch > kvs::kDecodeMaxBatch)
+    return fail(KVS_EUNSUPPORTED, "shared_kv_decode: batch %d above %d", batch, kvs::kDecodeMaxBatch);
   kvs::DecodePlan plan = kvs::plan_decode(batch, num_decoders, num_q_heads, pool->num_kv_heads,
                                           pool->head_dim, max_seq_len);
   if (!workspace || workspace_bytes < plan.bytes)
@@ -167,7 +156,8 @@ int shared_kv_decode(const kvs_pool* pool, int32_t layer, const void* q, void* o
   char* ws = static_cast<char*>(workspace);
   kvs::DecodeArgs a{view(pool), layer, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
                     block_table, bt_stride, seq_lens, batch, num_decoders, num_q_heads, max_seq_len,
-                    scale * 1.4426950408889634f, reinterpret_cast<float*>(ws + plan.ml_offset),
+                    scale * 1.4426950408889634f, reinterpret_cast<int*>(ws + plan.cum_offset),
+                    reinterpret_cast<float*>(ws + plan.ml_offset),
                     reinterpret_cast<float*>(ws + plan.acc_offset), plan, dev_status};
   return launched(kvs::launch_decode(a, stream), "shared_kv_decode");
 }
