@@ -26,6 +26,8 @@ COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
     # packed fp32 arithmetic stays off in all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no NaN canonicalization around max/min: masked scores are -inf, never NaN
+    "-fno-honor-nans",
     "-I", os.path.join(ROOT, "include"),
 ]
 

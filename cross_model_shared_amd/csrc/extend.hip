@@ -3,58 +3,210 @@
 // partial prefill of the new tokens only; section 4: prefill is compute-bound).
 //
 // Rows of one (session, KV head) are the chunk's (token i, query head of the
-// group) pairs, token-major, so a 16-row block spans only a few positions and
-// the causal diagonal touches few pages.  A workgroup holds 128 rows (4 waves x
-// 32 rows) and walks the session's pages in order; every step is the shared
-// matrix-core page step.  Workgroups are laid out so that all row blocks of one
-// (session, KV head) land on the same XCD: hardware hands workgroup ids to the 8
-// XCDs round robin, and keeping a KV head's pages in one L2 lets its 16+ row
-// blocks reuse them there.
-#include "attn_core.h"
+// group) pairs, token-major, so a 16-row block spans few positions and the
+// causal diagonal touches few pages.  A workgroup holds 256 rows (4 waves x 64
+// rows, Q kept in registers) and walks the session's keys in blocks of 32 (two
+// pages).  Blocks are staged once per workgroup in LDS by direct global->LDS
+// 16-byte loads, kLook blocks ahead, and every wave reads its matrix-core
+// operands from there: per 32 keys a wave does 32 QK^T and 32 PV steps of
+// 16x16x32 bf16.  The QK^T of block k+1 is issued before the softmax of block k
+// so matrix and vector work of one wave can overlap.
+//
+// Workgroups are laid out so that all row blocks of one (session, KV head) land
+// on the same XCD: hardware hands workgroup ids to the 8 XCDs round robin, and
+// keeping a KV head's pages in one L2 lets its row blocks share them there.
+#include "kvs_device.h"
 #include "kvs_internal.h"
+
+#include <type_traits>
 
 namespace kvs {
 
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kRowsPerWave = 32;
+constexpr int kNB = 4;                       // 16-row column blocks per wave
+constexpr int kRowsPerWave = 16 * kNB;
 constexpr int kRowsPerBlock = 4 * kRowsPerWave;
+constexpr int kStages = 6;                   // LDS ring of 32-key blocks
+constexpr int kLook = 4;                     // blocks in flight ahead of compute
+constexpr float kLazy = 8.0f;                // rescaling path: max moves when it grows by > 2^8
+constexpr float kSafeSum = 1.0e18f;          // ~2^60: fixed-reference sums stay below this
+
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int PER>
+__device__ __forceinline__ void wait_blocks(int blocks_after) {
+  switch (blocks_after) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<PER * 1>(); break;
+    case 2: wait_vmcnt<PER * 2>(); break;
+    default: wait_vmcnt<PER * 3>(); break;
+  }
+}
 
 template <int D>
-__global__ __launch_bounds__(256) void extend_kernel(ExtendArgs a, int row_blocks) {
-  constexpr int NB = 2;
+struct ExtendState {
+  f32x4 acc[kNB][D / 16];
+  float m[kNB], l[kNB];
+};
+
+// S^T for one 32-key block: s[h][cb] covers page h of the block, rows of column block cb.
+template <int D>
+__device__ __forceinline__ void qk_block(f32x4 (&s)[2][kNB], const u32x4 (&qf)[kNB][D / 32],
+                                         const u32x4* stage, int lane) {
+  constexpr int TILE = D * 4;  // u32x4 per (page, head) tile
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    u32x4 kf[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) kf[i] = stage[h * TILE + i * 64 + lane];
+#pragma unroll
+    for (int cb = 0; cb < kNB; ++cb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc = mma_16x16x32(kf[i], qf[cb][i], acc);
+      s[h][cb] = acc;
+    }
+  }
+}
+
+// Scores of one 32-key block for column block cb: 8 per lane (page 0 slots
+// s0..s0+3, then page 1), masked to -inf past each row's key limit.
+template <bool MASKED>
+__device__ __forceinline__ void block_scores(float (&x)[8], const f32x4 (&s)[2][kNB], int cb, int kbase,
+                                             int lim, int s0) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v = s[h][cb][j];
+      if (MASKED) v = (kbase + 16 * h + s0 + j < lim) ? v : -INFINITY;
+      x[4 * h + j] = v;
+    }
+}
+
+__device__ __forceinline__ u32x4 pack_p8(const float (&p)[8]) {
+  const u32x2 lo = pack_bf16x4(p[0], p[1], p[2], p[3]);
+  const u32x2 hi = pack_bf16x4(p[4], p[5], p[6], p[7]);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Softmax weights of one 32-key block against a FIXED per-row reference m
+// (set from the row's first block): p = 2^(s*c - m).  Moving the reference is
+// never needed for correctness, only to keep p inside fp32/bf16 range; weights
+// may exceed 1, and a row whose sum leaves the safe range (checked once, after
+// the loop) is recomputed by the rescaling variant below.  Keeping the
+// accumulators free of vector ops lets them stay in accumulation registers.
+template <int D, bool MASKED>
+__device__ __forceinline__ void softmax_fixed(ExtendState<D>& st, const f32x4 (&s)[2][kNB], u32x4 (&pb)[kNB],
+                                              float c, int kbase, const int (&lim_abs)[kNB], int s0) {
+#pragma unroll
+  for (int cb = 0; cb < kNB; ++cb) {
+    float x[8], p[8];
+    block_scores<MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
+    const float neg = -st.m[cb];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, neg));
+    st.l[cb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    pb[cb] = pack_p8(p);
+  }
+}
+
+// First block of a row: the reference is the block's row maximum.
+template <int D, bool MASKED>
+__device__ __forceinline__ void softmax_first(ExtendState<D>& st, const f32x4 (&s)[2][kNB], u32x4 (&pb)[kNB],
+                                              float c, int kbase, const int (&lim_abs)[kNB], int s0) {
+#pragma unroll
+  for (int cb = 0; cb < kNB; ++cb) {
+    float x[8];
+    block_scores<MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
+    const float t = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    const float m = wave_max_across_quads(t) * c;  // c > 0: the max commutes with the scale
+    st.m[cb] = (m == -INFINITY) ? 0.f : m;
+  }
+  softmax_fixed<D, MASKED>(st, s, pb, c, kbase, lim_abs, s0);
+}
+
+// Rescaling variant (the recomputation path): the reference follows the running
+// maximum, moved only when it grows by more than 2^kLazy, and the accumulators
+// are rescaled then.
+template <int D, bool MASKED>
+__device__ __forceinline__ void softmax_rescale(ExtendState<D>& st, const f32x4 (&s)[2][kNB], u32x4 (&pb)[kNB],
+                                                float c, int kbase, const int (&lim_abs)[kNB], int s0) {
+  float alpha[kNB];
+  bool any_move = false;
+#pragma unroll
+  for (int cb = 0; cb < kNB; ++cb) {
+    float x[8], p[8];
+    block_scores<MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
+    const float t = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    const float tmax = wave_max_across_quads(t) * c;
+    const float m_old = st.m[cb];
+    const bool move = tmax > m_old + kLazy;
+    const float m_new = move ? tmax : m_old;
+    any_move |= move;
+    alpha[cb] = move ? exp2_fast(m_old - m_new) : 1.f;
+    const float neg = (m_new == -INFINITY) ? 0.f : -m_new;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, neg));
+    st.l[cb] = st.l[cb] * alpha[cb] + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+    st.m[cb] = m_new;
+    pb[cb] = pack_p8(p);
+  }
+  if (__builtin_amdgcn_ballot_w64(any_move)) {
+#pragma unroll
+    for (int cb = 0; cb < kNB; ++cb)
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) st.acc[cb][i] *= alpha[cb];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void extend_kernel(ExtendArgs a, int row_blocks) {
+  constexpr int TILE = D * 4;                 // u32x4 per page tile (K then V)
+  constexpr int PER_PAGE = TILE / 256;        // DMA instructions per thread per page
+  constexpr int PER_BLOCK = 2 * PER_PAGE;
+  __shared__ u32x4 ring[kStages][2 * TILE];
+
   const int Hkv = a.pool.num_kv_heads;
   const int units = a.batch * Hkv;
   const int xcd = blockIdx.x % kXcds;
-  const int k = blockIdx.x / kXcds;
-  const int unit = (k / row_blocks) * kXcds + xcd;
-  const int rb = k % row_blocks;
+  const int kk = blockIdx.x / kXcds;
+  const int unit = (kk / row_blocks) * kXcds + xcd;
+  const int rb = kk % row_blocks;
   if (unit >= units) return;
   const int b = unit / Hkv, g = unit % Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.num_q_heads / Hkv;
 
-  int P = a.seq_lens[b];
-  const int c0 = a.cu_new[b], c1 = a.cu_new[b + 1];
-  int C = c1 - c0;
+  const int P = load_uniform(a.seq_lens + b);
+  const int c0 = load_uniform(a.cu_new + b), c1 = load_uniform(a.cu_new + b + 1);
+  const int C = c1 - c0;
   if (P < 0 || C < 0 || C > a.max_new || P + C > a.max_seq_len || c0 < 0 || c1 > a.total_new) {
-    if (threadIdx.x == 0 && rb == 0 && g == 0) flag_error(a.dev_status, 2);
+    if (threadIdx.x == 0 && rb == 0) flag_error(a.dev_status, KVS_DEV_BAD_LEN_BIT);
     return;
   }
   const int rows = C * G;
   const int rbase = rb * kRowsPerBlock;
-  if (rbase >= rows) return;
+  if (rbase >= rows) return;  // whole workgroup: uniform
   const int total = P + C;
-  const int r0 = rbase + wave * kRowsPerWave;
-  if (r0 >= rows) return;  // no barriers below: a wave may leave early
+  const int npages = (total + kPage - 1) / kPage;
+  const int wg_last_tok = (min(rbase + kRowsPerBlock, rows) - 1) / G;
+  const int nblk = (P + wg_last_tok + 1 + 31) / 32;   // 32-key blocks this workgroup needs
 
-  QFrag<D, NB> qf;
-  int lim_abs[NB];
-  int tok[NB], head[NB];
-  bool rvalid[NB];
+  // ---- this wave's rows ----
+  const int r0 = rbase + wave * kRowsPerWave;
+  u32x4 qf[kNB][D / 32];
+  int lim_abs[kNB], tok[kNB], head[kNB];
+  bool rvalid[kNB];
 #pragma unroll
-  for (int cb = 0; cb < NB; ++cb) {
+  for (int cb = 0; cb < kNB; ++cb) {
     const int r = r0 + cb * 16 + (lane & 15);
     rvalid[cb] = r < rows;
     const int i = rvalid[cb] ? r / G : C - 1;
@@ -64,63 +216,118 @@ __global__ __launch_bounds__(256) void extend_kernel(ExtendArgs a, int row_block
     const uint16_t* qrow = a.q + (int64_t(c0 + i) * a.num_q_heads + head[cb]) * D;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
-      qf.q[cb][s] = rvalid[cb] ? *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * (lane >> 4))
-                               : u32x4{0u, 0u, 0u, 0u};
+      qf[cb][s] = rvalid[cb] ? *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * (lane >> 4))
+                             : u32x4{0u, 0u, 0u, 0u};
   }
-  // wave-uniform bounds of the key limits of this wave's rows
-  const int last_row = min(r0 + kRowsPerWave, rows) - 1;
-  const int lim_lo = P + r0 / G + 1;
-  const int lim_hi = P + last_row / G + 1;
-  const int npages = (lim_hi + kPage - 1) / kPage;
+  const bool wave_has_rows = r0 < rows;
+  const int wave_lo = wave_has_rows ? P + r0 / G + 1 : 0;  // smallest key limit among the wave's rows
 
-  RowState<D, NB> st;
-  st.init();
   const int32_t* btrow = a.bt + int64_t(b) * a.bt_stride;
   const int num_pages = a.pool.num_pages;
-  u32x4 kf[D / 32], vf[D / 32], kn[D / 32], vn[D / 32];
-
-  int pid = btrow[0];
-  bool ok = pid >= 0 && pid < num_pages;
-  if (!ok) flag_error(a.dev_status, 1);
-  if (ok) {
-    const uint16_t* tile = a.pool.data + tile_offset(a.layer, pid, g, num_pages, Hkv, D);
+  const int tid = threadIdx.x;
+  auto issue = [&](int k) {
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      kf[s] = load_k_slab(tile, s, lane);
-      vf[s] = load_v_slab(tile, D, s, lane);
-    }
-  }
-  for (int p = 0; p < npages; ++p) {
-    const int pn = p + 1;
-    const int pidn = pn < npages ? btrow[pn] : -1;
-    const bool okn = pidn >= 0 && pidn < num_pages;
-    if (pn < npages && !okn) flag_error(a.dev_status, 1);
-    if (okn) {
-      const uint16_t* tile = a.pool.data + tile_offset(a.layer, pidn, g, num_pages, Hkv, D);
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        kn[s] = load_k_slab(tile, s, lane);
-        vn[s] = load_v_slab(tile, D, s, lane);
+    for (int h = 0; h < 2; ++h) {
+      int p = 2 * k + h;
+      if (p >= npages) p = 2 * k;  // no second page: reload the first (never used unmasked)
+      int pid = load_uniform(btrow + p);
+      if (pid < 0 || pid >= num_pages) {
+        flag_error(a.dev_status, KVS_DEV_BAD_PAGE_BIT);
+        __builtin_amdgcn_s_waitcnt(0);
+        pid = 0;  // in-range stand-in; the session's output is unspecified
       }
-    }
-    if (ok) {
-      const int pstart = p * kPage;
-      const int nvalid = min(kPage, total - pstart);
-      int lim[NB];
+      const u32x4* tile = reinterpret_cast<const u32x4*>(a.pool.data + tile_offset(a.layer, pid, g, num_pages, Hkv, D));
+      u32x4* dst = &ring[k % kStages][h * TILE];
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb) lim[cb] = lim_abs[cb] - pstart;
-      attend_page<D, NB>(st, qf, kf, vf, a.scale_log2, pstart + kPage > lim_lo, lim, nvalid, lane);
+      for (int j = 0; j < PER_PAGE; ++j)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + j * 256 + tid),
+                                         (__attribute__((address_space(3))) void*)(dst + j * 256 + wave * 64),
+                                         16, 0, 0);
     }
+  };
+
+  const int s0 = 4 * (lane >> 4);
+  const float c = a.scale_log2;
+  ExtendState<D> st;
+
+  // The whole key walk.  FAST: fixed reference per row; otherwise rescaling.
+  auto run = [&](auto fast_tag) {
+    constexpr bool FAST = decltype(fast_tag)::value;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      kf[s] = kn[s];
-      vf[s] = vn[s];
+    for (int cb = 0; cb < kNB; ++cb) {
+      st.m[cb] = -INFINITY;
+      st.l[cb] = 0.f;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) st.acc[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    ok = okn;
-  }
+    // one 32-key block: QK^T of block k+1 into nxt, softmax + PV of block k from cur
+    auto step = [&](int k, f32x4 (&cur)[2][kNB], f32x4 (&nxt)[2][kNB]) {
+      if (k + kLook < nblk) issue(k + kLook);
+      if (k + 1 < nblk) {
+        wait_blocks<PER_BLOCK>(min(nblk - 1, k + kLook) - (k + 1));
+        __syncthreads();
+        qk_block<D>(nxt, qf, ring[(k + 1) % kStages], lane);
+      }
+      const int kbase = k * 32;
+      const bool masked = kbase + 32 > wave_lo;  // some row of the wave stops inside this block
+      u32x4 pb[kNB];
+      if (!FAST) {
+        if (masked) softmax_rescale<D, true>(st, cur, pb, c, kbase, lim_abs, s0);
+        else softmax_rescale<D, false>(st, cur, pb, c, kbase, lim_abs, s0);
+      } else if (k == 0) {
+        if (masked) softmax_first<D, true>(st, cur, pb, c, kbase, lim_abs, s0);
+        else softmax_first<D, false>(st, cur, pb, c, kbase, lim_abs, s0);
+      } else {
+        if (masked) softmax_fixed<D, true>(st, cur, pb, c, kbase, lim_abs, s0);
+        else softmax_fixed<D, false>(st, cur, pb, c, kbase, lim_abs, s0);
+      }
+      const u32x4* stg = ring[k % kStages];
+      const int nv0 = total - kbase, nv1 = total - kbase - 16;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) {
+        u32x4 v0 = stg[TILE / 2 + i * 64 + lane];
+        u32x4 v1 = stg[TILE + TILE / 2 + i * 64 + lane];
+        if (nv0 < kPage) v0 = mask_v_slab(v0, lane, nv0);
+        if (nv1 < kPage) v1 = mask_v_slab(v1, lane, nv1);
+        const u32x4 a0 = {v0[0], v0[1], v1[0], v1[1]};   // head dims 32i + 0..15
+        const u32x4 a1 = {v0[2], v0[3], v1[2], v1[3]};   // head dims 32i + 16..31
+#pragma unroll
+        for (int cb = 0; cb < kNB; ++cb) {
+          st.acc[cb][2 * i] = mma_16x16x32(a0, pb[cb], st.acc[cb][2 * i]);
+          st.acc[cb][2 * i + 1] = mma_16x16x32(a1, pb[cb], st.acc[cb][2 * i + 1]);
+        }
+      }
+    };
+#pragma unroll 1
+    for (int k = 0; k < kLook && k < nblk; ++k) issue(k);
+    wait_blocks<PER_BLOCK>(min(kLook, nblk) - 1);
+    __syncthreads();
+    f32x4 sa[2][kNB], sb[2][kNB];
+    qk_block<D>(sa, qf, ring[0], lane);
+#pragma unroll 1
+    for (int k = 0; k < nblk; ++k) {
+      step(k, sa, sb);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int cb = 0; cb < kNB; ++cb) sa[h][cb] = sb[h][cb];
+    }
+  };
+
+  run(std::integral_constant<bool, true>{});
+  // a fixed-reference sum out of range (or not finite) sends the workgroup down the rescaling path
+  __shared__ int redo;
+  if (threadIdx.x == 0) redo = 0;
+  __syncthreads();
+  bool bad = false;
+#pragma unroll
+  for (int cb = 0; cb < kNB; ++cb) bad |= !(st.l[cb] < kSafeSum);
+  if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) redo = 1;
+  __syncthreads();
+  if (redo) run(std::integral_constant<bool, false>{});
 
 #pragma unroll
-  for (int cb = 0; cb < NB; ++cb) {
+  for (int cb = 0; cb < kNB; ++cb) {
     const float l = wave_sum_across_quads(st.l[cb]);
     if (!rvalid[cb]) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;

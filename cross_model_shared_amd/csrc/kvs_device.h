@@ -61,17 +61,27 @@ __device__ __forceinline__ u32x2 pack_bf16x4(float a, float b, float c, float d)
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Reductions over lanes l, l^16, l^32, l^48 (the four lane groups that hold one
+// row of a 16x16 matrix-core result).  gfx950's row swaps exchange 16-lane rows
+// (permlane16) and 32-lane halves (permlane32) between two registers; with both
+// operands equal, the element-wise max/sum of the two results is the pairwise
+// reduction, in plain VALU instructions.
 __device__ __forceinline__ float wave_max_across_quads(float x) {
-  // lanes l, l^16, l^32, l^48 hold the same row
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float wave_sum_across_quads(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+
+// 2^x on the transcendental unit (no subnormal range handling: results below
+// 2^-126 flush to zero, which a softmax weight can afford).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Zero the V operand entries (both halves) of slots >= nvalid.  Slots past a
 // session's end may hold anything, NaN included, and 0 * NaN would poison PV.

@@ -262,3 +262,67 @@ def test_decode_equals_single_row_extend():
     case = dict(pool=c["pool"], Hkv=2, layer=0, status=c["status"])
     dec = gu.host_f64(gu.run_decode(case, q_bits=c["q"][None], lens=[612], bt=c["bt"]))
     assert np.max(np.abs(dec[0, 0] - ext[0])) <= TOL
+
+
+# ---------------------------------------------------------------------------
+# Score ranges far beyond fp32 exp range: exercises the rescaling paths
+# ---------------------------------------------------------------------------
+def _growing_keys(L, Hkv, D, top):
+    """K rows whose entries grow linearly from 0 to `top` along the sequence."""
+    ramp = (np.arange(L, dtype=np.float32) * (top / max(L - 1, 1)))[:, None, None]
+    return wlmod.f32_to_bf16_bits(np.broadcast_to(ramp, (L, Hkv, D)).copy())
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_extend_huge_score_range_takes_rescaling_path(D):
+    """q = 1 and K entries ramping from 0 to 8: the last key scores 8*sqrt(D) (90 at
+    D=128, 130 in log2 units) above the first, far past the 2^60 headroom of the
+    fixed-reference pass, so the workgroups must recompute with rescaling."""
+    import torch
+
+    prefix, new, Hkv, G = [300, 0], [40, 70], 2, 4
+    rng = np.random.default_rng(77)
+    full = [p + c for p, c in zip(prefix, new)]
+    fk = [_growing_keys(L, Hkv, D, 8.0) for L in full]
+    fv = [wlmod.draw_bf16(rng, (L, Hkv, D), 1.0) for L in full]
+    bt, num_pages = wlmod.build_block_table(full, 5)
+    pool = binding.Pool(1, num_pages, Hkv, D, fill=np.int16(np.uint16(gu.POISON_NAN).view(np.int16)))
+    st = gu.status_tensor()
+    kk, cu_all = wlmod.concat_rows(fk)
+    vv, _ = wlmod.concat_rows(fv)
+    # whole sequences through extend (prefix 0), so both prefix and chunk use the pool
+    q = wlmod.f32_to_bf16_bits(np.ones((int(cu_all[-1]), Hkv * G, D), np.float32))
+    out = torch.empty((q.shape[0], Hkv * G, D), dtype=torch.bfloat16, device="cuda")
+    binding.extend(pool, 0, gu.dev_bf16(q), gu.dev_bf16(kk), gu.dev_bf16(vv), out, gu.dev_i32(cu_all),
+                   gu.dev_i32(bt), gu.dev_i32([0, 0]), max_new=max(full), max_seq_len=max(full),
+                   scale=1.0 / math.sqrt(D), dev_status=st)
+    gu.sync()
+    got = gu.host_f64(out)
+    for b in range(2):
+        rows = list(range(full[b]))
+        want = oracle.extend_from_logical(q[cu_all[b]:cu_all[b + 1]], fk[b], fv[b], 0, rows, 1.0 / math.sqrt(D))
+        assert np.all(np.isfinite(got[cu_all[b]:cu_all[b + 1]]))
+        assert np.max(np.abs(got[cu_all[b]:cu_all[b + 1]] - want)) <= TOL
+    assert int(st.item()) == 0
+
+
+@pytest.mark.parametrize("N,G", [(1, 4), (8, 4)])
+def test_decode_huge_score_range(N, G):
+    Hkv, D = 2, 128
+    lens = [3000, 517, 4100]
+    rng = np.random.default_rng(3)
+    K = [_growing_keys(L, Hkv, D, 6.0) for L in lens]
+    V = [wlmod.draw_bf16(rng, (L, Hkv, D), 1.0) for L in lens]
+    bt, num_pages = wlmod.build_block_table(lens, 3)
+    pool = binding.Pool(1, num_pages, Hkv, D)
+    st = gu.status_tensor()
+    kk, cu = wlmod.concat_rows(K)
+    vv, _ = wlmod.concat_rows(V)
+    binding.append(pool, 0, gu.dev_bf16(kk), gu.dev_bf16(vv), gu.dev_i32(cu), gu.dev_i32(bt),
+                   gu.dev_i32([0, 0, 0]), max_new=max(lens), max_seq_len=max(lens), dev_status=st)
+    q = wlmod.f32_to_bf16_bits(np.ones((3, N, Hkv * G, D), np.float32))
+    case = dict(pool=pool, Hkv=Hkv, layer=0, status=st, lens=lens, bt=bt)
+    out = gu.host_f64(gu.run_decode(case, q_bits=q))
+    want = oracle.decode_from_logical(q, K, V, 1.0 / math.sqrt(D))
+    assert np.all(np.isfinite(out))
+    assert np.max(np.abs(out - want)) <= TOL
