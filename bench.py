@@ -45,8 +45,58 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--layers", type=int, default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--layers", type=int, default=None,
+                    help="decode layers per step (default: the workload's 36; fewer only for counter runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a 1 GiB device-to-device copy before timing (scale for HBM byte counters)")
     return ap.parse_args()
+
+
+DECODE_SOURCES = ["cross_model_shared_amd/csrc/decode.hip", "cross_model_shared_amd/csrc/attn_core.h",
+                  "cross_model_shared_amd/csrc/kvs_device.h"]
+PMC_SUMMARY = "profiles/decode_qwen3_8b_n8_hbm_counters.md"
+
+
+def kernel_source_hash(paths):
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, PMC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_hash(DECODE_SOURCES):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    """A plain 1 GiB copy: its FETCH_SIZE / WRITE_SIZE readings give the counters' scale."""
+    import torch
+
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("[bench] calibration copy: 3 x 1 GiB device-to-device")
+    del src, dst
 
 
 def decode_bytes(lens, B, N, Hq, Hkv, D):
@@ -242,6 +292,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     binding.load()
+    if args.calibrate_copy:
+        calibrate_copy()
     wl = W.make_workload(DECODE_WORKLOAD)
     layers = args.layers or wl.num_layers
     B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
@@ -334,7 +386,7 @@ def main():
         "roofline": {
             "bound": "hbm", "kernel": "shared_kv_decode (per-layer call)",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
             "launch_ms": round(call_ms, 5),
         },
         "cpu_baseline": cpu,

@@ -293,20 +293,23 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
 
 // Merge the partial states of units that cross share boundaries:
 // m* = max m_s, out = sum_s 2^(m_s - m*) acc_s / sum_s 2^(m_s - m*) l_s.
-// Also writes zeros for empty sessions (softmax over nothing).
+// Also writes zeros for empty sessions (softmax over nothing).  One thread per
+// (row, 4 head dims), all loads of a pass issued before any is used, so a unit
+// costs about two memory round trips.
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
   const int B = a.batch, Hkv = a.pool.num_kv_heads, RGs = a.plan.rowgroups;
   const int unit = blockIdx.x;  // (gr, b) with b fastest
   const int b = unit % B, gr = unit / B;
   const int g = gr / RGs, rg = gr % RGs;
   const int RG = a.plan.rg_rows;
   const int G = a.num_q_heads / Hkv;
-  const int Ptot = a.ws_cum[B];
-  const int npg = a.ws_cum[b + 1] - a.ws_cum[b];
+  const int Ptot = load_uniform(a.ws_cum + B);
+  const int cb0 = load_uniform(a.ws_cum + b);
+  const int npg = load_uniform(a.ws_cum + b + 1) - cb0;
   const int W = a.plan.blocks * kWaves;
   if (npg == 0) {
-    for (int e = threadIdx.x; e < RG * (D / 8); e += 256) {
+    for (int e = threadIdx.x; e < RG * (D / 8); e += blockDim.x) {
       const int r = rg * RG + e / (D / 8);
       if (r >= a.plan.rows) continue;
       const int n = r / G, h = g * G + r % G;
@@ -316,27 +319,31 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     return;
   }
   const int64_t T = int64_t(Ptot) * Hkv * RGs;
-  const int64_t s_u = int64_t(gr) * Ptot + a.ws_cum[b], e_u = s_u + npg;
+  const int64_t s_u = int64_t(gr) * Ptot + cb0, e_u = s_u + npg;
   // share of tile t: floor(((t + 1) W - 1) / T)
   const int k0 = int(((s_u + 1) * W - 1) / T), k1 = int((e_u * W - 1) / T);
   if (k0 == k1) return;  // written directly by its wave
-  for (int e = threadIdx.x; e < RG * (D / 4); e += 256) {
+  const float* __restrict__ ml = a.ws_ml;
+  const float* __restrict__ accp = a.ws_acc;
+  for (int e = threadIdx.x; e < RG * (D / 4); e += blockDim.x) {
     const int rl = e / (D / 4), d4 = e % (D / 4);
     const int r = rg * RG + rl;
     if (r >= a.plan.rows) continue;
+    // slot of share k: its "started before" slot (0) except the first share (1)
     float M = -INFINITY;
-    for (int k = k0; k <= k1; ++k) {
-      const int slot = k * 2 + (k == k0 ? 1 : 0);
-      M = fmaxf(M, a.ws_ml[(int64_t(slot) * RG + rl) * 2]);
-    }
+#pragma unroll 8
+    for (int k = k0; k <= k1; ++k) M = fmaxf(M, ml[(int64_t(k * 2 + (k == k0)) * RG + rl) * 2]);
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
+#pragma unroll 4
     for (int k = k0; k <= k1; ++k) {
-      const int slot = k * 2 + (k == k0 ? 1 : 0);
-      const float ms = a.ws_ml[(int64_t(slot) * RG + rl) * 2];
-      const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      den += w * a.ws_ml[(int64_t(slot) * RG + rl) * 2 + 1];
-      num += w * reinterpret_cast<const f32x4*>(a.ws_acc + (int64_t(slot) * RG + rl) * D)[d4];
+      const int64_t slot = k * 2 + (k == k0);
+      const float ms = ml[(slot * RG + rl) * 2];
+      const float ls = ml[(slot * RG + rl) * 2 + 1];
+      const f32x4 as = reinterpret_cast<const f32x4*>(accp + (slot * RG + rl) * D)[d4];
+      const float w = (ms == -INFINITY) ? 0.f : exp2_fast(ms - M);
+      den += w * ls;
+      num += w * as;
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     const int n = r / G, h = g * G + r % G;
@@ -352,7 +359,8 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units = a.pool.num_kv_heads * a.plan.rowgroups * a.batch;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(units), dim3(256), 0, stream, a);
+  const int threads = min(1024, a.plan.rg_rows * (D / 4));
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(units), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,149 @@
+"""Parity at the workloads' full sizes, in the launch configuration the bench times.
+
+The GPU path appends device-drawn K/V (torch's seeded generator, the input
+generator for large sizes) into a poisoned pool with kv_pool_append, then runs
+shared_kv_decode / partial_prefill_extend.  The oracle checks a seeded sample of
+sessions (decode: every decoder and head of each sampled session) or rows
+(extend: first, last and boundary rows of sampled sessions) from the same
+logical K/V copied to the host, and compares the sampled sessions' page tiles
+bit for bit against its own append of those K/V.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from cross_model_shared_amd import binding
+from cross_model_shared_amd import workload as W
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+
+
+def host_rows(t):
+    import torch
+
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def sample_sessions(lens, k, seed):
+    order = np.argsort(lens)
+    picks = {int(order[0]), int(order[-1])}
+    rng = np.random.default_rng(seed)
+    for b in rng.permutation(len(lens)):
+        if len(picks) >= k:
+            break
+        picks.add(int(b))
+    return sorted(picks)
+
+
+def check_tiles(pool, bt, layer, b, kb, vb, Hkv, D):
+    """The session's pages in the GPU pool equal the oracle's append of its K/V."""
+    L = kb.shape[0]
+    npg = (L + 15) // 16
+    shape = oracle.PoolShape(1, npg, Hkv, D)
+    img = oracle.append(np.full(shape.elems, gu.POISON_NAN, np.uint16), shape, 0, kb, vb, [0, L],
+                        np.arange(npg, dtype=np.int32)[None], [0])
+    tile = Hkv * 32 * D
+    flat = pool.data.view(-1)
+    per_layer = pool.num_pages * tile
+    for p in range(npg):
+        pid = int(bt[b, p])
+        got = flat[layer * per_layer + pid * tile:layer * per_layer + (pid + 1) * tile]
+        got = got.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, img[p * tile:(p + 1) * tile]), (b, p)
+
+
+@pytest.mark.parametrize("name,layers,layer", [("llama8b_n4", 1, 0), ("qwen3_8b_n8", 2, 1),
+                                               ("qwen3_14b_long", 1, 0)])
+def test_decode_full_size_sampled(name, layers, layer):
+    import torch
+
+    wl = W.make_workload(name)
+    B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    lens = wl.lens
+    print(f"[fullsize] {name}: B={B} N={N} sum(L)={sum(lens)} max(L)={max(lens)}", flush=True)
+    bt, num_pages = W.build_block_table(lens, wl.seed)
+    pool = binding.Pool(layers, num_pages, Hkv, D, fill=np.int16(np.uint16(gu.POISON_NAN).view(np.int16)))
+    total = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    k = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 10, layer)).view(total, Hkv, D)
+    v = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 11, layer)).view(total, Hkv, D)
+    st = gu.status_tensor()
+    maxL = max(lens)
+    bt_d = torch.from_numpy(bt).cuda()
+    binding.append(pool, layer, k, v, gu.dev_i32(cu), bt_d, gu.dev_i32(np.zeros(B)), max_new=maxL,
+                   max_seq_len=maxL, dev_status=st)
+    q = W.device_normal_bf16(B * N * Hq * D, wl.std, W.mix_seed(wl.seed, 12, layer)).view(B, N, Hq, D)
+    out = torch.empty_like(q)
+    ws = torch.zeros(binding.decode_workspace_bytes(B, N, Hq, Hkv, D, maxL), dtype=torch.uint8, device="cuda")
+    binding.decode(pool, layer, q, out, bt_d, gu.dev_i32(lens), maxL, wl.scale, ws, dev_status=st)
+    gu.sync()
+    assert int(st.item()) == 0
+    got = gu.host_f64(out)
+    assert np.all(np.isfinite(got))
+    picks = sample_sessions(lens, 8, wl.seed)
+    qh = host_rows(q)
+    Ks = [None] * B
+    Vs = [None] * B
+    for b in picks:
+        Ks[b] = host_rows(k[cu[b]:cu[b + 1]])
+        Vs[b] = host_rows(v[cu[b]:cu[b + 1]])
+    want = oracle.decode_from_logical(qh, Ks, Vs, wl.scale)
+    err = max(float(np.max(np.abs(got[b] - want[b]))) for b in picks)
+    print(f"[fullsize] {name}: sessions {picks} max-abs err {err:.3e}", flush=True)
+    assert err <= TOL
+    for b in sorted(picks, key=lambda b: lens[b])[:2]:   # the two shortest sampled sessions
+        check_tiles(pool, bt, layer, b, Ks[b], Vs[b], Hkv, D)
+
+
+def test_extend_full_size_sampled():
+    import torch
+
+    wl = W.make_workload("extend_8k_512")
+    B, Hq, Hkv, D = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    full = wl.total_lens()
+    print(f"[fullsize] extend_8k_512: B={B} prefix={wl.prefix[0]} new={wl.new[0]}", flush=True)
+    bt, num_pages = W.build_block_table(full, wl.seed)
+    pool = binding.Pool(1, num_pages, Hkv, D, fill=np.int16(np.uint16(gu.POISON_NAN).view(np.int16)))
+    bt_d = torch.from_numpy(bt).cuda()
+    st = gu.status_tensor()
+    P, T = sum(wl.prefix), sum(wl.new)
+    kp = W.device_normal_bf16(P * Hkv * D, wl.std, W.mix_seed(wl.seed, 20)).view(P, Hkv, D)
+    vp = W.device_normal_bf16(P * Hkv * D, wl.std, W.mix_seed(wl.seed, 21)).view(P, Hkv, D)
+    cup = np.concatenate([[0], np.cumsum(wl.prefix)]).astype(np.int32)
+    binding.append(pool, 0, kp, vp, gu.dev_i32(cup), bt_d, gu.dev_i32(np.zeros(B)), max_new=max(wl.prefix),
+                   max_seq_len=max(full), dev_status=st)
+    q = W.device_normal_bf16(T * Hq * D, wl.std, W.mix_seed(wl.seed, 22)).view(T, Hq, D)
+    kn = W.device_normal_bf16(T * Hkv * D, wl.std, W.mix_seed(wl.seed, 23)).view(T, Hkv, D)
+    vn = W.device_normal_bf16(T * Hkv * D, wl.std, W.mix_seed(wl.seed, 24)).view(T, Hkv, D)
+    cu = np.concatenate([[0], np.cumsum(wl.new)]).astype(np.int32)
+    out = torch.empty_like(q)
+    binding.extend(pool, 0, q, kn, vn, out, gu.dev_i32(cu), bt_d, gu.dev_i32(wl.prefix), max(wl.new), max(full),
+                   wl.scale, dev_status=st)
+    gu.sync()
+    assert int(st.item()) == 0
+    got = gu.host_f64(out)
+    assert np.all(np.isfinite(got))
+    picks = sample_sessions(full, 3, wl.seed)
+    for b in picks:
+        C = wl.new[b]
+        rows = sorted(set(list(range(8)) + list(range(C - 8, C)) + [63, 64, 127, 128, 255, 256, 300]))
+        kf = np.concatenate([host_rows(kp[cup[b]:cup[b + 1]]), host_rows(kn[cu[b]:cu[b + 1]])])
+        vf = np.concatenate([host_rows(vp[cup[b]:cup[b + 1]]), host_rows(vn[cu[b]:cu[b + 1]])])
+        want = oracle.extend_from_logical(host_rows(q[cu[b]:cu[b + 1]]), kf, vf, wl.prefix[b], rows, wl.scale)
+        err = float(np.max(np.abs(got[cu[b] + np.array(rows)] - want)))
+        print(f"[fullsize] extend session {b}: {len(rows)} rows, max-abs err {err:.3e}", flush=True)
+        assert err <= TOL
+    check_tiles(pool, bt, 0, picks[-1], kf, vf, Hkv, D)  # prefix + appended chunk of the last pick
