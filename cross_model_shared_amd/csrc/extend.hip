@@ -4,13 +4,14 @@
 //
 // Rows of one (session, KV head) are the chunk's (token i, query head of the
 // group) pairs, token-major, so a 16-row block spans few positions and the
-// causal diagonal touches few pages.  A workgroup holds 256 rows (4 waves x 64
-// rows, Q kept in registers) and walks the session's keys in blocks of 32 (two
-// pages).  Blocks are staged once per workgroup in LDS by direct global->LDS
-// 16-byte loads, kLook blocks ahead, and every wave reads its matrix-core
-// operands from there: per 32 keys a wave does 32 QK^T and 32 PV steps of
-// 16x16x32 bf16.  The QK^T of block k+1 is issued before the softmax of block k
-// so matrix and vector work of one wave can overlap.
+// causal diagonal touches few pages.  A workgroup holds 256 rows (16*NB rows
+// per wave, Q kept in registers; at D=128 eight 32-row waves, two per SIMD, so
+// one wave's softmax and LDS waits overlap the other's matrix-core work) and
+// walks the session's keys in blocks of 32 (two pages).  Blocks are staged once
+// per workgroup in LDS by direct global->LDS 16-byte loads, kLook blocks ahead,
+// and every wave reads its matrix-core operands from there: per 32 keys and 16
+// rows a wave does 8 QK^T and 8 PV steps of 16x16x32 bf16.  The QK^T of block
+// k+1 is issued before the softmax of block k.
 //
 // Workgroups are laid out so that all row blocks of one (session, KV head) land
 // on the same XCD: hardware hands workgroup ids to the 8 XCDs round robin, and
@@ -25,9 +26,7 @@ namespace kvs {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kNB = 4;                       // 16-row column blocks per wave
-constexpr int kRowsPerWave = 16 * kNB;
-constexpr int kRowsPerBlock = 4 * kRowsPerWave;
+constexpr int kRowsPerBlock = 256;           // query rows per workgroup (waves x 16*NB)
 constexpr int kStages = 6;                   // LDS ring of 32-key blocks
 constexpr int kLook = 4;                     // blocks in flight ahead of compute
 constexpr float kLazy = 8.0f;                // rescaling path: max moves when it grows by > 2^8
@@ -49,15 +48,15 @@ __device__ __forceinline__ void wait_blocks(int blocks_after) {
   }
 }
 
-template <int D>
+template <int D, int NB>
 struct ExtendState {
-  f32x4 acc[kNB][D / 16];
-  float m[kNB], l[kNB];
+  f32x4 acc[NB][D / 16];
+  float m[NB], l[NB];
 };
 
 // S^T for one 32-key block: s[h][cb] covers page h of the block, rows of column block cb.
-template <int D>
-__device__ __forceinline__ void qk_block(f32x4 (&s)[2][kNB], const u32x4 (&qf)[kNB][D / 32],
+template <int D, int NB>
+__device__ __forceinline__ void qk_block(f32x4 (&s)[2][NB], const u32x4 (&qf)[NB][D / 32],
                                          const u32x4* stage, int lane) {
   constexpr int TILE = D * 4;  // u32x4 per (page, head) tile
 #pragma unroll
@@ -66,7 +65,7 @@ __device__ __forceinline__ void qk_block(f32x4 (&s)[2][kNB], const u32x4 (&qf)[k
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) kf[i] = stage[h * TILE + i * 64 + lane];
 #pragma unroll
-    for (int cb = 0; cb < kNB; ++cb) {
+    for (int cb = 0; cb < NB; ++cb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) acc = mma_16x16x32(kf[i], qf[cb][i], acc);
@@ -77,8 +76,8 @@ __device__ __forceinline__ void qk_block(f32x4 (&s)[2][kNB], const u32x4 (&qf)[k
 
 // Scores of one 32-key block for column block cb: 8 per lane (page 0 slots
 // s0..s0+3, then page 1), masked to -inf past each row's key limit.
-template <bool MASKED>
-__device__ __forceinline__ void block_scores(float (&x)[8], const f32x4 (&s)[2][kNB], int cb, int kbase,
+template <int NB, bool MASKED>
+__device__ __forceinline__ void block_scores(float (&x)[8], const f32x4 (&s)[2][NB], int cb, int kbase,
                                              int lim, int s0) {
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -102,13 +101,13 @@ __device__ __forceinline__ u32x4 pack_p8(const float (&p)[8]) {
 // may exceed 1, and a row whose sum leaves the safe range (checked once, after
 // the loop) is recomputed by the rescaling variant below.  Keeping the
 // accumulators free of vector ops lets them stay in accumulation registers.
-template <int D, bool MASKED>
-__device__ __forceinline__ void softmax_fixed(ExtendState<D>& st, const f32x4 (&s)[2][kNB], u32x4 (&pb)[kNB],
-                                              float c, int kbase, const int (&lim_abs)[kNB], int s0) {
+template <int D, int NB, bool MASKED>
+__device__ __forceinline__ void softmax_fixed(ExtendState<D, NB>& st, const f32x4 (&s)[2][NB], u32x4 (&pb)[NB],
+                                              float c, int kbase, const int (&lim_abs)[NB], int s0) {
 #pragma unroll
-  for (int cb = 0; cb < kNB; ++cb) {
+  for (int cb = 0; cb < NB; ++cb) {
     float x[8], p[8];
-    block_scores<MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
+    block_scores<NB, MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
     const float neg = -st.m[cb];
 #pragma unroll
     for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, neg));
@@ -118,32 +117,32 @@ __device__ __forceinline__ void softmax_fixed(ExtendState<D>& st, const f32x4 (&
 }
 
 // First block of a row: the reference is the block's row maximum.
-template <int D, bool MASKED>
-__device__ __forceinline__ void softmax_first(ExtendState<D>& st, const f32x4 (&s)[2][kNB], u32x4 (&pb)[kNB],
-                                              float c, int kbase, const int (&lim_abs)[kNB], int s0) {
+template <int D, int NB, bool MASKED>
+__device__ __forceinline__ void softmax_first(ExtendState<D, NB>& st, const f32x4 (&s)[2][NB], u32x4 (&pb)[NB],
+                                              float c, int kbase, const int (&lim_abs)[NB], int s0) {
 #pragma unroll
-  for (int cb = 0; cb < kNB; ++cb) {
+  for (int cb = 0; cb < NB; ++cb) {
     float x[8];
-    block_scores<MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
+    block_scores<NB, MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
     const float t = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     const float m = wave_max_across_quads(t) * c;  // c > 0: the max commutes with the scale
     st.m[cb] = (m == -INFINITY) ? 0.f : m;
   }
-  softmax_fixed<D, MASKED>(st, s, pb, c, kbase, lim_abs, s0);
+  softmax_fixed<D, NB, MASKED>(st, s, pb, c, kbase, lim_abs, s0);
 }
 
 // Rescaling variant (the recomputation path): the reference follows the running
 // maximum, moved only when it grows by more than 2^kLazy, and the accumulators
 // are rescaled then.
-template <int D, bool MASKED>
-__device__ __forceinline__ void softmax_rescale(ExtendState<D>& st, const f32x4 (&s)[2][kNB], u32x4 (&pb)[kNB],
-                                                float c, int kbase, const int (&lim_abs)[kNB], int s0) {
-  float alpha[kNB];
+template <int D, int NB, bool MASKED>
+__device__ __forceinline__ void softmax_rescale(ExtendState<D, NB>& st, const f32x4 (&s)[2][NB], u32x4 (&pb)[NB],
+                                                float c, int kbase, const int (&lim_abs)[NB], int s0) {
+  float alpha[NB];
   bool any_move = false;
 #pragma unroll
-  for (int cb = 0; cb < kNB; ++cb) {
+  for (int cb = 0; cb < NB; ++cb) {
     float x[8], p[8];
-    block_scores<MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
+    block_scores<NB, MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
     const float t = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     const float tmax = wave_max_across_quads(t) * c;
     const float m_old = st.m[cb];
@@ -160,16 +159,20 @@ __device__ __forceinline__ void softmax_rescale(ExtendState<D>& st, const f32x4 
   }
   if (__builtin_amdgcn_ballot_w64(any_move)) {
 #pragma unroll
-    for (int cb = 0; cb < kNB; ++cb)
+    for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) st.acc[cb][i] *= alpha[cb];
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 1) void extend_kernel(ExtendArgs a, int row_blocks) {
+template <int D, int NB>
+__global__ __launch_bounds__(64 * (16 / NB), 1) void extend_kernel(ExtendArgs a, int row_blocks) {
+  constexpr int WAVES = 16 / NB;              // 256 rows per workgroup
+  constexpr int THREADS = 64 * WAVES;
+  constexpr int kRowsPerWave = 16 * NB;
   constexpr int TILE = D * 4;                 // u32x4 per page tile (K then V)
-  constexpr int PER_PAGE = TILE / 256;        // DMA instructions per thread per page
+  static_assert(TILE % THREADS == 0, "a page tile must split evenly over the workgroup");
+  constexpr int PER_PAGE = TILE / THREADS;    // DMA instructions per thread per page
   constexpr int PER_BLOCK = 2 * PER_PAGE;
   __shared__ u32x4 ring[kStages][2 * TILE];
 
@@ -202,11 +205,11 @@ __global__ __launch_bounds__(256, 1) void extend_kernel(ExtendArgs a, int row_bl
 
   // ---- this wave's rows ----
   const int r0 = rbase + wave * kRowsPerWave;
-  u32x4 qf[kNB][D / 32];
-  int lim_abs[kNB], tok[kNB], head[kNB];
-  bool rvalid[kNB];
+  u32x4 qf[NB][D / 32];
+  int lim_abs[NB], tok[NB], head[NB];
+  bool rvalid[NB];
 #pragma unroll
-  for (int cb = 0; cb < kNB; ++cb) {
+  for (int cb = 0; cb < NB; ++cb) {
     const int r = r0 + cb * 16 + (lane & 15);
     rvalid[cb] = r < rows;
     const int i = rvalid[cb] ? r / G : C - 1;
@@ -240,77 +243,120 @@ __global__ __launch_bounds__(256, 1) void extend_kernel(ExtendArgs a, int row_bl
       u32x4* dst = &ring[k % kStages][h * TILE];
 #pragma unroll
       for (int j = 0; j < PER_PAGE; ++j)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + j * 256 + tid),
-                                         (__attribute__((address_space(3))) void*)(dst + j * 256 + wave * 64),
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + j * THREADS + tid),
+                                         (__attribute__((address_space(3))) void*)(dst + j * THREADS + wave * 64),
                                          16, 0, 0);
     }
   };
 
   const int s0 = 4 * (lane >> 4);
   const float c = a.scale_log2;
-  ExtendState<D> st;
+  ExtendState<D, NB> st;
+
+  // PV of block k from stage stg: the two pages' V quads side by side as the A
+  // operand, the bf16 weights pb as the B operand (32 keys per step).
+  auto pv_block = [&](const u32x4* stg, const u32x4 (&pb)[NB], int nv0, int nv1, bool vmask) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      u32x4 v0 = stg[TILE / 2 + i * 64 + lane];
+      u32x4 v1 = stg[TILE + TILE / 2 + i * 64 + lane];
+      if (vmask) {
+        v0 = mask_v_slab(v0, lane, nv0);
+        v1 = mask_v_slab(v1, lane, nv1);
+      }
+      const u32x4 a0 = {v0[0], v0[1], v1[0], v1[1]};   // head dims 32i + 0..15
+      const u32x4 a1 = {v0[2], v0[3], v1[2], v1[3]};   // head dims 32i + 16..31
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        st.acc[cb][2 * i] = mma_16x16x32(a0, pb[cb], st.acc[cb][2 * i]);
+        st.acc[cb][2 * i + 1] = mma_16x16x32(a1, pb[cb], st.acc[cb][2 * i + 1]);
+      }
+    }
+  };
+
+  // Blocks below fast_end are seen in full by every row of the workgroup and are
+  // followed by at least kLook more blocks: their steps have no masks and no
+  // data-dependent branches, so the matrix-core steps of QK^T(k+1) and PV(k)
+  // can be scheduled around the softmax of block k.
+  const int wg_lo = P + rbase / G + 1;                 // smallest key limit in the workgroup
+  const int fast_end = max(1, min(wg_lo / 32, nblk - kLook));
 
   // The whole key walk.  FAST: fixed reference per row; otherwise rescaling.
   auto run = [&](auto fast_tag) {
     constexpr bool FAST = decltype(fast_tag)::value;
 #pragma unroll
-    for (int cb = 0; cb < kNB; ++cb) {
+    for (int cb = 0; cb < NB; ++cb) {
       st.m[cb] = -INFINITY;
       st.l[cb] = 0.f;
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) st.acc[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // one 32-key block: QK^T of block k+1 into nxt, softmax + PV of block k from cur
-    auto step = [&](int k, f32x4 (&cur)[2][kNB], f32x4 (&nxt)[2][kNB]) {
+    // general step (any block): QK^T of block k+1 into nxt, softmax + PV of block k from cur
+    auto step = [&](int k, f32x4 (&cur)[2][NB], f32x4 (&nxt)[2][NB]) {
       if (k + kLook < nblk) issue(k + kLook);
       if (k + 1 < nblk) {
         wait_blocks<PER_BLOCK>(min(nblk - 1, k + kLook) - (k + 1));
         __syncthreads();
-        qk_block<D>(nxt, qf, ring[(k + 1) % kStages], lane);
+        qk_block<D, NB>(nxt, qf, ring[(k + 1) % kStages], lane);
       }
       const int kbase = k * 32;
       const bool masked = kbase + 32 > wave_lo;  // some row of the wave stops inside this block
-      u32x4 pb[kNB];
+      u32x4 pb[NB];
       if (!FAST) {
-        if (masked) softmax_rescale<D, true>(st, cur, pb, c, kbase, lim_abs, s0);
-        else softmax_rescale<D, false>(st, cur, pb, c, kbase, lim_abs, s0);
+        if (masked) softmax_rescale<D, NB, true>(st, cur, pb, c, kbase, lim_abs, s0);
+        else softmax_rescale<D, NB, false>(st, cur, pb, c, kbase, lim_abs, s0);
       } else if (k == 0) {
-        if (masked) softmax_first<D, true>(st, cur, pb, c, kbase, lim_abs, s0);
-        else softmax_first<D, false>(st, cur, pb, c, kbase, lim_abs, s0);
+        if (masked) softmax_first<D, NB, true>(st, cur, pb, c, kbase, lim_abs, s0);
+        else softmax_first<D, NB, false>(st, cur, pb, c, kbase, lim_abs, s0);
       } else {
-        if (masked) softmax_fixed<D, true>(st, cur, pb, c, kbase, lim_abs, s0);
-        else softmax_fixed<D, false>(st, cur, pb, c, kbase, lim_abs, s0);
+        if (masked) softmax_fixed<D, NB, true>(st, cur, pb, c, kbase, lim_abs, s0);
+        else softmax_fixed<D, NB, false>(st, cur, pb, c, kbase, lim_abs, s0);
       }
-      const u32x4* stg = ring[k % kStages];
       const int nv0 = total - kbase, nv1 = total - kbase - 16;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) {
-        u32x4 v0 = stg[TILE / 2 + i * 64 + lane];
-        u32x4 v1 = stg[TILE + TILE / 2 + i * 64 + lane];
-        if (nv0 < kPage) v0 = mask_v_slab(v0, lane, nv0);
-        if (nv1 < kPage) v1 = mask_v_slab(v1, lane, nv1);
-        const u32x4 a0 = {v0[0], v0[1], v1[0], v1[1]};   // head dims 32i + 0..15
-        const u32x4 a1 = {v0[2], v0[3], v1[2], v1[3]};   // head dims 32i + 16..31
-#pragma unroll
-        for (int cb = 0; cb < kNB; ++cb) {
-          st.acc[cb][2 * i] = mma_16x16x32(a0, pb[cb], st.acc[cb][2 * i]);
-          st.acc[cb][2 * i + 1] = mma_16x16x32(a1, pb[cb], st.acc[cb][2 * i + 1]);
-        }
-      }
+      pv_block(ring[k % kStages], pb, nv0, nv1, nv1 < kPage);
+    };
+    // fast step: no masks, constant waits, unconditional prefetch
+    auto fast_step = [&](int k, f32x4 (&cur)[2][NB], f32x4 (&nxt)[2][NB]) {
+      issue(k + kLook);
+      wait_vmcnt<PER_BLOCK * (kLook - 1)>();
+      __syncthreads();
+      qk_block<D, NB>(nxt, qf, ring[(k + 1) % kStages], lane);
+      u32x4 pb[NB];
+      softmax_fixed<D, NB, false>(st, cur, pb, c, k * 32, lim_abs, s0);
+      pv_block(ring[k % kStages], pb, kPage, kPage, false);
     };
 #pragma unroll 1
     for (int k = 0; k < kLook && k < nblk; ++k) issue(k);
     wait_blocks<PER_BLOCK>(min(kLook, nblk) - 1);
     __syncthreads();
-    f32x4 sa[2][kNB], sb[2][kNB];
-    qk_block<D>(sa, qf, ring[0], lane);
+    f32x4 sa[2][NB], sb[2][NB];
+    qk_block<D, NB>(sa, qf, ring[0], lane);
+    step(0, sa, sb);                        // sets each row's reference (FAST) or starts rescaling
+    int k = 1;
+    if (FAST) {
+      // blocks 1 .. fast_end-1, two per iteration so the score buffers swap roles
 #pragma unroll 1
-    for (int k = 0; k < nblk; ++k) {
-      step(k, sa, sb);
+      for (; k + 1 < fast_end; k += 2) {
+        fast_step(k, sb, sa);
+        fast_step(k + 1, sa, sb);
+      }
+      if (k < fast_end) {
+        fast_step(k, sb, sa);
+        ++k;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int cb = 0; cb < NB; ++cb) sb[h][cb] = sa[h][cb];
+      }
+    }
+    // remaining blocks: the causal diagonal, the sequence end
+#pragma unroll 1
+    for (; k < nblk; ++k) {
+      step(k, sb, sa);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int cb = 0; cb < kNB; ++cb) sa[h][cb] = sb[h][cb];
+        for (int cb = 0; cb < NB; ++cb) sb[h][cb] = sa[h][cb];
     }
   };
 
@@ -321,13 +367,13 @@ __global__ __launch_bounds__(256, 1) void extend_kernel(ExtendArgs a, int row_bl
   __syncthreads();
   bool bad = false;
 #pragma unroll
-  for (int cb = 0; cb < kNB; ++cb) bad |= !(st.l[cb] < kSafeSum);
+  for (int cb = 0; cb < NB; ++cb) bad |= !(st.l[cb] < kSafeSum);
   if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) redo = 1;
   __syncthreads();
   if (redo) run(std::integral_constant<bool, false>{});
 
 #pragma unroll
-  for (int cb = 0; cb < kNB; ++cb) {
+  for (int cb = 0; cb < NB; ++cb) {
     const float l = wave_sum_across_quads(st.l[cb]);
     if (!rvalid[cb]) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -340,7 +386,7 @@ __global__ __launch_bounds__(256, 1) void extend_kernel(ExtendArgs a, int row_bl
   }
 }
 
-template <int D>
+template <int D, int NB>
 hipError_t launch_extend_t(const ExtendArgs& a, hipStream_t stream) {
   const int G = a.num_q_heads / a.pool.num_kv_heads;
   const int row_blocks = (a.max_new * G + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -348,15 +394,17 @@ hipError_t launch_extend_t(const ExtendArgs& a, hipStream_t stream) {
   const int unit_rounds = (units + kXcds - 1) / kXcds;
   const int64_t blocks = int64_t(unit_rounds) * row_blocks * kXcds;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((extend_kernel<D>), dim3(unsigned(blocks)), dim3(256), 0, stream, a, row_blocks);
+  hipLaunchKernelGGL((extend_kernel<D, NB>), dim3(unsigned(blocks)), dim3(64 * (16 / NB)), 0, stream, a, row_blocks);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream) {
-  if (a.pool.head_dim == 128) return launch_extend_t<128>(a, stream);
-  return launch_extend_t<64>(a, stream);
+  // D=128: 8 waves x 32 rows (two waves per SIMD hide each other's softmax and
+  // LDS latency); D=64: 4 waves x 64 rows (a 4 KiB page tile is one 256-thread load)
+  if (a.pool.head_dim == 128) return launch_extend_t<128, 2>(a, stream);
+  return launch_extend_t<64, 4>(a, stream);
 }
 
 }  // namespace kvs
