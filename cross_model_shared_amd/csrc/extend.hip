@@ -19,6 +19,8 @@
 #include "kvs_device.h"
 #include "kvs_internal.h"
 
+#include <stdlib.h>
+
 #include <type_traits>
 
 namespace kvs {
@@ -26,9 +28,6 @@ namespace kvs {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kRowsPerBlock = 256;           // query rows per workgroup (waves x 16*NB)
-constexpr int kStages = 6;                   // LDS ring of 32-key blocks
-constexpr int kLook = 4;                     // blocks in flight ahead of compute
 constexpr float kLazy = 8.0f;                // rescaling path: max moves when it grows by > 2^8
 constexpr float kSafeSum = 1.0e18f;          // ~2^60: fixed-reference sums stay below this
 
@@ -37,6 +36,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(VM >= 0 && VM < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+
+// Workgroup barrier WITHOUT the memory fence of __syncthreads(): the fence would
+// wait for every outstanding vector-memory op, i.e. drain the blocks being
+// prefetched into LDS.  Each wave first waits (vmcnt) for its own share of the
+// block it needs; after the barrier the whole block is in LDS.  A ring stage is
+// overwritten only kStages - kLook >= 2 blocks after its last reads, whose
+// results every wave has already consumed.
+__device__ __forceinline__ void block_barrier() { __builtin_amdgcn_s_barrier(); }
 
 template <int PER>
 __device__ __forceinline__ void wait_blocks(int blocks_after) {
@@ -51,7 +58,8 @@ __device__ __forceinline__ void wait_blocks(int blocks_after) {
 template <int D, int NB>
 struct ExtendState {
   f32x4 acc[NB][D / 16];
-  float m[NB], l[NB];
+  f32x4 lsum[NB];   // row sums of the bf16 weights: sum_k 1 * P^T[k][row], every element equal
+  float m[NB];
 };
 
 // S^T for one 32-key block: s[h][cb] covers page h of the block, rows of column block cb.
@@ -96,7 +104,8 @@ __device__ __forceinline__ u32x4 pack_p8(const float (&p)[8]) {
 }
 
 // Softmax weights of one 32-key block against a FIXED per-row reference m
-// (set from the row's first block): p = 2^(s*c - m).  Moving the reference is
+// (set from the row's first block): p = 2^(s*c - m).  Row sums are taken by the
+// PV step (an all-ones A operand), from the same bf16 weights PV uses.  Moving the reference is
 // never needed for correctness, only to keep p inside fp32/bf16 range; weights
 // may exceed 1, and a row whose sum leaves the safe range (checked once, after
 // the loop) is recomputed by the rescaling variant below.  Keeping the
@@ -111,7 +120,6 @@ __device__ __forceinline__ void softmax_fixed(ExtendState<D, NB>& st, const f32x
     const float neg = -st.m[cb];
 #pragma unroll
     for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, neg));
-    st.l[cb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     pb[cb] = pack_p8(p);
   }
 }
@@ -153,23 +161,27 @@ __device__ __forceinline__ void softmax_rescale(ExtendState<D, NB>& st, const f3
     const float neg = (m_new == -INFINITY) ? 0.f : -m_new;
 #pragma unroll
     for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, neg));
-    st.l[cb] = st.l[cb] * alpha[cb] + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
     st.m[cb] = m_new;
     pb[cb] = pack_p8(p);
   }
   if (__builtin_amdgcn_ballot_w64(any_move)) {
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb)
+    for (int cb = 0; cb < NB; ++cb) {
+      st.lsum[cb] *= alpha[cb];
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) st.acc[cb][i] *= alpha[cb];
+    }
   }
 }
 
-template <int D, int NB>
-__global__ __launch_bounds__(64 * (16 / NB), 1) void extend_kernel(ExtendArgs a, int row_blocks) {
-  constexpr int WAVES = 16 / NB;              // 256 rows per workgroup
+// NB: 16-row column blocks per wave; WAVES per workgroup; kStages-deep LDS ring
+// of 32-key blocks with kLook blocks in flight; BLOCKS_PER_CU workgroups share a CU.
+template <int D, int NB, int WAVES, int kStages, int kLook, int BLOCKS_PER_CU>
+__global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(ExtendArgs a, int row_blocks) {
+  static_assert(kStages >= kLook + 2, "a stage is rewritten only after every wave has left it");
   constexpr int THREADS = 64 * WAVES;
   constexpr int kRowsPerWave = 16 * NB;
+  constexpr int kRowsPerBlock = WAVES * kRowsPerWave;
   constexpr int TILE = D * 4;                 // u32x4 per page tile (K then V)
   static_assert(TILE % THREADS == 0, "a page tile must split evenly over the workgroup");
   constexpr int PER_PAGE = TILE / THREADS;    // DMA instructions per thread per page
@@ -256,6 +268,10 @@ __global__ __launch_bounds__(64 * (16 / NB), 1) void extend_kernel(ExtendArgs a,
   // PV of block k from stage stg: the two pages' V quads side by side as the A
   // operand, the bf16 weights pb as the B operand (32 keys per step).
   auto pv_block = [&](const u32x4* stg, const u32x4 (&pb)[NB], int nv0, int nv1, bool vmask) {
+    constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+      st.lsum[cb] = mma_16x16x32(u32x4{kOnes, kOnes, kOnes, kOnes}, pb[cb], st.lsum[cb]);
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
       u32x4 v0 = stg[TILE / 2 + i * 64 + lane];
@@ -287,7 +303,7 @@ __global__ __launch_bounds__(64 * (16 / NB), 1) void extend_kernel(ExtendArgs a,
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
       st.m[cb] = -INFINITY;
-      st.l[cb] = 0.f;
+      st.lsum[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) st.acc[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -296,7 +312,7 @@ __global__ __launch_bounds__(64 * (16 / NB), 1) void extend_kernel(ExtendArgs a,
       if (k + kLook < nblk) issue(k + kLook);
       if (k + 1 < nblk) {
         wait_blocks<PER_BLOCK>(min(nblk - 1, k + kLook) - (k + 1));
-        __syncthreads();
+        block_barrier();
         qk_block<D, NB>(nxt, qf, ring[(k + 1) % kStages], lane);
       }
       const int kbase = k * 32;
@@ -319,7 +335,7 @@ __global__ __launch_bounds__(64 * (16 / NB), 1) void extend_kernel(ExtendArgs a,
     auto fast_step = [&](int k, f32x4 (&cur)[2][NB], f32x4 (&nxt)[2][NB]) {
       issue(k + kLook);
       wait_vmcnt<PER_BLOCK * (kLook - 1)>();
-      __syncthreads();
+      block_barrier();
       qk_block<D, NB>(nxt, qf, ring[(k + 1) % kStages], lane);
       u32x4 pb[NB];
       softmax_fixed<D, NB, false>(st, cur, pb, c, k * 32, lim_abs, s0);
@@ -328,7 +344,7 @@ __global__ __launch_bounds__(64 * (16 / NB), 1) void extend_kernel(ExtendArgs a,
 #pragma unroll 1
     for (int k = 0; k < kLook && k < nblk; ++k) issue(k);
     wait_blocks<PER_BLOCK>(min(kLook, nblk) - 1);
-    __syncthreads();
+    block_barrier();
     f32x4 sa[2][NB], sb[2][NB];
     qk_block<D, NB>(sa, qf, ring[0], lane);
     step(0, sa, sb);                        // sets each row's reference (FAST) or starts rescaling
@@ -362,19 +378,21 @@ __global__ __launch_bounds__(64 * (16 / NB), 1) void extend_kernel(ExtendArgs a,
 
   run(std::integral_constant<bool, true>{});
   // a fixed-reference sum out of range (or not finite) sends the workgroup down the rescaling path
-  __shared__ int redo;
+  // the ring is idle from here on: its first word holds the workgroup's redo flag
+  int& redo = *reinterpret_cast<int*>(&ring[0][0]);
+  __syncthreads();
   if (threadIdx.x == 0) redo = 0;
   __syncthreads();
   bool bad = false;
 #pragma unroll
-  for (int cb = 0; cb < NB; ++cb) bad |= !(st.l[cb] < kSafeSum);
+  for (int cb = 0; cb < NB; ++cb) bad |= !(st.lsum[cb][0] < kSafeSum);
   if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) redo = 1;
   __syncthreads();
   if (redo) run(std::integral_constant<bool, false>{});
 
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
-    const float l = wave_sum_across_quads(st.l[cb]);
+    const float l = st.lsum[cb][0];
     if (!rvalid[cb]) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     uint16_t* o = a.out + (int64_t(c0 + tok[cb]) * a.num_q_heads + head[cb]) * D;
@@ -386,15 +404,17 @@ __global__ __launch_bounds__(64 * (16 / NB), 1) void extend_kernel(ExtendArgs a,
   }
 }
 
-template <int D, int NB>
+template <int D, int NB, int WAVES, int STAGES, int LOOK, int PER_CU>
 hipError_t launch_extend_t(const ExtendArgs& a, hipStream_t stream) {
+  constexpr int kRowsPerBlock = WAVES * 16 * NB;
   const int G = a.num_q_heads / a.pool.num_kv_heads;
   const int row_blocks = (a.max_new * G + kRowsPerBlock - 1) / kRowsPerBlock;
   const int units = a.batch * a.pool.num_kv_heads;
   const int unit_rounds = (units + kXcds - 1) / kXcds;
   const int64_t blocks = int64_t(unit_rounds) * row_blocks * kXcds;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((extend_kernel<D, NB>), dim3(unsigned(blocks)), dim3(64 * (16 / NB)), 0, stream, a, row_blocks);
+  hipLaunchKernelGGL((extend_kernel<D, NB, WAVES, STAGES, LOOK, PER_CU>), dim3(unsigned(blocks)), dim3(64 * WAVES), 0,
+                     stream, a, row_blocks);
   return hipGetLastError();
 }
 
@@ -403,8 +423,13 @@ hipError_t launch_extend_t(const ExtendArgs& a, hipStream_t stream) {
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream) {
   // D=128: 8 waves x 32 rows (two waves per SIMD hide each other's softmax and
   // LDS latency); D=64: 4 waves x 64 rows (a 4 KiB page tile is one 256-thread load)
-  if (a.pool.head_dim == 128) return launch_extend_t<128, 2>(a, stream);
-  return launch_extend_t<64, 4>(a, stream);
+  if (a.pool.head_dim == 128) {
+    const char* v = getenv("KVS_EXTEND_VARIANT");  // tuning only
+    if (v && v[0] == '1') return launch_extend_t<128, 2, 8, 6, 4, 1>(a, stream);
+    if (v && v[0] == '2') return launch_extend_t<128, 2, 4, 5, 3, 2>(a, stream);
+    return launch_extend_t<128, 2, 4, 4, 2, 2>(a, stream);
+  }
+  return launch_extend_t<64, 4, 4, 6, 4, 1>(a, stream);
 }
 
 }  // namespace kvs
