@@ -176,7 +176,10 @@ __device__ __forceinline__ void softmax_rescale(ExtendState<D, NB>& st, const f3
 
 // NB: 16-row column blocks per wave; WAVES per workgroup; kStages-deep LDS ring
 // of 32-key blocks with kLook blocks in flight; BLOCKS_PER_CU workgroups share a CU.
-template <int D, int NB, int WAVES, int kStages, int kLook, int BLOCKS_PER_CU>
+// PIPE: QK^T of block k+1 is issued before the softmax of block k (two score
+// buffers); otherwise each block runs QK^T, softmax, PV in turn (fewer registers,
+// so more waves per SIMD can hide each other's latency).
+template <int D, int NB, int WAVES, int kStages, int kLook, int BLOCKS_PER_CU, bool PIPE>
 __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(ExtendArgs a, int row_blocks) {
   static_assert(kStages >= kLook + 2, "a stage is rewritten only after every wave has left it");
   constexpr int THREADS = 64 * WAVES;
@@ -343,6 +346,50 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
     };
 #pragma unroll 1
     for (int k = 0; k < kLook && k < nblk; ++k) issue(k);
+    if constexpr (!PIPE) {
+      // one block at a time: prefetch k+kLook, wait for k, QK^T, softmax, PV
+      auto seq_step = [&](int k, bool fast) {
+        f32x4 sc[2][NB];
+        if (fast) {
+          issue(k + kLook);
+          wait_vmcnt<PER_BLOCK * kLook>();
+        } else {
+          if (k + kLook < nblk) issue(k + kLook);
+          wait_blocks<PER_BLOCK>(min(nblk - 1, k + kLook) - k);
+        }
+        block_barrier();
+        qk_block<D, NB>(sc, qf, ring[k % kStages], lane);
+        const int kbase = k * 32;
+        u32x4 pb[NB];
+        if (fast) {
+          softmax_fixed<D, NB, false>(st, sc, pb, c, kbase, lim_abs, s0);
+          pv_block(ring[k % kStages], pb, kPage, kPage, false);
+          return;
+        }
+        const bool masked = kbase + 32 > wave_lo;
+        if (!FAST) {
+          if (masked) softmax_rescale<D, NB, true>(st, sc, pb, c, kbase, lim_abs, s0);
+          else softmax_rescale<D, NB, false>(st, sc, pb, c, kbase, lim_abs, s0);
+        } else if (k == 0) {
+          if (masked) softmax_first<D, NB, true>(st, sc, pb, c, kbase, lim_abs, s0);
+          else softmax_first<D, NB, false>(st, sc, pb, c, kbase, lim_abs, s0);
+        } else {
+          if (masked) softmax_fixed<D, NB, true>(st, sc, pb, c, kbase, lim_abs, s0);
+          else softmax_fixed<D, NB, false>(st, sc, pb, c, kbase, lim_abs, s0);
+        }
+        const int nv0 = total - kbase, nv1 = total - kbase - 16;
+        pv_block(ring[k % kStages], pb, nv0, nv1, nv1 < kPage);
+      };
+      seq_step(0, false);
+      int k = 1;
+      if (FAST) {
+#pragma unroll 1
+        for (; k < fast_end; ++k) seq_step(k, true);
+      }
+#pragma unroll 1
+      for (; k < nblk; ++k) seq_step(k, false);
+      return;
+    }
     wait_blocks<PER_BLOCK>(min(kLook, nblk) - 1);
     block_barrier();
     f32x4 sa[2][NB], sb[2][NB];
@@ -404,7 +451,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
   }
 }
 
-template <int D, int NB, int WAVES, int STAGES, int LOOK, int PER_CU>
+template <int D, int NB, int WAVES, int STAGES, int LOOK, int PER_CU, bool PIPE>
 hipError_t launch_extend_t(const ExtendArgs& a, hipStream_t stream) {
   constexpr int kRowsPerBlock = WAVES * 16 * NB;
   const int G = a.num_q_heads / a.pool.num_kv_heads;
@@ -413,7 +460,7 @@ hipError_t launch_extend_t(const ExtendArgs& a, hipStream_t stream) {
   const int unit_rounds = (units + kXcds - 1) / kXcds;
   const int64_t blocks = int64_t(unit_rounds) * row_blocks * kXcds;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((extend_kernel<D, NB, WAVES, STAGES, LOOK, PER_CU>), dim3(unsigned(blocks)), dim3(64 * WAVES), 0,
+  hipLaunchKernelGGL((extend_kernel<D, NB, WAVES, STAGES, LOOK, PER_CU, PIPE>), dim3(unsigned(blocks)), dim3(64 * WAVES), 0,
                      stream, a, row_blocks);
   return hipGetLastError();
 }
@@ -425,11 +472,14 @@ hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream) {
   // LDS latency); D=64: 4 waves x 64 rows (a 4 KiB page tile is one 256-thread load)
   if (a.pool.head_dim == 128) {
     const char* v = getenv("KVS_EXTEND_VARIANT");  // tuning only
-    if (v && v[0] == '1') return launch_extend_t<128, 2, 8, 6, 4, 1>(a, stream);
-    if (v && v[0] == '2') return launch_extend_t<128, 2, 4, 5, 3, 2>(a, stream);
-    return launch_extend_t<128, 2, 4, 4, 2, 2>(a, stream);
+    if (v && v[0] == '1') return launch_extend_t<128, 2, 8, 6, 4, 1, true>(a, stream);
+    if (v && v[0] == '2') return launch_extend_t<128, 2, 4, 5, 3, 2, true>(a, stream);
+    if (v && v[0] == '3') return launch_extend_t<128, 2, 4, 4, 2, 2, true>(a, stream);
+    if (v && v[0] == '4') return launch_extend_t<128, 2, 4, 4, 2, 2, false>(a, stream);
+    // three 4-wave workgroups per CU (three waves per SIMD), one block at a time
+    return launch_extend_t<128, 2, 4, 3, 1, 3, false>(a, stream);
   }
-  return launch_extend_t<64, 4, 4, 6, 4, 1>(a, stream);
+  return launch_extend_t<64, 4, 4, 6, 4, 1, true>(a, stream);
 }
 
 }  // namespace kvs
