@@ -4,14 +4,17 @@
 //
 // Rows of one (session, KV head) are the chunk's (token i, query head of the
 // group) pairs, token-major, so a 16-row block spans few positions and the
-// causal diagonal touches few pages.  A workgroup holds 256 rows (16*NB rows
-// per wave, Q kept in registers; at D=128 eight 32-row waves, two per SIMD, so
-// one wave's softmax and LDS waits overlap the other's matrix-core work) and
-// walks the session's keys in blocks of 32 (two pages).  Blocks are staged once
-// per workgroup in LDS by direct global->LDS 16-byte loads, kLook blocks ahead,
-// and every wave reads its matrix-core operands from there: per 32 keys and 16
-// rows a wave does 8 QK^T and 8 PV steps of 16x16x32 bf16.  The QK^T of block
-// k+1 is issued before the softmax of block k.
+// causal diagonal touches few pages.  At D=128 a workgroup of 4 waves holds 128
+// rows (32 per wave, Q in registers) and walks the session's keys in blocks of
+// 32 (two pages), staged once per workgroup in a 3-stage LDS ring by direct
+// global->LDS 16-byte loads one block ahead; three workgroups share a CU, so
+// each SIMD runs three waves whose softmax and matrix-core phases interleave.
+// Per 32 keys and 16 rows a wave does 8 QK^T and 8 PV steps of 16x16x32 bf16
+// (plus one step for the row sums).
+//
+// Q is pre-multiplied by scale*log2(e) and rounded to bf16 once, so scores leave
+// the matrix cores in log2 units; in the steady-state blocks the accumulators
+// start at -m (the row's fixed reference), and the softmax is one exp2 per score.
 //
 // Workgroups are laid out so that all row blocks of one (session, KV head) land
 // on the same XCD: hardware hands workgroup ids to the 8 XCDs round robin, and
@@ -62,10 +65,12 @@ struct ExtendState {
   float m[NB];
 };
 
-// S^T for one 32-key block: s[h][cb] covers page h of the block, rows of column block cb.
+// S^T for one 32-key block: s[h][cb] covers page h of the block, rows of column
+// block cb.  The accumulators start at init[cb] (0, or -m of the row so that the
+// block's scores come out already shifted by the row's reference).
 template <int D, int NB>
 __device__ __forceinline__ void qk_block(f32x4 (&s)[2][NB], const u32x4 (&qf)[NB][D / 32],
-                                         const u32x4* stage, int lane) {
+                                         const u32x4* stage, int lane, const float (&init)[NB]) {
   constexpr int TILE = D * 4;  // u32x4 per (page, head) tile
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -74,12 +79,27 @@ __device__ __forceinline__ void qk_block(f32x4 (&s)[2][NB], const u32x4 (&qf)[NB
     for (int i = 0; i < D / 32; ++i) kf[i] = stage[h * TILE + i * 64 + lane];
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc = {init[cb], init[cb], init[cb], init[cb]};
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) acc = mma_16x16x32(kf[i], qf[cb][i], acc);
       s[h][cb] = acc;
     }
   }
+}
+
+// q * c rounded to bf16 (8 values): the query rows carry the softmax scale in
+// log2 units, so scores come out of the matrix cores ready for exp2.
+__device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float c) {
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 4; w += 2) {
+    const float f0 = __uint_as_float(v[w] << 16) * c, f1 = __uint_as_float(v[w] & 0xFFFF0000u) * c;
+    const float f2 = __uint_as_float(v[w + 1] << 16) * c, f3 = __uint_as_float(v[w + 1] & 0xFFFF0000u) * c;
+    const u32x2 pk = pack_bf16x4(f0, f1, f2, f3);
+    r[w] = pk[0];
+    r[w + 1] = pk[1];
+  }
+  return r;
 }
 
 // Scores of one 32-key block for column block cb: 8 per lane (page 0 slots
@@ -104,7 +124,7 @@ __device__ __forceinline__ u32x4 pack_p8(const float (&p)[8]) {
 }
 
 // Softmax weights of one 32-key block against a FIXED per-row reference m
-// (set from the row's first block): p = 2^(s*c - m).  Row sums are taken by the
+// (set from the row's first block): p = 2^(s - m), s in log2 units.  Row sums are taken by the
 // PV step (an all-ones A operand), from the same bf16 weights PV uses.  Moving the reference is
 // never needed for correctness, only to keep p inside fp32/bf16 range; weights
 // may exceed 1, and a row whose sum leaves the safe range (checked once, after
@@ -112,14 +132,29 @@ __device__ __forceinline__ u32x4 pack_p8(const float (&p)[8]) {
 // accumulators free of vector ops lets them stay in accumulation registers.
 template <int D, int NB, bool MASKED>
 __device__ __forceinline__ void softmax_fixed(ExtendState<D, NB>& st, const f32x4 (&s)[2][NB], u32x4 (&pb)[NB],
-                                              float c, int kbase, const int (&lim_abs)[NB], int s0) {
+                                              int kbase, const int (&lim_abs)[NB], int s0) {
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     float x[8], p[8];
     block_scores<NB, MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
-    const float neg = -st.m[cb];
+    const float m = st.m[cb];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, neg));
+    for (int j = 0; j < 8; ++j) p[j] = exp2_fast(x[j] - m);
+    pb[cb] = pack_p8(p);
+  }
+}
+
+// Weights of a block whose scores already had the row reference subtracted (the
+// accumulators started at -m) and that no row masks: p = 2^s.
+template <int NB>
+__device__ __forceinline__ void softmax_shifted(const f32x4 (&s)[2][NB], u32x4 (&pb)[NB]) {
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+    float p[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[4 * h + j] = exp2_fast(s[h][cb][j]);
     pb[cb] = pack_p8(p);
   }
 }
@@ -127,16 +162,16 @@ __device__ __forceinline__ void softmax_fixed(ExtendState<D, NB>& st, const f32x
 // First block of a row: the reference is the block's row maximum.
 template <int D, int NB, bool MASKED>
 __device__ __forceinline__ void softmax_first(ExtendState<D, NB>& st, const f32x4 (&s)[2][NB], u32x4 (&pb)[NB],
-                                              float c, int kbase, const int (&lim_abs)[NB], int s0) {
+                                              int kbase, const int (&lim_abs)[NB], int s0) {
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     float x[8];
     block_scores<NB, MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
     const float t = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    const float m = wave_max_across_quads(t) * c;  // c > 0: the max commutes with the scale
+    const float m = wave_max_across_quads(t);
     st.m[cb] = (m == -INFINITY) ? 0.f : m;
   }
-  softmax_fixed<D, NB, MASKED>(st, s, pb, c, kbase, lim_abs, s0);
+  softmax_fixed<D, NB, MASKED>(st, s, pb, kbase, lim_abs, s0);
 }
 
 // Rescaling variant (the recomputation path): the reference follows the running
@@ -144,7 +179,7 @@ __device__ __forceinline__ void softmax_first(ExtendState<D, NB>& st, const f32x
 // are rescaled then.
 template <int D, int NB, bool MASKED>
 __device__ __forceinline__ void softmax_rescale(ExtendState<D, NB>& st, const f32x4 (&s)[2][NB], u32x4 (&pb)[NB],
-                                                float c, int kbase, const int (&lim_abs)[NB], int s0) {
+                                                int kbase, const int (&lim_abs)[NB], int s0) {
   float alpha[NB];
   bool any_move = false;
 #pragma unroll
@@ -152,7 +187,7 @@ __device__ __forceinline__ void softmax_rescale(ExtendState<D, NB>& st, const f3
     float x[8], p[8];
     block_scores<NB, MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
     const float t = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    const float tmax = wave_max_across_quads(t) * c;
+    const float tmax = wave_max_across_quads(t);
     const float m_old = st.m[cb];
     const bool move = tmax > m_old + kLazy;
     const float m_new = move ? tmax : m_old;
@@ -160,7 +195,7 @@ __device__ __forceinline__ void softmax_rescale(ExtendState<D, NB>& st, const f3
     alpha[cb] = move ? exp2_fast(m_old - m_new) : 1.f;
     const float neg = (m_new == -INFINITY) ? 0.f : -m_new;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, neg));
+    for (int j = 0; j < 8; ++j) p[j] = exp2_fast(x[j] + neg);
     st.m[cb] = m_new;
     pb[cb] = pack_p8(p);
   }
@@ -234,7 +269,8 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
     const uint16_t* qrow = a.q + (int64_t(c0 + i) * a.num_q_heads + head[cb]) * D;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
-      qf[cb][s] = rvalid[cb] ? *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * (lane >> 4))
+      qf[cb][s] = rvalid[cb] ? scale_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * (lane >> 4)),
+                                            a.scale_log2)
                              : u32x4{0u, 0u, 0u, 0u};
   }
   const bool wave_has_rows = r0 < rows;
@@ -265,8 +301,8 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
   };
 
   const int s0 = 4 * (lane >> 4);
-  const float c = a.scale_log2;
   ExtendState<D, NB> st;
+  const float zero[NB] = {};
 
   // PV of block k from stage stg: the two pages' V quads side by side as the A
   // operand, the bf16 weights pb as the B operand (32 keys per step).
@@ -316,20 +352,20 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
       if (k + 1 < nblk) {
         wait_blocks<PER_BLOCK>(min(nblk - 1, k + kLook) - (k + 1));
         block_barrier();
-        qk_block<D, NB>(nxt, qf, ring[(k + 1) % kStages], lane);
+        qk_block<D, NB>(nxt, qf, ring[(k + 1) % kStages], lane, zero);
       }
       const int kbase = k * 32;
       const bool masked = kbase + 32 > wave_lo;  // some row of the wave stops inside this block
       u32x4 pb[NB];
       if (!FAST) {
-        if (masked) softmax_rescale<D, NB, true>(st, cur, pb, c, kbase, lim_abs, s0);
-        else softmax_rescale<D, NB, false>(st, cur, pb, c, kbase, lim_abs, s0);
+        if (masked) softmax_rescale<D, NB, true>(st, cur, pb, kbase, lim_abs, s0);
+        else softmax_rescale<D, NB, false>(st, cur, pb, kbase, lim_abs, s0);
       } else if (k == 0) {
-        if (masked) softmax_first<D, NB, true>(st, cur, pb, c, kbase, lim_abs, s0);
-        else softmax_first<D, NB, false>(st, cur, pb, c, kbase, lim_abs, s0);
+        if (masked) softmax_first<D, NB, true>(st, cur, pb, kbase, lim_abs, s0);
+        else softmax_first<D, NB, false>(st, cur, pb, kbase, lim_abs, s0);
       } else {
-        if (masked) softmax_fixed<D, NB, true>(st, cur, pb, c, kbase, lim_abs, s0);
-        else softmax_fixed<D, NB, false>(st, cur, pb, c, kbase, lim_abs, s0);
+        if (masked) softmax_fixed<D, NB, true>(st, cur, pb, kbase, lim_abs, s0);
+        else softmax_fixed<D, NB, false>(st, cur, pb, kbase, lim_abs, s0);
       }
       const int nv0 = total - kbase, nv1 = total - kbase - 16;
       pv_block(ring[k % kStages], pb, nv0, nv1, nv1 < kPage);
@@ -339,9 +375,9 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
       issue(k + kLook);
       wait_vmcnt<PER_BLOCK * (kLook - 1)>();
       block_barrier();
-      qk_block<D, NB>(nxt, qf, ring[(k + 1) % kStages], lane);
+      qk_block<D, NB>(nxt, qf, ring[(k + 1) % kStages], lane, zero);
       u32x4 pb[NB];
-      softmax_fixed<D, NB, false>(st, cur, pb, c, k * 32, lim_abs, s0);
+      softmax_fixed<D, NB, false>(st, cur, pb, k * 32, lim_abs, s0);
       pv_block(ring[k % kStages], pb, kPage, kPage, false);
     };
 #pragma unroll 1
@@ -358,27 +394,42 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
           wait_blocks<PER_BLOCK>(min(nblk - 1, k + kLook) - k);
         }
         block_barrier();
-        qk_block<D, NB>(sc, qf, ring[k % kStages], lane);
+        // matrix-core phases run at raised wave priority, so a SIMD's other waves
+        // fill the gaps with their softmax work rather than delaying these steps
+        __builtin_amdgcn_s_setprio(2);
+        if (fast) {
+          float negm[NB];
+#pragma unroll
+          for (int cb = 0; cb < NB; ++cb) negm[cb] = -st.m[cb];
+          qk_block<D, NB>(sc, qf, ring[k % kStages], lane, negm);
+        } else {
+          qk_block<D, NB>(sc, qf, ring[k % kStages], lane, zero);
+        }
+        __builtin_amdgcn_s_setprio(0);
         const int kbase = k * 32;
         u32x4 pb[NB];
         if (fast) {
-          softmax_fixed<D, NB, false>(st, sc, pb, c, kbase, lim_abs, s0);
+          softmax_shifted<NB>(sc, pb);
+          __builtin_amdgcn_s_setprio(2);
           pv_block(ring[k % kStages], pb, kPage, kPage, false);
+          __builtin_amdgcn_s_setprio(0);
           return;
         }
         const bool masked = kbase + 32 > wave_lo;
         if (!FAST) {
-          if (masked) softmax_rescale<D, NB, true>(st, sc, pb, c, kbase, lim_abs, s0);
-          else softmax_rescale<D, NB, false>(st, sc, pb, c, kbase, lim_abs, s0);
+          if (masked) softmax_rescale<D, NB, true>(st, sc, pb, kbase, lim_abs, s0);
+          else softmax_rescale<D, NB, false>(st, sc, pb, kbase, lim_abs, s0);
         } else if (k == 0) {
-          if (masked) softmax_first<D, NB, true>(st, sc, pb, c, kbase, lim_abs, s0);
-          else softmax_first<D, NB, false>(st, sc, pb, c, kbase, lim_abs, s0);
+          if (masked) softmax_first<D, NB, true>(st, sc, pb, kbase, lim_abs, s0);
+          else softmax_first<D, NB, false>(st, sc, pb, kbase, lim_abs, s0);
         } else {
-          if (masked) softmax_fixed<D, NB, true>(st, sc, pb, c, kbase, lim_abs, s0);
-          else softmax_fixed<D, NB, false>(st, sc, pb, c, kbase, lim_abs, s0);
+          if (masked) softmax_fixed<D, NB, true>(st, sc, pb, kbase, lim_abs, s0);
+          else softmax_fixed<D, NB, false>(st, sc, pb, kbase, lim_abs, s0);
         }
         const int nv0 = total - kbase, nv1 = total - kbase - 16;
+        __builtin_amdgcn_s_setprio(2);
         pv_block(ring[k % kStages], pb, nv0, nv1, nv1 < kPage);
+        __builtin_amdgcn_s_setprio(0);
       };
       seq_step(0, false);
       int k = 1;
@@ -393,7 +444,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
     wait_blocks<PER_BLOCK>(min(kLook, nblk) - 1);
     block_barrier();
     f32x4 sa[2][NB], sb[2][NB];
-    qk_block<D, NB>(sa, qf, ring[0], lane);
+    qk_block<D, NB>(sa, qf, ring[0], lane, zero);
     step(0, sa, sb);                        // sets each row's reference (FAST) or starts rescaling
     int k = 1;
     if (FAST) {
