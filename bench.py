@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--extend-calls", type=int, default=20)
+    ap.add_argument("--extend-calls", type=int, default=40)
+    ap.add_argument("--extend-warmup", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -349,7 +350,7 @@ def main():
     # ---- extend ----
     ew = W.make_workload(EXTEND_WORKLOAD)
     es = setup_extend(ew)
-    for _ in range(3):
+    for _ in range(args.extend_warmup):  # ~1 ms each: brings the clocks to their steady state
         extend_call(ew, es)
     torch.cuda.synchronize()
     et = EventTimer()

@@ -4,8 +4,8 @@
 // in fixed-size blocks; ICaRus, overall framework: E_base writes the KV all
 // decoders read).  One workgroup per (window of up to 16 new tokens that share a
 // page, KV head, session).  K rows are moved as 16-byte runs; the V part of a
-// tile is stored with 4 slots of one head-dim value side by side, so a thread
-// gathers those 4 slots and writes them as one 8-byte word when all 4 are new,
+// tile is stored with 8 slots of one head-dim value side by side, so a thread
+// gathers those 8 slots and writes them as one 16-byte run when all 8 are new,
 // and slot by slot otherwise (slots not being appended are never touched).
 #include "kvs_device.h"
 #include "kvs_internal.h"
@@ -51,21 +51,24 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(ksrc + int64_t(c0 + t - P) * row_stride + d0);
     *reinterpret_cast<u32x4*>(tile + ((d0 / 32) * 64 + ((d0 % 32) / 8) * 16 + slot) * 8) = v;
   }
-  // V: one thread per (group of 4 slots, head-dim value)
+  // V: one thread per (run of 8 slots, head-dim value)
   uint16_t* vt = tile + kPage * D;
-  for (int e = threadIdx.x; e < 4 * D; e += 256) {
-    const int quad = e / D, d = e % D;
-    const int base = lp * kPage + 4 * quad;
-    uint16_t* dst = vt + ((d / 32) * 64 + quad * 16 + d % 16) * 8 + ((d / 16) % 2) * 4;
-    if (base >= t0 && base + 3 < t1) {
-      uint16_t x[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) x[c] = vsrc[int64_t(c0 + base + c - P) * row_stride + d];
-      *reinterpret_cast<u32x2*>(dst) =
-          u32x2{uint32_t(x[0]) | (uint32_t(x[1]) << 16), uint32_t(x[2]) | (uint32_t(x[3]) << 16)};
-    } else {
+  for (int e = threadIdx.x; e < 2 * D; e += 256) {
+    const int run = e / D, d = e % D;
+    const int base = lp * kPage + 8 * run;
+    uint16_t* dst = vt + ((d / 16) * 32 + run * 16 + d % 16) * 8;
+    if (base >= t0 && base + 7 < t1) {
+      uint32_t w[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
+        const uint32_t lo = vsrc[int64_t(c0 + base + 2 * c - P) * row_stride + d];
+        const uint32_t hi = vsrc[int64_t(c0 + base + 2 * c + 1 - P) * row_stride + d];
+        w[c] = lo | (hi << 16);
+      }
+      *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
         const int t = base + c;
         if (t >= t0 && t < t1) dst[c] = vsrc[int64_t(c0 + t - P) * row_stride + d];
       }

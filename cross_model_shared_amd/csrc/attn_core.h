@@ -42,21 +42,23 @@ struct QFrag {
   u32x4 q[NB][D / 32];
 };
 
-// Process one page.  kf/vf: the lane's K and V slab operands of the page.
+// Process one page.  kf: the lane's K operands of the page (head dims 32i +
+// 8(lane/16) .. +7 of slot lane%16); vf: its V operands (slots 4(lane/16) .. +3 of
+// head dim 16s + lane%16).
 // lim[cb]: exclusive key limit of this lane's row in column block cb, as a slot
 // count relative to the page start (<= 0: row sees nothing here; >= 16: all).
 // nvalid: slots of the page holding data (later slots are never read).
 // masked: false when every row sees all 16 slots (the common case).
 template <int D, int NB>
 __device__ __forceinline__ void attend_page(RowState<D, NB>& st, const QFrag<D, NB>& qf,
-                                            const u32x4 (&kf)[D / 32], u32x4 (&vf)[D / 32],
+                                            const u32x4 (&kf)[D / 32], u32x2 (&vf)[D / 16],
                                             float scale_log2, bool masked, const int (&lim)[NB],
                                             int nvalid, int lane) {
+  const int s0 = 4 * (lane >> 4);
   if (nvalid < kPage) {
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) vf[i] = mask_v_slab(vf[i], lane, nvalid);
+    for (int i = 0; i < D / 16; ++i) vf[i] = mask_v_quad(vf[i], s0, nvalid);
   }
-  const int s0 = 4 * (lane >> 4);
   f32x4 s[NB];
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
@@ -98,12 +100,9 @@ __device__ __forceinline__ void attend_page(RowState<D, NB>& st, const QFrag<D, 
       for (int i = 0; i < D / 16; ++i) st.acc[cb][i] *= alpha[cb];
   }
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
+  for (int i = 0; i < D / 16; ++i) {
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-      st.acc[cb][2 * i] = mma_16x16x16(u32x2{vf[i][0], vf[i][1]}, pb[cb], st.acc[cb][2 * i]);
-      st.acc[cb][2 * i + 1] = mma_16x16x16(u32x2{vf[i][2], vf[i][3]}, pb[cb], st.acc[cb][2 * i + 1]);
-    }
+    for (int cb = 0; cb < NB; ++cb) st.acc[cb][i] = mma_16x16x16(vf[i], pb[cb], st.acc[cb][i]);
   }
 }
 

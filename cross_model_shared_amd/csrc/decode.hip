@@ -256,12 +256,13 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
     if (j + S - 1 < n) issue((j + S - 1) % S);
     wait_ring<SLABS, S>(min(S - 1, n - 1 - j));
     if (!((bad >> slot) & 1u)) {
-      u32x4 kf[D / 32], vf[D / 32];
+      u32x4 kf[D / 32];
+      u32x2 vf[D / 16];
+      const u32x2* v2 = reinterpret_cast<const u32x2*>(ring[wave][slot]);
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) {
-        kf[i] = ring[wave][slot][i * 64 + lane];
-        vf[i] = ring[wave][slot][(D / 32 + i) * 64 + lane];
-      }
+      for (int i = 0; i < D / 32; ++i) kf[i] = ring[wave][slot][k_run(i, lane >> 4, lane & 15)];
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) vf[i] = v2[2 * v_run(D, i, lane >> 5, lane & 15) + ((lane >> 4) & 1)];
       const int L = clamp_len(load_uniform(a.seq_lens + cw.b), a.max_seq_len);
       const int nvalid = min(kPage, L - cw.page * kPage);
       int lim[NB];

@@ -65,18 +65,28 @@ struct ExtendState {
   float m[NB];
 };
 
-// S^T for one 32-key block: s[h][cb] covers page h of the block, rows of column
-// block cb.  The accumulators start at init[cb] (0, or -m of the row so that the
-// block's scores come out already shifted by the row's reference).
+// Stage layout: the two page tiles of a block as stored in the pool, the second
+// one 64 bytes further on, so that lanes reading the same run index of both
+// pages hit different LDS banks.
+constexpr int kPad = 4;  // u32x4
+
+// S^T for one 32-key block, as two 16-key halves h.  Lane l (row l%16 on the N
+// side, group g = l/16 on the M side) reads, for half h, the K run of page
+// (l%16)/8 and slot 8((l/4)%2) + 4h + l%4: the M index of a half mixes the two
+// pages so that the result holds, in lane group g, block keys 8g + 4h + j (j =
+// 0..3), i.e. 8 consecutive keys of one page over both halves.  That is the
+// B-operand order of the PV step, whose A operand is then one 16-byte run of V
+// (8 consecutive slots of one head-dim value).  koff[h]: the lane's run index
+// for half h.  The accumulators start at init[cb] (0, or -m of the row so that
+// the block's scores come out already shifted by the row's reference).
 template <int D, int NB>
 __device__ __forceinline__ void qk_block(f32x4 (&s)[2][NB], const u32x4 (&qf)[NB][D / 32],
-                                         const u32x4* stage, int lane, const float (&init)[NB]) {
-  constexpr int TILE = D * 4;  // u32x4 per (page, head) tile
+                                         const u32x4* stage, const int (&koff)[2], const float (&init)[NB]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     u32x4 kf[D / 32];
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) kf[i] = stage[h * TILE + i * 64 + lane];
+    for (int i = 0; i < D / 32; ++i) kf[i] = stage[koff[h] + k_run(i, 0, 0)];
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
       f32x4 acc = {init[cb], init[cb], init[cb], init[cb]};
@@ -102,8 +112,8 @@ __device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float c) {
   return r;
 }
 
-// Scores of one 32-key block for column block cb: 8 per lane (page 0 slots
-// s0..s0+3, then page 1), masked to -inf past each row's key limit.
+// Scores of one 32-key block for column block cb: 8 per lane, block keys
+// s0..s0+7 (s0 = 8 * lane group), masked to -inf past each row's key limit.
 template <int NB, bool MASKED>
 __device__ __forceinline__ void block_scores(float (&x)[8], const f32x4 (&s)[2][NB], int cb, int kbase,
                                              int lim, int s0) {
@@ -112,7 +122,7 @@ __device__ __forceinline__ void block_scores(float (&x)[8], const f32x4 (&s)[2][
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float v = s[h][cb][j];
-      if (MASKED) v = (kbase + 16 * h + s0 + j < lim) ? v : -INFINITY;
+      if (MASKED) v = (kbase + s0 + 4 * h + j < lim) ? v : -INFINITY;
       x[4 * h + j] = v;
     }
 }
@@ -224,7 +234,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
   static_assert(TILE % THREADS == 0, "a page tile must split evenly over the workgroup");
   constexpr int PER_PAGE = TILE / THREADS;    // DMA instructions per thread per page
   constexpr int PER_BLOCK = 2 * PER_PAGE;
-  __shared__ u32x4 ring[kStages][2 * TILE];
+  __shared__ u32x4 ring[kStages][2 * TILE + kPad];
 
   const int Hkv = a.pool.num_kv_heads;
   const int units = a.batch * Hkv;
@@ -291,7 +301,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
         pid = 0;  // in-range stand-in; the session's output is unspecified
       }
       const u32x4* tile = reinterpret_cast<const u32x4*>(a.pool.data + tile_offset(a.layer, pid, g, num_pages, Hkv, D));
-      u32x4* dst = &ring[k % kStages][h * TILE];
+      u32x4* dst = &ring[k % kStages][h * (TILE + kPad)];
 #pragma unroll
       for (int j = 0; j < PER_PAGE; ++j)
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + j * THREADS + tid),
@@ -300,32 +310,31 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
     }
   };
 
-  const int s0 = 4 * (lane >> 4);
+  const int s0 = 8 * (lane >> 4);  // first block key of the lane's scores and weights
   ExtendState<D, NB> st;
   const float zero[NB] = {};
+  int koff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    koff[h] = ((lane >> 3) & 1) * (TILE + kPad) + k_run(0, lane >> 4, 8 * ((lane >> 2) & 1) + 4 * h + (lane & 3));
+  // V run of page (lane/32), slots 8((lane/16)%2) .. +7, head dim 16s + lane%16
+  const int voff = (lane >> 5) * (TILE + kPad) + v_run(D, 0, (lane >> 4) & 1, lane & 15);
+  const int vfirst = 8 * ((lane >> 4) & 1);
 
-  // PV of block k from stage stg: the two pages' V quads side by side as the A
-  // operand, the bf16 weights pb as the B operand (32 keys per step).
+  // PV of block k from stage stg: one V run per 16 head dims as the A operand,
+  // the bf16 weights pb as the B operand (32 keys per step).
   auto pv_block = [&](const u32x4* stg, const u32x4 (&pb)[NB], int nv0, int nv1, bool vmask) {
     constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb)
       st.lsum[cb] = mma_16x16x32(u32x4{kOnes, kOnes, kOnes, kOnes}, pb[cb], st.lsum[cb]);
+    const int nv = (lane >> 5) ? nv1 : nv0;
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      u32x4 v0 = stg[TILE / 2 + i * 64 + lane];
-      u32x4 v1 = stg[TILE + TILE / 2 + i * 64 + lane];
-      if (vmask) {
-        v0 = mask_v_slab(v0, lane, nv0);
-        v1 = mask_v_slab(v1, lane, nv1);
-      }
-      const u32x4 a0 = {v0[0], v0[1], v1[0], v1[1]};   // head dims 32i + 0..15
-      const u32x4 a1 = {v0[2], v0[3], v1[2], v1[3]};   // head dims 32i + 16..31
+    for (int i = 0; i < D / 16; ++i) {
+      u32x4 va = stg[voff + v_run(D, i, 0, 0) - v_run(D, 0, 0, 0)];
+      if (vmask) va = mask_v_run(va, vfirst, nv);
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        st.acc[cb][2 * i] = mma_16x16x32(a0, pb[cb], st.acc[cb][2 * i]);
-        st.acc[cb][2 * i + 1] = mma_16x16x32(a1, pb[cb], st.acc[cb][2 * i + 1]);
-      }
+      for (int cb = 0; cb < NB; ++cb) st.acc[cb][i] = mma_16x16x32(va, pb[cb], st.acc[cb][i]);
     }
   };
 
@@ -352,7 +361,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
       if (k + 1 < nblk) {
         wait_blocks<PER_BLOCK>(min(nblk - 1, k + kLook) - (k + 1));
         block_barrier();
-        qk_block<D, NB>(nxt, qf, ring[(k + 1) % kStages], lane, zero);
+        qk_block<D, NB>(nxt, qf, ring[(k + 1) % kStages], koff, zero);
       }
       const int kbase = k * 32;
       const bool masked = kbase + 32 > wave_lo;  // some row of the wave stops inside this block
@@ -375,7 +384,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
       issue(k + kLook);
       wait_vmcnt<PER_BLOCK * (kLook - 1)>();
       block_barrier();
-      qk_block<D, NB>(nxt, qf, ring[(k + 1) % kStages], lane, zero);
+      qk_block<D, NB>(nxt, qf, ring[(k + 1) % kStages], koff, zero);
       u32x4 pb[NB];
       softmax_fixed<D, NB, false>(st, cur, pb, k * 32, lim_abs, s0);
       pv_block(ring[k % kStages], pb, kPage, kPage, false);
@@ -401,9 +410,9 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
           float negm[NB];
 #pragma unroll
           for (int cb = 0; cb < NB; ++cb) negm[cb] = -st.m[cb];
-          qk_block<D, NB>(sc, qf, ring[k % kStages], lane, negm);
+          qk_block<D, NB>(sc, qf, ring[k % kStages], koff, negm);
         } else {
-          qk_block<D, NB>(sc, qf, ring[k % kStages], lane, zero);
+          qk_block<D, NB>(sc, qf, ring[k % kStages], koff, zero);
         }
         __builtin_amdgcn_s_setprio(0);
         const int kbase = k * 32;
@@ -444,7 +453,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
     wait_blocks<PER_BLOCK>(min(kLook, nblk) - 1);
     block_barrier();
     f32x4 sa[2][NB], sb[2][NB];
-    qk_block<D, NB>(sa, qf, ring[0], lane, zero);
+    qk_block<D, NB>(sa, qf, ring[0], koff, zero);
     step(0, sa, sb);                        // sets each row's reference (FAST) or starts rescaling
     int k = 1;
     if (FAST) {

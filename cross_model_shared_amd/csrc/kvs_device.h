@@ -27,17 +27,11 @@ __device__ __forceinline__ int64_t tile_offset(int layer, int page, int head, in
   return ((int64_t(layer) * num_pages + page) * num_kv_heads + head) * int64_t(32 * D);
 }
 
-// One lane's 16-byte operand of K slab `i` (head dims 32i..32i+31): slot lane%16,
-// head dims 32i + 8*(lane/16) .. +7.  As an A operand of the 16x16x32 step this is
-// row (slot) lane%16, k = 8*(lane/16)+c — the K tile is stored in exactly this order.
-__device__ __forceinline__ u32x4 load_k_slab(const uint16_t* tile, int i, int lane) {
-  return reinterpret_cast<const u32x4*>(tile)[i * kWave + lane];
-}
-// One lane's 16 bytes of V slab `i`: head dims 32i + 16*half + lane%16 (half = 0, 1),
-// slots 4*(lane/16) .. +3 for each half.
-__device__ __forceinline__ u32x4 load_v_slab(const uint16_t* tile, int D, int i, int lane) {
-  return reinterpret_cast<const u32x4*>(tile + 16 * D)[i * kWave + lane];
-}
+// Tile geometry in 16-byte units: a K part of 2*D runs (run (i, kg, t) = 8 head
+// dims 32i+8kg.. of slot t at index 64i + 16kg + t), then a V part of 2*D runs
+// (run (s, o, m) = slots 8o..8o+7 of head dim 16s+m at index 2*D + 32s + 16o + m).
+__device__ __forceinline__ constexpr int k_run(int i, int kg, int t) { return 64 * i + 16 * kg + t; }
+__device__ __forceinline__ constexpr int v_run(int D, int s, int o, int m) { return 2 * D + 32 * s + 16 * o + m; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ i16x4 as_i16x4(u32x2 v) { return __builtin_bit_cast(i16x4, v); }
@@ -83,18 +77,19 @@ __device__ __forceinline__ float wave_sum_across_quads(float x) {
 // 2^-126 flush to zero, which a softmax weight can afford).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Zero the V operand entries (both halves) of slots >= nvalid.  Slots past a
-// session's end may hold anything, NaN included, and 0 * NaN would poison PV.
-__device__ __forceinline__ u32x4 mask_v_slab(u32x4 v, int lane, int nvalid) {
-  const int s0 = 4 * (lane >> 4);
-  // dword j of each half holds slots s0+2j (low 16 bits) and s0+2j+1 (high)
-  uint32_t m0 = (s0 + 0 < nvalid ? 0x0000FFFFu : 0u) | (s0 + 1 < nvalid ? 0xFFFF0000u : 0u);
-  uint32_t m1 = (s0 + 2 < nvalid ? 0x0000FFFFu : 0u) | (s0 + 3 < nvalid ? 0xFFFF0000u : 0u);
-  v[0] &= m0;
-  v[1] &= m1;
-  v[2] &= m0;
-  v[3] &= m1;
+// Zero the entries of slots >= nvalid in 4 consecutive slots first..first+3 of
+// one head-dim value (8 bytes).  Slots past a session's end may hold anything,
+// NaN included, and 0 * NaN would poison PV.
+__device__ __forceinline__ u32x2 mask_v_quad(u32x2 v, int first, int nvalid) {
+  v[0] &= (first + 0 < nvalid ? 0x0000FFFFu : 0u) | (first + 1 < nvalid ? 0xFFFF0000u : 0u);
+  v[1] &= (first + 2 < nvalid ? 0x0000FFFFu : 0u) | (first + 3 < nvalid ? 0xFFFF0000u : 0u);
   return v;
+}
+// The same for 8 consecutive slots first..first+7 (16 bytes).
+__device__ __forceinline__ u32x4 mask_v_run(u32x4 v, int first, int nvalid) {
+  const u32x2 lo = mask_v_quad(u32x2{v[0], v[1]}, first, nvalid);
+  const u32x2 hi = mask_v_quad(u32x2{v[2], v[3]}, first + 4, nvalid);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
 // Load through the constant address space: with a wave-uniform address this is

@@ -52,12 +52,15 @@
  *
  *    tile(layer, page, head) = ((layer*num_pages + page)*num_kv_heads + head) * 32*D
  *    K(t, d) = tile + ((d/32)*64 + ((d%32)/8)*16 + t) * 8 + d%8
- *    V(t, d) = tile + 16*D + ((d/32)*64 + (t/4)*16 + d%16) * 8 + ((d/16)%2)*4 + t%4
+ *    V(t, d) = tile + 16*D + ((d/16)*32 + (t/8)*16 + d%16) * 8 + t%8
  *
- *  t is the slot in the page (0..15), d the head-dim index.  Each 1 KiB group
- *  (fixed d/32) is exactly the set of 64 16-byte lane operands of one gfx950
- *  16x16 bf16 matrix-core step, so a wave reads a K or V tile with fully
- *  contiguous 16-byte loads and needs no transpose.  A tile is 8 KiB at D=128.
+ *  t is the slot in the page (0..15), d the head-dim index.  K: each 1 KiB group
+ *  (fixed d/32) is the set of 64 16-byte lane operands (8 head-dim values of one
+ *  slot) of one gfx950 16x16x32 bf16 matrix-core step.  V: each 512-byte group
+ *  (fixed d/16) holds the 16-byte runs of 8 consecutive slots of one head-dim
+ *  value, the A operand of a 16x16x32 step whose 32 reduction indices are the
+ *  slots of two pages.  Both parts are read as contiguous 16-byte loads, with
+ *  no transpose.  A tile is 8 KiB at D=128.
  *
  *  Logical token position p of session b lives in page block_table[b*bt_stride
  *  + p/16], slot p%16.  Block table entries past ceil(len/16) are never read

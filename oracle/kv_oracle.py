@@ -63,10 +63,9 @@ def k_offset(t: int, d: int) -> int:
 
 def v_offset(t: int, d: int) -> int:
     """Offset of V(slot t, dim d) inside the V part of a tile."""
-    group = d // 32
-    lane = (t // 4) * 16 + d % 16
-    half = (d // 16) % 2
-    return (group * 64 + lane) * 8 + half * 4 + t % 4
+    slab = d // 16                  # which 16-wide slab of the head dim
+    run = (t // 8) * 16 + d % 16    # 8 consecutive slots of one head-dim value
+    return (slab * 32 + run) * 8 + t % 8
 
 
 def tile_start(layer: int, page: int, head: int, num_pages: int, num_kv_heads: int,

@@ -105,11 +105,15 @@ def test_layout_lane_operand_runs(D):
         for d0 in range(0, D, 8):
             offs = [oracle.k_offset(t, d0 + c) for c in range(8)]
             assert offs == list(range(offs[0], offs[0] + 8)) and offs[0] % 8 == 0
-    # V: 4 consecutive slots of one head-dim value are 8 contiguous bytes
+    # V: 8 consecutive slots of one head-dim value are 16 contiguous bytes
     for d in range(D):
-        for t0 in range(0, 16, 4):
-            offs = [oracle.v_offset(t0 + c, d) for c in range(4)]
-            assert offs == list(range(offs[0], offs[0] + 4)) and offs[0] % 4 == 0
+        for t0 in (0, 8):
+            offs = [oracle.v_offset(t0 + c, d) for c in range(8)]
+            assert offs == list(range(offs[0], offs[0] + 8)) and offs[0] % 8 == 0
+    # V: the runs of one 16-wide slab of the head dim fill their own 512 bytes
+    for t in range(16):
+        for d in range(D):
+            assert oracle.v_offset(t, d) // 256 == d // 16
     # each 32-wide slab of the head dim occupies its own 1 KiB (512 elements)
     for t in range(16):
         for d in range(D):

@@ -50,7 +50,8 @@ MUTANTS = {
     "append_wrong_position": ("p = int(seq_lens[b]) + j", "p = int(seq_lens[b]) + j + 1"),
     "bf16_wrong_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
     "layout_lane_order": ("lane = sub * 16 + t", "lane = t * 4 + sub"),
-    "v_layout_half": ("half = (d // 16) % 2", "half = (d // 32) % 2"),
+    "v_layout_run": ("run = (t // 8) * 16 + d % 16", "run = (t // 8) * 16 + d % 8"),
+    "v_layout_slab": ("slab = d // 16 ", "slab = d // 32 "),
     "decode_prefix_off_by_one": ("K, V = gather(pool, shape, layer, block_table[b], L)",
                                  "K, V = gather(pool, shape, layer, block_table[b], max(L - 1, 0))"),
 }
