@@ -76,17 +76,17 @@ constexpr int kPad = 4;  // u32x4
 // pages so that the result holds, in lane group g, block keys 8g + 4h + j (j =
 // 0..3), i.e. 8 consecutive keys of one page over both halves.  That is the
 // B-operand order of the PV step, whose A operand is then one 16-byte run of V
-// (8 consecutive slots of one head-dim value).  koff[h]: the lane's run index
-// for half h.  The accumulators start at init[cb] (0, or -m of the row so that
+// (8 consecutive slots of one head-dim value).  koff: the lane's run index for
+// half 0 (half 1 reads 4 slots further on).  The accumulators start at init[cb] (0, or -m of the row so that
 // the block's scores come out already shifted by the row's reference).
 template <int D, int NB>
 __device__ __forceinline__ void qk_block(f32x4 (&s)[2][NB], const u32x4 (&qf)[NB][D / 32],
-                                         const u32x4* stage, const int (&koff)[2], const float (&init)[NB]) {
+                                         const u32x4* stage, int koff, const float (&init)[NB]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     u32x4 kf[D / 32];
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) kf[i] = stage[koff[h] + k_run(i, 0, 0)];
+    for (int i = 0; i < D / 32; ++i) kf[i] = stage[koff + k_run(i, 0, 4 * h)];
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
       f32x4 acc = {init[cb], init[cb], init[cb], init[cb]};
@@ -112,11 +112,21 @@ __device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float c) {
   return r;
 }
 
+// A copy of the lane id that the compiler cannot hoist or keep: values derived
+// from it are recomputed where they are used (on the cold, masked paths) rather
+// than held in registers across the key walk.
+__device__ __forceinline__ int fresh_lane() {
+  int ln = threadIdx.x & 63;
+  asm volatile("" : "+v"(ln));
+  return ln;
+}
+
 // Scores of one 32-key block for column block cb: 8 per lane, block keys
 // s0..s0+7 (s0 = 8 * lane group), masked to -inf past each row's key limit.
 template <int NB, bool MASKED>
 __device__ __forceinline__ void block_scores(float (&x)[8], const f32x4 (&s)[2][NB], int cb, int kbase,
-                                             int lim, int s0) {
+                                             int lim) {
+  const int s0 = MASKED ? 8 * (fresh_lane() >> 4) : 0;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -142,11 +152,11 @@ __device__ __forceinline__ u32x4 pack_p8(const float (&p)[8]) {
 // accumulators free of vector ops lets them stay in accumulation registers.
 template <int D, int NB, bool MASKED>
 __device__ __forceinline__ void softmax_fixed(ExtendState<D, NB>& st, const f32x4 (&s)[2][NB], u32x4 (&pb)[NB],
-                                              int kbase, const int (&lim_abs)[NB], int s0) {
+                                              int kbase, const int (&lim_abs)[NB]) {
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     float x[8], p[8];
-    block_scores<NB, MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
+    block_scores<NB, MASKED>(x, s, cb, kbase, lim_abs[cb]);
     const float m = st.m[cb];
 #pragma unroll
     for (int j = 0; j < 8; ++j) p[j] = exp2_fast(x[j] - m);
@@ -172,16 +182,16 @@ __device__ __forceinline__ void softmax_shifted(const f32x4 (&s)[2][NB], u32x4 (
 // First block of a row: the reference is the block's row maximum.
 template <int D, int NB, bool MASKED>
 __device__ __forceinline__ void softmax_first(ExtendState<D, NB>& st, const f32x4 (&s)[2][NB], u32x4 (&pb)[NB],
-                                              int kbase, const int (&lim_abs)[NB], int s0) {
+                                              int kbase, const int (&lim_abs)[NB]) {
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     float x[8];
-    block_scores<NB, MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
+    block_scores<NB, MASKED>(x, s, cb, kbase, lim_abs[cb]);
     const float t = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     const float m = wave_max_across_quads(t);
     st.m[cb] = (m == -INFINITY) ? 0.f : m;
   }
-  softmax_fixed<D, NB, MASKED>(st, s, pb, kbase, lim_abs, s0);
+  softmax_fixed<D, NB, MASKED>(st, s, pb, kbase, lim_abs);
 }
 
 // Rescaling variant (the recomputation path): the reference follows the running
@@ -189,13 +199,13 @@ __device__ __forceinline__ void softmax_first(ExtendState<D, NB>& st, const f32x
 // are rescaled then.
 template <int D, int NB, bool MASKED>
 __device__ __forceinline__ void softmax_rescale(ExtendState<D, NB>& st, const f32x4 (&s)[2][NB], u32x4 (&pb)[NB],
-                                                int kbase, const int (&lim_abs)[NB], int s0) {
+                                                int kbase, const int (&lim_abs)[NB]) {
   float alpha[NB];
   bool any_move = false;
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     float x[8], p[8];
-    block_scores<NB, MASKED>(x, s, cb, kbase, lim_abs[cb], s0);
+    block_scores<NB, MASKED>(x, s, cb, kbase, lim_abs[cb]);
     const float t = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     const float tmax = wave_max_across_quads(t);
     const float m_old = st.m[cb];
@@ -266,17 +276,15 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
   // ---- this wave's rows ----
   const int r0 = rbase + wave * kRowsPerWave;
   u32x4 qf[NB][D / 32];
-  int lim_abs[NB], tok[NB], head[NB];
+  int lim_abs[NB];
   bool rvalid[NB];
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     const int r = r0 + cb * 16 + (lane & 15);
     rvalid[cb] = r < rows;
     const int i = rvalid[cb] ? r / G : C - 1;
-    tok[cb] = i;
-    head[cb] = g * G + (rvalid[cb] ? r % G : 0);
     lim_abs[cb] = P + i + 1;
-    const uint16_t* qrow = a.q + (int64_t(c0 + i) * a.num_q_heads + head[cb]) * D;
+    const uint16_t* qrow = a.q + (int64_t(c0 + i) * a.num_q_heads + g * G + (rvalid[cb] ? r % G : 0)) * D;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
       qf[cb][s] = rvalid[cb] ? scale_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * (lane >> 4)),
@@ -310,16 +318,11 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
     }
   };
 
-  const int s0 = 8 * (lane >> 4);  // first block key of the lane's scores and weights
   ExtendState<D, NB> st;
   const float zero[NB] = {};
-  int koff[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-    koff[h] = ((lane >> 3) & 1) * (TILE + kPad) + k_run(0, lane >> 4, 8 * ((lane >> 2) & 1) + 4 * h + (lane & 3));
+  const int koff = ((lane >> 3) & 1) * (TILE + kPad) + k_run(0, lane >> 4, 8 * ((lane >> 2) & 1) + (lane & 3));
   // V run of page (lane/32), slots 8((lane/16)%2) .. +7, head dim 16s + lane%16
   const int voff = (lane >> 5) * (TILE + kPad) + v_run(D, 0, (lane >> 4) & 1, lane & 15);
-  const int vfirst = 8 * ((lane >> 4) & 1);
 
   // PV of block k from stage stg: one V run per 16 head dims as the A operand,
   // the bf16 weights pb as the B operand (32 keys per step).
@@ -332,7 +335,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
       u32x4 va = stg[voff + v_run(D, i, 0, 0) - v_run(D, 0, 0, 0)];
-      if (vmask) va = mask_v_run(va, vfirst, nv);
+      if (vmask) va = mask_v_run(va, 8 * ((fresh_lane() >> 4) & 1), nv);
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) st.acc[cb][i] = mma_16x16x32(va, pb[cb], st.acc[cb][i]);
     }
@@ -367,14 +370,14 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
       const bool masked = kbase + 32 > wave_lo;  // some row of the wave stops inside this block
       u32x4 pb[NB];
       if (!FAST) {
-        if (masked) softmax_rescale<D, NB, true>(st, cur, pb, kbase, lim_abs, s0);
-        else softmax_rescale<D, NB, false>(st, cur, pb, kbase, lim_abs, s0);
+        if (masked) softmax_rescale<D, NB, true>(st, cur, pb, kbase, lim_abs);
+        else softmax_rescale<D, NB, false>(st, cur, pb, kbase, lim_abs);
       } else if (k == 0) {
-        if (masked) softmax_first<D, NB, true>(st, cur, pb, kbase, lim_abs, s0);
-        else softmax_first<D, NB, false>(st, cur, pb, kbase, lim_abs, s0);
+        if (masked) softmax_first<D, NB, true>(st, cur, pb, kbase, lim_abs);
+        else softmax_first<D, NB, false>(st, cur, pb, kbase, lim_abs);
       } else {
-        if (masked) softmax_fixed<D, NB, true>(st, cur, pb, kbase, lim_abs, s0);
-        else softmax_fixed<D, NB, false>(st, cur, pb, kbase, lim_abs, s0);
+        if (masked) softmax_fixed<D, NB, true>(st, cur, pb, kbase, lim_abs);
+        else softmax_fixed<D, NB, false>(st, cur, pb, kbase, lim_abs);
       }
       const int nv0 = total - kbase, nv1 = total - kbase - 16;
       pv_block(ring[k % kStages], pb, nv0, nv1, nv1 < kPage);
@@ -386,7 +389,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
       block_barrier();
       qk_block<D, NB>(nxt, qf, ring[(k + 1) % kStages], koff, zero);
       u32x4 pb[NB];
-      softmax_fixed<D, NB, false>(st, cur, pb, k * 32, lim_abs, s0);
+      softmax_fixed<D, NB, false>(st, cur, pb, k * 32, lim_abs);
       pv_block(ring[k % kStages], pb, kPage, kPage, false);
     };
 #pragma unroll 1
@@ -426,14 +429,14 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
         }
         const bool masked = kbase + 32 > wave_lo;
         if (!FAST) {
-          if (masked) softmax_rescale<D, NB, true>(st, sc, pb, kbase, lim_abs, s0);
-          else softmax_rescale<D, NB, false>(st, sc, pb, kbase, lim_abs, s0);
+          if (masked) softmax_rescale<D, NB, true>(st, sc, pb, kbase, lim_abs);
+          else softmax_rescale<D, NB, false>(st, sc, pb, kbase, lim_abs);
         } else if (k == 0) {
-          if (masked) softmax_first<D, NB, true>(st, sc, pb, kbase, lim_abs, s0);
-          else softmax_first<D, NB, false>(st, sc, pb, kbase, lim_abs, s0);
+          if (masked) softmax_first<D, NB, true>(st, sc, pb, kbase, lim_abs);
+          else softmax_first<D, NB, false>(st, sc, pb, kbase, lim_abs);
         } else {
-          if (masked) softmax_fixed<D, NB, true>(st, sc, pb, kbase, lim_abs, s0);
-          else softmax_fixed<D, NB, false>(st, sc, pb, kbase, lim_abs, s0);
+          if (masked) softmax_fixed<D, NB, true>(st, sc, pb, kbase, lim_abs);
+          else softmax_fixed<D, NB, false>(st, sc, pb, kbase, lim_abs);
         }
         const int nv0 = total - kbase, nv1 = total - kbase - 16;
         __builtin_amdgcn_s_setprio(2);
@@ -497,16 +500,21 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
   __syncthreads();
   if (redo) run(std::integral_constant<bool, false>{});
 
+  // the output rows are recomputed here from a fresh copy of the lane id, so that
+  // no row address stays live (in registers or spilled) across the key walk
+  int ln = lane, Gq = G;
+  asm volatile("" : "+v"(ln), "+s"(Gq));
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     const float l = st.lsum[cb][0];
-    if (!rvalid[cb]) continue;
+    const int r = r0 + cb * 16 + (ln & 15);
+    if (r >= rows) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* o = a.out + (int64_t(c0 + tok[cb]) * a.num_q_heads + head[cb]) * D;
+    uint16_t* o = a.out + (int64_t(c0 + r / Gq) * a.num_q_heads + g * Gq + r % Gq) * D;
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
       const f32x4 v = st.acc[cb][i] * inv;
-      *reinterpret_cast<u32x2*>(o + 16 * i + 4 * (lane >> 4)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<u32x2*>(o + 16 * i + 4 * (ln >> 4)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
     }
   }
 }
