@@ -20,6 +20,9 @@ normal, no trained weights exist here):
 * qwen3_14b_long  — Qwen3-14B-shaped: 40 q / 8 KV heads, D=128, N=2, 8 sessions,
                     lengths truncated log-normal (sigma 1, mu 9.7869, truncated
                     to [4K, 128K], mean ~27K).
+* qwen3_8b_n8_private — qwen3_8b_n8's sessions and shared prefixes, plus a
+                    private suffix per decoder (its own generated tokens),
+                    lengths uniform in [0, 2048].
 
 1K = 1024 tokens.  bf16 values are float32 normal draws rounded to nearest even.
 """
@@ -48,6 +51,7 @@ class Workload:
     lens: list = field(default_factory=list)      # decode: tokens attended
     prefix: list = field(default_factory=list)    # extend: cached prefix
     new: list = field(default_factory=list)       # extend: new chunk sizes
+    priv: list = field(default_factory=list)      # decode: private suffix of decoder n of session b at b*N + n
 
     @property
     def group(self) -> int:
@@ -92,6 +96,13 @@ def make_workload(name: str, seed: int | None = None) -> Workload:
         r = _rng(s, 0)
         lens = [int(x) for x in r.integers(4096, 16384, size=64, endpoint=True)]
         return Workload(name, 64, 8, 32, 8, 128, 36, 1.0, s, "decode", lens=lens)
+    if name == "qwen3_8b_n8_private":
+        s = 2 if seed is None else seed
+        base = make_workload("qwen3_8b_n8", s)
+        r = _rng(s, 5)
+        priv = [int(x) for x in r.integers(0, 2048, size=base.batch * base.num_decoders, endpoint=True)]
+        return Workload(name, base.batch, base.num_decoders, base.num_q_heads, base.num_kv_heads,
+                        base.head_dim, 1, base.std, s, "decode", lens=base.lens, priv=priv)
     if name == "extend_8k_512":
         s = 3 if seed is None else seed
         return Workload(name, 16, 1, 32, 8, 128, 1, 1.0, s, "extend",
@@ -104,7 +115,7 @@ def make_workload(name: str, seed: int | None = None) -> Workload:
     raise KeyError(name)
 
 
-WORKLOADS = ("tiny", "llama8b_n4", "qwen3_8b_n8", "extend_8k_512", "qwen3_14b_long")
+WORKLOADS = ("tiny", "llama8b_n4", "qwen3_8b_n8", "extend_8k_512", "qwen3_14b_long", "qwen3_8b_n8_private")
 
 
 # ---------------------------------------------------------------------------
@@ -130,6 +141,20 @@ def build_block_table(lengths, seed: int, spare_frac: float = 0.02, min_spare: i
         bt[b, :n] = perm[pos:pos + n]
         pos += n
     return bt, num_pages
+
+
+def build_private_tables(lens, priv_lens, seed: int, spare_frac: float = 0.02):
+    """Pages for B shared prefixes and B*N private suffixes from one seeded pool.
+
+    Returns (block_table int32 [B, S], private block table int32 [B*N, S_p],
+    num_pages): row b*N + n of the private table lists the pages of decoder n's
+    own tokens in session b.  Both tables draw from one permutation of the pool.
+    """
+    B = len(lens)
+    allbt, num_pages = build_block_table(list(lens) + list(priv_lens), seed, spare_frac)
+    s1 = max(max((int(L) + PAGE - 1) // PAGE for L in lens), 1)
+    s2 = max(max((int(U) + PAGE - 1) // PAGE for U in priv_lens), 1)
+    return allbt[:B, :s1].copy(), allbt[B:, :s2].copy(), num_pages
 
 
 # ---------------------------------------------------------------------------

@@ -196,6 +196,35 @@ def decode(pool: np.ndarray, shape: PoolShape, layer: int, q_bits: np.ndarray,
     return out
 
 
+def decode_private(pool: np.ndarray, shape: PoolShape, layer: int, q_bits: np.ndarray,
+                   block_table: np.ndarray, seq_lens, priv_table: np.ndarray, priv_lens, scale: float,
+                   sessions=None) -> np.ndarray:
+    """Decode attention over a shared prefix plus each decoder's private suffix.
+
+    PrefillShare, section 3.3: every decoder starts from the base model's cache
+    C_base and then extends it with its own generated tokens (the decoder-private
+    Delta C_t); the memory model of Eq. 9 keeps the shared prefix once and only
+    the private parts per decoder.  Decoder n of session b therefore attends the
+    sequence  shared prefix (seq_lens[b] tokens through block_table[b])  followed
+    by  its private suffix (priv_lens[b*N + n] tokens through priv_table[b*N + n]).
+    Returns float64 [B, N, H_q, D]; sessions not in `sessions` stay zero.
+    """
+    B, N, Hq, D = q_bits.shape
+    G = Hq // shape.num_kv_heads
+    q = bf16_to_f64(q_bits)
+    out = np.zeros((B, N, Hq, D), dtype=np.float64)
+    for b in (range(B) if sessions is None else sessions):
+        Ks, Vs = gather(pool, shape, layer, block_table[b], int(seq_lens[b]))
+        for n in range(N):
+            Kp, Vp = gather(pool, shape, layer, priv_table[b * N + n], int(priv_lens[b * N + n]))
+            K = np.concatenate([Ks, Kp])
+            V = np.concatenate([Vs, Vp])
+            for h in range(Hq):
+                g = h // G
+                out[b, n, h] = attend(q[b, n, h], K[:, g], V[:, g], scale)
+    return out
+
+
 def extend(pool: np.ndarray, shape: PoolShape, layer: int, q_bits: np.ndarray, k_new: np.ndarray,
            v_new: np.ndarray, cu_new, block_table: np.ndarray, seq_lens, scale: float,
            sessions=None, rows=None):

@@ -298,6 +298,83 @@ def test_page_permutation_invariance():
 
 
 # ---------------------------------------------------------------------------
+# Shared prefix + decoder-private suffixes (PrefillShare, section 3.3: each
+# decoder extends C_base with its own Delta C_t; Eq. 9 stores the prefix once)
+# ---------------------------------------------------------------------------
+def build_private_pool(lens, priv, Hkv, D, seed):
+    """Pool with B shared prefixes (table bt) and B*N private suffixes (table pbt)."""
+    bt, pbt, num_pages = wlmod.build_private_tables(lens, priv, seed)
+    shape = oracle.PoolShape(1, num_pages, Hkv, D)
+    rng = RNG(seed + 100)
+    K = [bits(rng, (L, Hkv, D)) for L in lens]
+    V = [bits(rng, (L, Hkv, D)) for L in lens]
+    Kp = [bits(rng, (U, Hkv, D)) for U in priv]
+    Vp = [bits(rng, (U, Hkv, D)) for U in priv]
+    pool = poison_pool(shape)
+    kk, cu = wlmod.concat_rows(K)
+    vv, _ = wlmod.concat_rows(V)
+    pool = oracle.append(pool, shape, 0, kk, vv, cu, bt, np.zeros(len(lens), np.int32))
+    kk, cu = wlmod.concat_rows(Kp)
+    vv, _ = wlmod.concat_rows(Vp)
+    pool = oracle.append(pool, shape, 0, kk, vv, cu, pbt, np.zeros(len(priv), np.int32))
+    return shape, pool, bt, pbt, K, V, Kp, Vp
+
+
+def test_private_decode_matches_brute_force_over_prefix_then_suffix():
+    lens, priv, N, Hkv, G, D = [21, 0], [3, 16, 0, 9], 2, 1, 2, 16
+    shape, pool, bt, pbt, K, V, Kp, Vp = build_private_pool(lens, priv, Hkv, D, seed=41)
+    q = bits(RNG(41), (2, N, Hkv * G, D))
+    got = oracle.decode_private(pool, shape, 0, q, bt, lens, pbt, priv, 0.25)
+    qf = oracle.bf16_to_f64(q)
+    for b in range(2):
+        for n in range(N):
+            Kf = oracle.bf16_to_f64(np.concatenate([K[b], Kp[b * N + n]])).tolist()
+            Vf = oracle.bf16_to_f64(np.concatenate([V[b], Vp[b * N + n]])).tolist()
+            for h in range(Hkv * G):
+                g = h // G
+                want = brute_attention(qf[b, n, h].tolist(), [r[g] for r in Kf], [r[g] for r in Vf], 0.25)
+                assert np.max(np.abs(got[b, n, h] - want)) < 1e-12
+
+
+def test_private_decode_matches_torch_sdpa():
+    lens, N, Hkv, G, D = [37, 130], 3, 2, 4, 64
+    priv = [40, 0, 17, 1, 64, 33]
+    shape, pool, bt, pbt, K, V, Kp, Vp = build_private_pool(lens, priv, Hkv, D, seed=43)
+    q = bits(RNG(43), (2, N, Hkv * G, D))
+    scale = 1.0 / math.sqrt(D)
+    got = oracle.decode_private(pool, shape, 0, q, bt, lens, pbt, priv, scale)
+    qf = oracle.bf16_to_f64(q)
+    for b in range(2):
+        for n in range(N):
+            Kr = np.repeat(oracle.bf16_to_f64(np.concatenate([K[b], Kp[b * N + n]])), G, axis=1)
+            Vr = np.repeat(oracle.bf16_to_f64(np.concatenate([V[b], Vp[b * N + n]])), G, axis=1)
+            want = sdpa(qf[b, n][None], Kr, Vr, scale)[0]
+            assert np.max(np.abs(got[b, n] - want)) < 1e-12
+
+
+def test_private_decode_without_suffixes_is_shared_decode():
+    lens, N = [50, 7], 2
+    shape, pool, bt, pbt, _, _, _, _ = build_private_pool(lens, [0] * 4, 2, 64, seed=44)
+    q = bits(RNG(44), (2, N, 4, 64))
+    got = oracle.decode_private(pool, shape, 0, q, bt, lens, pbt, [0] * 4, 0.125)
+    assert np.array_equal(got, oracle.decode(pool, shape, 0, q, bt, lens, 0.125))
+
+
+def test_private_suffix_reaches_only_its_decoder():
+    """Changing decoder 1's private K/V changes decoder 1 only; decoder 0 is bit-identical."""
+    lens, priv, N = [30], [12, 20], 2
+    shape, pool, bt, pbt, K, V, Kp, Vp = build_private_pool(lens, priv, 2, 64, seed=45)
+    q = bits(RNG(45), (1, N, 4, 64))
+    base = oracle.decode_private(pool, shape, 0, q, bt, lens, pbt, priv, 0.125)
+    kk, cu = wlmod.concat_rows([np.zeros((0, 2, 64), np.uint16), bits(RNG(46), (20, 2, 64))])
+    vv, _ = wlmod.concat_rows([np.zeros((0, 2, 64), np.uint16), bits(RNG(47), (20, 2, 64))])
+    pool2 = oracle.append(pool, shape, 0, kk, vv, cu, pbt, np.zeros(2, np.int32))
+    other = oracle.decode_private(pool2, shape, 0, q, bt, lens, pbt, priv, 0.125)
+    assert np.array_equal(other[:, 0], base[:, 0])
+    assert not np.allclose(other[:, 1], base[:, 1])
+
+
+# ---------------------------------------------------------------------------
 # Extend
 # ---------------------------------------------------------------------------
 def _extend_case(prefix, new, Hkv, G, D, seed):

@@ -54,6 +54,12 @@ MUTANTS = {
     "v_layout_slab": ("slab = d // 16 ", "slab = d // 32 "),
     "decode_prefix_off_by_one": ("K, V = gather(pool, shape, layer, block_table[b], L)",
                                  "K, V = gather(pool, shape, layer, block_table[b], max(L - 1, 0))"),
+    "private_row_order": ("priv_table[b * N + n], int(priv_lens[b * N + n])",
+                          "priv_table[n * B + b], int(priv_lens[n * B + b])"),
+    "private_suffix_dropped": ("K = np.concatenate([Ks, Kp])\n            V = np.concatenate([Vs, Vp])",
+                               "K = Ks\n            V = Vs"),
+    "private_prefix_dropped": ("K = np.concatenate([Ks, Kp])\n            V = np.concatenate([Vs, Vp])",
+                               "K = Kp\n            V = Vp"),
 }
 
 PIN_CHECKS = [
@@ -68,6 +74,8 @@ PIN_CHECKS = [
     pins.test_closed_form_single_token_returns_v,
     pins.test_closed_form_zero_query_gives_mean_of_v,
     lambda: pins.test_extend_equals_causal_sdpa_over_whole_sequence([40, 0, 16], [9, 20, 1]),
+    pins.test_private_decode_matches_brute_force_over_prefix_then_suffix,
+    pins.test_private_suffix_reaches_only_its_decoder,
 ]
 
 
@@ -83,7 +91,7 @@ def _mutant_module(old, new):
 def test_pins_catch_mutant(name, monkeypatch):
     mod = _mutant_module(*MUTANTS[name])
     for attr in ("bf16_to_f64", "k_offset", "v_offset", "tile_start", "append", "gather", "attend",
-                 "decode", "extend", "decode_from_logical", "extend_from_logical", "PoolShape",
+                 "decode", "decode_private", "extend", "decode_from_logical", "extend_from_logical", "PoolShape",
                  "tile_elems", "pool_elems"):
         monkeypatch.setattr(oracle, attr, getattr(mod, attr))
     failed = []
