@@ -40,6 +40,8 @@ _SIGNATURES = {
     "shared_kv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "shared_kv_decode": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                         _f, _vp, _sz, _vp, _vp]),
+    "shared_kv_decode_private": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32,
+                                                _i32, _i32, _i32, _i32, _f, _vp, _sz, _vp, _vp]),
     "partial_prefill_extend": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                               _i32, _i32, _i32, _i32, _i32, _f, _vp, _vp]),
     "kvs_last_error": (ctypes.c_char_p, []),
@@ -157,7 +159,7 @@ def decode_workspace_bytes(batch, num_decoders, num_q_heads, num_kv_heads, head_
 
 def decode(pool: Pool, layer, q, out, block_table, seq_lens, max_seq_len, scale, workspace,
            dev_status=None, stream=None):
-    """q, out: bf16 [B, N, H_q, D]; workspace: a zero-filled uint8 device tensor."""
+    """q, out: bf16 [B, N, H_q, D]; workspace: a uint8 device tensor of decode_workspace_bytes."""
     torch = _torch()
     B, N, Hq, D = q.shape
     if D != pool.head_dim or tuple(out.shape) != tuple(q.shape):
@@ -166,6 +168,26 @@ def decode(pool: Pool, layer, q, out, block_table, seq_lens, max_seq_len, scale,
         pool.struct, layer, _ptr(q, "q", torch.bfloat16), _ptr(out, "out", torch.bfloat16),
         _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
         _ptr(seq_lens, "seq_lens", torch.int32, B), B, N, Hq, max_seq_len, float(scale),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True), _stream(stream)))
+
+
+def decode_private(pool: Pool, layer, q, out, block_table, seq_lens, priv_block_table, priv_lens,
+                   max_seq_len, max_priv_len, scale, workspace, dev_status=None, stream=None):
+    """Shared prefix + per-decoder private suffix.  q, out: bf16 [B, N, H_q, D];
+    priv_block_table: int32 [B*N, S_p]; priv_lens: int32 [B*N]; workspace as for decode."""
+    torch = _torch()
+    B, N, Hq, D = q.shape
+    if D != pool.head_dim or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q/out shape does not match the pool")
+    if priv_block_table.dim() != 2 or priv_block_table.shape[0] != B * N:
+        raise ValueError("priv_block_table must be [batch*num_decoders, stride]")
+    _check(load().shared_kv_decode_private(
+        pool.struct, layer, _ptr(q, "q", torch.bfloat16), _ptr(out, "out", torch.bfloat16),
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
+        _ptr(seq_lens, "seq_lens", torch.int32, B),
+        _ptr(priv_block_table, "priv_block_table", torch.int32), priv_block_table.shape[1],
+        _ptr(priv_lens, "priv_lens", torch.int32, B * N), B, N, Hq, max_seq_len, max_priv_len, float(scale),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True), _stream(stream)))
 

@@ -15,6 +15,14 @@
 // runs the page step of attn_core.h, and at every unit boundary either writes
 // the final output (unit wholly inside its share) or its partial softmax state
 // (m, l, acc) for decode_combine_kernel (unit crossing a share boundary).
+//
+// Decoder-private suffixes (PrefillShare, section 3.3: each decoder extends
+// C_base with its own generated tokens; Eq. 9 keeps the prefix once and the
+// suffixes per decoder): a unit's tile list is the session's shared pages
+// followed by every decoder's private pages, decoder by decoder.  A private page
+// is read once, by the wave that holds all of the KV head's rows, with the rows
+// of the other decoders masked out, so the shared prefix still streams once for
+// all N decoders and each suffix once for its own.
 #include "attn_core.h"
 #include "kvs_internal.h"
 
@@ -51,9 +59,40 @@ __device__ __forceinline__ void wait_ring(int pages_after) {
 __device__ __forceinline__ int clamp_len(int L, int max_len) { return L < 0 ? 0 : (L > max_len ? max_len : L); }
 
 // Position in the tile list: unit (gr = KV head * rowgroups + row group, session b), page.
+// With private suffixes, pages nsh.. of a unit are private: page pp of decoder pn
+// (pnpg pages, plen tokens).
 struct Walker {
   int gr, b, page, npg;
+  int nsh, pn, pp, pnpg, plen;
 };
+
+__device__ __forceinline__ int shared_pages(const DecodeArgs& a, int b) {
+  return (clamp_len(load_uniform(a.seq_lens + b), a.max_seq_len) + kPage - 1) / kPage;
+}
+
+// Private tokens of decoder n of session b.
+__device__ __forceinline__ int priv_len(const DecodeArgs& a, int b, int n) {
+  return clamp_len(load_uniform(a.plens + int64_t(b) * a.num_decoders + n), a.max_priv_len);
+}
+
+// First decoder at or after n with private pages (the caller knows one exists).
+__device__ __forceinline__ void first_priv(const DecodeArgs& a, Walker& w, int n) {
+  int U = priv_len(a, w.b, n);
+  while (U == 0 && n + 1 < a.num_decoders) U = priv_len(a, w.b, ++n);
+  w.pn = n;
+  w.pp = 0;
+  w.plen = U;
+  w.pnpg = (U + kPage - 1) / kPage;
+}
+
+// Private sub-position after w.page moved to the next page of the same unit, or
+// to page 0 of a new unit (w.nsh already set).
+template <bool PRIV>
+__device__ __forceinline__ void enter_page(const DecodeArgs& a, Walker& w) {
+  if (!PRIV || w.page < w.nsh) return;
+  if (w.page == w.nsh) first_priv(a, w, 0);
+  else if (++w.pp == w.pnpg) first_priv(a, w, w.pn + 1);
+}
 
 __device__ __forceinline__ int read_cum(const int* cum, int i) {
   return __builtin_amdgcn_readfirstlane(cum[i]);
@@ -65,8 +104,9 @@ __device__ __forceinline__ int next_nonempty(const int* cum, int b, int B) {
   return b;
 }
 
-__device__ __forceinline__ Walker seek(const int* cum, int B, int Ptot, int64_t tau) {
-  Walker w;
+template <bool PRIV>
+__device__ __forceinline__ Walker seek(const DecodeArgs& a, const int* cum, int B, int Ptot, int64_t tau) {
+  Walker w{};
   w.gr = int(tau / Ptot);
   const int r = int(tau % Ptot);
   int lo = 0, hi = B;  // largest b with cum[b] <= r, among b < B
@@ -79,11 +119,32 @@ __device__ __forceinline__ Walker seek(const int* cum, int B, int Ptot, int64_t 
   w.b = lo;
   w.page = r - read_cum(cum, lo);
   w.npg = read_cum(cum, lo + 1) - read_cum(cum, lo);
+  if (PRIV && lo < B) {
+    w.nsh = shared_pages(a, lo);
+    if (w.page >= w.nsh) {  // find the decoder and page of private position page - nsh
+      int q = w.page - w.nsh, n = 0;
+      for (;; ++n) {
+        const int U = priv_len(a, lo, n), np = (U + kPage - 1) / kPage;
+        if (q < np || n + 1 == a.num_decoders) {
+          w.pn = n;
+          w.pp = q;
+          w.plen = U;
+          w.pnpg = np;
+          break;
+        }
+        q -= np;
+      }
+    }
+  }
   return w;
 }
 
-__device__ __forceinline__ void advance(Walker& w, const int* cum, int B) {
-  if (++w.page < w.npg) return;
+template <bool PRIV>
+__device__ __forceinline__ void advance(const DecodeArgs& a, Walker& w, const int* cum, int B) {
+  if (++w.page < w.npg) {
+    enter_page<PRIV>(a, w);
+    return;
+  }
   w.page = 0;
   int b = next_nonempty(cum, w.b + 1, B);
   if (b >= B) {
@@ -92,6 +153,10 @@ __device__ __forceinline__ void advance(Walker& w, const int* cum, int B) {
   }
   w.b = b;
   w.npg = b < B ? read_cum(cum, b + 1) - read_cum(cum, b) : 0;
+  if (PRIV && b < B) {
+    w.nsh = shared_pages(a, b);
+    enter_page<PRIV>(a, w);
+  }
 }
 
 __device__ __forceinline__ int64_t share_start(int k, int64_t T, int W) { return int64_t(k) * T / W; }
@@ -153,7 +218,18 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, const RowStat
   }
 }
 
-template <int D, int NB, int S>
+// Private pages of all decoders of session b (per-thread loads; flags bad lengths).
+__device__ __forceinline__ int priv_pages(const DecodeArgs& a, int b) {
+  int pages = 0;
+  for (int n = 0; n < a.num_decoders; ++n) {
+    const int U = a.plens[int64_t(b) * a.num_decoders + n];
+    if ((U < 0 || U > a.max_priv_len) && blockIdx.x == 0) flag_error(a.dev_status, KVS_DEV_BAD_LEN_BIT);
+    pages += (clamp_len(U, a.max_priv_len) + kPage - 1) / kPage;
+  }
+  return pages;
+}
+
+template <int D, int NB, int S, bool PRIV>
 __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
   constexpr int SLABS = D / 16;  // 1 KiB slabs per (page, head) tile: K slabs then V slabs
   __shared__ u32x4 ring[kWaves][S][SLABS * 64];
@@ -173,6 +249,7 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       const int L = a.seq_lens[b];
       if ((L < 0 || L > a.max_seq_len) && blockIdx.x == 0) flag_error(a.dev_status, KVS_DEV_BAD_LEN_BIT);
       local += (clamp_len(L, a.max_seq_len) + kPage - 1) / kPage;
+      if (PRIV) local += priv_pages(a, b);
     }
   }
   part_s[tid] = local;
@@ -199,6 +276,7 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       if (b < B) {
         cum_s[b] = run;
         run += (clamp_len(a.seq_lens[b], a.max_seq_len) + kPage - 1) / kPage;
+        if (PRIV) run += priv_pages(a, b);
       }
     }
     if (tid == 255) cum_s[B] = run;
@@ -219,11 +297,13 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
   const int num_pages = a.pool.num_pages;
   uint32_t bad = 0;  // ring slots whose page id was out of range
 
-  Walker iw = seek(cum_s, B, Ptot, tau0);
+  Walker iw = seek<PRIV>(a, cum_s, B, Ptot, tau0);
   Walker cw = iw;
   auto issue = [&](int slot) {
     const int g = iw.gr / RGs;
-    int pid = load_uniform(a.bt + int64_t(iw.b) * a.bt_stride + iw.page);
+    int pid = (PRIV && iw.page >= iw.nsh)
+                  ? load_uniform(a.pbt + (int64_t(iw.b) * a.num_decoders + iw.pn) * a.pbt_stride + iw.pp)
+                  : load_uniform(a.bt + int64_t(iw.b) * a.bt_stride + iw.page);
     const bool ok = pid >= 0 && pid < num_pages;
     bad = ok ? (bad & ~(1u << slot)) : (bad | (1u << slot));
     if (!ok) {
@@ -237,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + s * 64 + lane),
                                        (__attribute__((address_space(3))) void*)(&ring[wave][slot][s * 64]),
                                        16, 0, 0);
-    advance(iw, cum_s, B);
+    advance<PRIV>(a, iw, cum_s, B);
   };
 
   QFrag<D, NB> qf;
@@ -263,15 +343,27 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       for (int i = 0; i < D / 32; ++i) kf[i] = ring[wave][slot][k_run(i, lane >> 4, lane & 15)];
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) vf[i] = v2[2 * v_run(D, i, lane >> 5, lane & 15) + ((lane >> 4) & 1)];
-      const int L = clamp_len(load_uniform(a.seq_lens + cw.b), a.max_seq_len);
-      const int nvalid = min(kPage, L - cw.page * kPage);
       int lim[NB];
+      if (PRIV && cw.page >= cw.nsh) {
+        // a private page of decoder pn: only its rows (r / G == pn) see it
+        const int nvalid = min(kPage, cw.plen - cw.pp * kPage);
+        const int G = a.num_q_heads / Hkv;
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb) lim[cb] = nvalid;
-      attend_page<D, NB>(st, qf, kf, vf, a.scale_log2, nvalid < kPage, lim, nvalid, lane);
+        for (int cb = 0; cb < NB; ++cb) {
+          const int r = (cw.gr % RGs) * 16 * NB + cb * 16 + (lane & 15);
+          lim[cb] = (r / G == cw.pn) ? nvalid : 0;
+        }
+        attend_page<D, NB>(st, qf, kf, vf, a.scale_log2, true, lim, nvalid, lane);
+      } else {
+        const int L = clamp_len(load_uniform(a.seq_lens + cw.b), a.max_seq_len);
+        const int nvalid = min(kPage, L - cw.page * kPage);
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) lim[cb] = nvalid;
+        attend_page<D, NB>(st, qf, kf, vf, a.scale_log2, nvalid < kPage, lim, nvalid, lane);
+      }
     }
     const int cur_gr = cw.gr, cur_b = cw.b;
-    advance(cw, cum_s, B);
+    advance<PRIV>(a, cw, cum_s, B);
     const bool last = (j == n - 1);
     if (last || cw.gr != cur_gr || cw.b != cur_b) {
       // unit (cur_gr, cur_b) ends here for this wave
@@ -324,6 +416,8 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
   // share of tile t: floor(((t + 1) W - 1) / T)
   const int k0 = int(((s_u + 1) * W - 1) / T), k1 = int((e_u * W - 1) / T);
   if (k0 == k1) return;  // written directly by its wave
+  // shares between k0 and k1 that hold no tile (T < W) wrote nothing: skip them
+  auto empty = [&](int k) { return share_start(k, T, W) == share_start(k + 1, T, W); };
   const float* __restrict__ ml = a.ws_ml;
   const float* __restrict__ accp = a.ws_acc;
   for (int e = threadIdx.x; e < RG * (D / 4); e += blockDim.x) {
@@ -333,11 +427,13 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
     // slot of share k: its "started before" slot (0) except the first share (1)
     float M = -INFINITY;
 #pragma unroll 8
-    for (int k = k0; k <= k1; ++k) M = fmaxf(M, ml[(int64_t(k * 2 + (k == k0)) * RG + rl) * 2]);
+    for (int k = k0; k <= k1; ++k)
+      if (!empty(k)) M = fmaxf(M, ml[(int64_t(k * 2 + (k == k0)) * RG + rl) * 2]);
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
 #pragma unroll 4
     for (int k = k0; k <= k1; ++k) {
+      if (empty(k)) continue;
       const int64_t slot = k * 2 + (k == k0);
       const float ms = ml[(slot * RG + rl) * 2];
       const float ls = ml[(slot * RG + rl) * 2 + 1];
@@ -356,7 +452,10 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
 template <int D, int NB>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   constexpr int S = D == 128 ? 4 : 8;  // 32 KiB of ring per wave
-  hipLaunchKernelGGL((decode_stream_kernel<D, NB, S>), dim3(a.plan.blocks), dim3(256), 0, stream, a);
+  if (a.pbt)
+    hipLaunchKernelGGL((decode_stream_kernel<D, NB, S, true>), dim3(a.plan.blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_stream_kernel<D, NB, S, false>), dim3(a.plan.blocks), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units = a.pool.num_kv_heads * a.plan.rowgroups * a.batch;

@@ -22,8 +22,6 @@
 #include "kvs_device.h"
 #include "kvs_internal.h"
 
-#include <stdlib.h>
-
 #include <type_traits>
 
 namespace kvs {
@@ -536,17 +534,10 @@ hipError_t launch_extend_t(const ExtendArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream) {
-  // D=128: 8 waves x 32 rows (two waves per SIMD hide each other's softmax and
-  // LDS latency); D=64: 4 waves x 64 rows (a 4 KiB page tile is one 256-thread load)
-  if (a.pool.head_dim == 128) {
-    const char* v = getenv("KVS_EXTEND_VARIANT");  // tuning only
-    if (v && v[0] == '1') return launch_extend_t<128, 2, 8, 6, 4, 1, true>(a, stream);
-    if (v && v[0] == '2') return launch_extend_t<128, 2, 4, 5, 3, 2, true>(a, stream);
-    if (v && v[0] == '3') return launch_extend_t<128, 2, 4, 4, 2, 2, true>(a, stream);
-    if (v && v[0] == '4') return launch_extend_t<128, 2, 4, 4, 2, 2, false>(a, stream);
-    // three 4-wave workgroups per CU (three waves per SIMD), one block at a time
-    return launch_extend_t<128, 2, 4, 3, 1, 3, false>(a, stream);
-  }
+  // D=128: three 4-wave workgroups per CU (three waves per SIMD), one block at a
+  // time; D=64: 4 waves x 64 rows, the next block's QK^T ahead of this block's
+  // softmax (a 4 KiB page tile is one 256-thread load)
+  if (a.pool.head_dim == 128) return launch_extend_t<128, 2, 4, 3, 1, 3, false>(a, stream);
   return launch_extend_t<64, 4, 4, 6, 4, 1, true>(a, stream);
 }
 

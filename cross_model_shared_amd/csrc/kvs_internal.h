@@ -54,6 +54,13 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   int batch, num_decoders, num_q_heads, max_seq_len;
   float scale_log2;
+  // decoder-private suffixes (all null / 0 for a shared-only call): row b*N + n
+  // of pbt lists the pages of decoder n's own tokens in session b, plens[b*N + n]
+  // their count
+  const int32_t* pbt;
+  int pbt_stride;
+  const int32_t* plens;
+  int max_priv_len;
   int* ws_cum;    // [batch+1] page prefix sum, written by the decode kernel
   float* ws_ml;   // [4*blocks*2][rg_rows][2] partial (m, l)
   float* ws_acc;  // [4*blocks*2][rg_rows][D] partial acc

@@ -128,38 +128,80 @@ size_t shared_kv_decode_workspace_bytes(int32_t batch, int32_t num_decoders, int
   return kvs::plan_decode(batch, num_decoders, num_q_heads, num_kv_heads, head_dim, max_seq_len).bytes;
 }
 
+}  // extern "C"
+
+namespace {
+
+int decode_common(const char* name, const kvs_pool* pool, int32_t layer, const void* q, void* out,
+                  const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                  const int32_t* pbt, int32_t pbt_stride, const int32_t* plens, int32_t batch,
+                  int32_t num_decoders, int32_t num_q_heads, int32_t max_seq_len, int32_t max_priv_len,
+                  float scale, void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                  hipStream_t stream) {
+  int s = check_pool(pool, layer);
+  if (s) return s;
+  if (!q || !out || !block_table || !seq_lens) return fail(KVS_EINVAL, "%s: a required pointer is NULL", name);
+  if ((s = check_table(batch, bt_stride, max_seq_len))) return s;
+  if (num_decoders <= 0 || num_q_heads <= 0)
+    return fail(KVS_EINVAL, "%s: num_decoders %d and num_q_heads %d must be positive", name, num_decoders,
+                num_q_heads);
+  if (num_q_heads % pool->num_kv_heads)
+    return fail(KVS_EUNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                pool->num_kv_heads);
+  if (!(scale > 0.f) || scale != scale) return fail(KVS_EINVAL, "%s: scale must be a positive number", name);
+  if (batch > kvs::kDecodeMaxBatch)
+    return fail(KVS_EUNSUPPORTED, "%s: batch %d above %d", name, batch, kvs::kDecodeMaxBatch);
+  kvs::DecodePlan plan = kvs::plan_decode(batch, num_decoders, num_q_heads, pool->num_kv_heads,
+                                          pool->head_dim, max_seq_len);
+  if (pbt) {
+    if (pbt_stride <= 0) return fail(KVS_EINVAL, "%s: priv_bt_stride %d must be positive", name, pbt_stride);
+    if (max_priv_len < 0) return fail(KVS_EINVAL, "%s: max_priv_len %d is negative", name, max_priv_len);
+    if (int64_t(max_priv_len) > int64_t(pbt_stride) * 16)
+      return fail(KVS_ERANGE, "%s: max_priv_len %d exceeds private block-table capacity %lld", name,
+                  max_priv_len, (long long)pbt_stride * 16);
+    if (plan.rowgroups != 1)
+      return fail(KVS_EUNSUPPORTED, "%s: %d query rows per KV head (num_decoders * group) above 64", name,
+                  plan.rows);
+  }
+  if (!workspace || workspace_bytes < plan.bytes)
+    return fail(KVS_EWORKSPACE, "%s: workspace %zu bytes < required %zu", name,
+                workspace ? workspace_bytes : size_t(0), plan.bytes);
+  char* ws = static_cast<char*>(workspace);
+  kvs::DecodeArgs a{view(pool), layer, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+                    block_table, bt_stride, seq_lens, batch, num_decoders, num_q_heads, max_seq_len,
+                    scale * 1.4426950408889634f, pbt, pbt_stride, plens, max_priv_len,
+                    reinterpret_cast<int*>(ws + plan.cum_offset),
+                    reinterpret_cast<float*>(ws + plan.ml_offset),
+                    reinterpret_cast<float*>(ws + plan.acc_offset), plan, dev_status};
+  return launched(kvs::launch_decode(a, stream), name);
+}
+
+}  // namespace
+
+extern "C" {
+
 int shared_kv_decode(const kvs_pool* pool, int32_t layer, const void* q, void* out,
                      const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
                      int32_t batch, int32_t num_decoders, int32_t num_q_heads, int32_t max_seq_len,
                      float scale, void* workspace, size_t workspace_bytes, int32_t* dev_status,
                      hipStream_t stream) {
-  int s = check_pool(pool, layer);
-  if (s) return s;
-  if (!q || !out || !block_table || !seq_lens)
-    return fail(KVS_EINVAL, "shared_kv_decode: a required pointer is NULL");
-  if ((s = check_table(batch, bt_stride, max_seq_len))) return s;
-  if (num_decoders <= 0 || num_q_heads <= 0)
-    return fail(KVS_EINVAL, "shared_kv_decode: num_decoders %d and num_q_heads %d must be positive",
-                num_decoders, num_q_heads);
-  if (num_q_heads % pool->num_kv_heads)
-    return fail(KVS_EUNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
-                pool->num_kv_heads);
-  if (!(scale > 0.f) || scale != scale)
-    return fail(KVS_EINVAL, "shared_kv_decode: scale must be a positive number");
-  if (batch > kvs::kDecodeMaxBatch)
-    return fail(KVS_EUNSUPPORTED, "shared_kv_decode: batch %d above %d", batch, kvs::kDecodeMaxBatch);
-  kvs::DecodePlan plan = kvs::plan_decode(batch, num_decoders, num_q_heads, pool->num_kv_heads,
-                                          pool->head_dim, max_seq_len);
-  if (!workspace || workspace_bytes < plan.bytes)
-    return fail(KVS_EWORKSPACE, "shared_kv_decode: workspace %zu bytes < required %zu",
-                workspace ? workspace_bytes : size_t(0), plan.bytes);
-  char* ws = static_cast<char*>(workspace);
-  kvs::DecodeArgs a{view(pool), layer, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
-                    block_table, bt_stride, seq_lens, batch, num_decoders, num_q_heads, max_seq_len,
-                    scale * 1.4426950408889634f, reinterpret_cast<int*>(ws + plan.cum_offset),
-                    reinterpret_cast<float*>(ws + plan.ml_offset),
-                    reinterpret_cast<float*>(ws + plan.acc_offset), plan, dev_status};
-  return launched(kvs::launch_decode(a, stream), "shared_kv_decode");
+  return decode_common("shared_kv_decode", pool, layer, q, out, block_table, bt_stride, seq_lens, nullptr, 0,
+                       nullptr, batch, num_decoders, num_q_heads, max_seq_len, 0, scale, workspace,
+                       workspace_bytes, dev_status, stream);
+}
+
+int shared_kv_decode_private(const kvs_pool* pool, int32_t layer, const void* q, void* out,
+                             const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                             const int32_t* priv_block_table, int32_t priv_bt_stride,
+                             const int32_t* priv_lens, int32_t batch, int32_t num_decoders,
+                             int32_t num_q_heads, int32_t max_seq_len, int32_t max_priv_len,
+                             float scale, void* workspace, size_t workspace_bytes,
+                             int32_t* dev_status, hipStream_t stream) {
+  if (!priv_block_table || !priv_lens)
+    return fail(KVS_EINVAL, "shared_kv_decode_private: a required pointer is NULL");
+  return decode_common("shared_kv_decode_private", pool, layer, q, out, block_table, bt_stride, seq_lens,
+                       priv_block_table, priv_bt_stride, priv_lens, batch, num_decoders, num_q_heads,
+                       max_seq_len, max_priv_len, scale, workspace, workspace_bytes, dev_status, stream);
 }
 
 int partial_prefill_extend(const kvs_pool* pool, int32_t layer, const void* q, const void* k_new,

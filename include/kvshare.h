@@ -15,6 +15,7 @@
  * Three operations:
  *   kv_pool_append         write new K/V rows into pages        (the cache "store")
  *   shared_kv_decode       N decoders x G GQA heads, one KV read (decode attention)
+ *   shared_kv_decode_private  the same over a shared prefix + per-decoder private suffixes
  *   partial_prefill_extend append a chunk, then causal attention of the chunk
  *                          over cached prefix + chunk           (partial prefill)
  *
@@ -158,16 +159,48 @@ size_t shared_kv_decode_workspace_bytes(int32_t batch, int32_t num_decoders, int
  *  max_seq_len   host bound on seq_lens[b]; sizes the launch.
  *  scale         softmax scale (1/sqrt(head_dim) for the usual attention).
  *  workspace     device buffer of >= shared_kv_decode_workspace_bytes(...)
- *                bytes, ZERO-FILLED before its first use.  Every call leaves its
- *                counters at zero again, so a workspace may be reused by later
- *                calls on the same stream; calls that overlap in time must use
- *                different workspaces.
+ *                bytes.  Its contents on entry are ignored (every byte the call
+ *                reads it wrote earlier in the same call), so a workspace may be
+ *                reused by later calls on the same stream; calls that overlap in
+ *                time must use different workspaces.
  */
 int shared_kv_decode(const kvs_pool* pool, int32_t layer, const void* q, void* out,
                      const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
                      int32_t batch, int32_t num_decoders, int32_t num_q_heads,
                      int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
                      int32_t* dev_status, hipStream_t stream);
+
+/*
+ * shared_kv_decode_private — one decode step of N decoders over one shared
+ * prefix plus each decoder's own private suffix.
+ *
+ * PrefillShare, section 3.3: decoding starts from the base model's cache C_base
+ * and every step of a decoder adds its own KV (Delta C_t) to what that decoder
+ * attends; the memory model of Eq. 9 stores the shared prefix once and only the
+ * private parts per decoder.  Decoder n of session b attends its shared prefix
+ * (seq_lens[b] tokens through block_table row b) followed by its private suffix
+ * (priv_lens[b*N + n] tokens through priv_block_table row b*N + n):
+ *     out[b,n,h,:] = sum_t softmax_t(scale * q[b,n,h,:] . K_g[t,:]) V_g[t,:]
+ * over t in  prefix(b) ++ suffix(b, n);  out = 0 when both are empty.
+ * Each shared page is read once for all N decoders, each private page once.
+ * With every priv_lens entry 0 the result equals shared_kv_decode's.
+ *
+ *  priv_block_table  int32 [batch*num_decoders][priv_bt_stride], pages of the
+ *                    private suffixes in the same pool (written with
+ *                    kv_pool_append using this table, row b*N + n as a session).
+ *  priv_lens         int32 [batch*num_decoders], private tokens per decoder.
+ *  max_priv_len      host bound on priv_lens entries, <= priv_bt_stride * 16.
+ *  Other arguments as for shared_kv_decode (same workspace size).  Needs
+ *  num_decoders * (num_q_heads / num_kv_heads) <= 64 (all rows of a KV head in
+ *  one wave); larger row counts return KVS_EUNSUPPORTED.
+ */
+int shared_kv_decode_private(const kvs_pool* pool, int32_t layer, const void* q, void* out,
+                             const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                             const int32_t* priv_block_table, int32_t priv_bt_stride,
+                             const int32_t* priv_lens, int32_t batch, int32_t num_decoders,
+                             int32_t num_q_heads, int32_t max_seq_len, int32_t max_priv_len,
+                             float scale, void* workspace, size_t workspace_bytes,
+                             int32_t* dev_status, hipStream_t stream);
 
 /*
  * partial_prefill_extend — cached-prefix extension over the new tokens only.

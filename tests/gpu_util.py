@@ -49,6 +49,14 @@ def sync():
     torch.cuda.synchronize()
 
 
+def nan_workspace(nbytes):
+    """A decode workspace whose every float reads as NaN: the library must not
+    read a byte of it that the same call has not written."""
+    import torch
+
+    return torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+
+
 def make_decode_case(lens, N, Hkv, G, D, seed, std=1.0, layers=1, layer=0, poison=POISON_BIG,
                      spare_frac=0.05):
     """Pool (GPU, via kv_pool_append) holding each session's logical K/V, plus queries.
@@ -81,10 +89,50 @@ def run_decode(case, q_bits=None, lens=None, bt=None, max_seq_len=None, scale=No
     B, N, Hq, D = q_bits.shape
     msl = max(max(lens), 1) if max_seq_len is None else max_seq_len
     scale = 1.0 / np.sqrt(D) if scale is None else scale
-    ws = torch.zeros(binding.decode_workspace_bytes(B, N, Hq, case["Hkv"], D, msl), dtype=torch.uint8,
-                     device="cuda")
+    ws = nan_workspace(binding.decode_workspace_bytes(B, N, Hq, case["Hkv"], D, msl))
     out = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device="cuda")
     binding.decode(case["pool"], case["layer"], dev_bf16(q_bits), out, dev_i32(bt), dev_i32(lens), msl,
                    scale, ws, dev_status=case["status"])
+    sync()
+    return out
+
+
+def make_private_case(lens, priv, N, Hkv, G, D, seed, poison=POISON_NAN, std=1.0):
+    """Pool (GPU) with B shared prefixes and B*N private suffixes, appended with
+    kv_pool_append through the two block tables; logical K/V kept for the oracle."""
+    rng = np.random.default_rng(seed)
+    bt, pbt, num_pages = wlmod.build_private_tables(lens, priv, seed, spare_frac=0.05)
+    K = [wlmod.draw_bf16(rng, (L, Hkv, D), std) for L in lens]
+    V = [wlmod.draw_bf16(rng, (L, Hkv, D), std) for L in lens]
+    Kp = [wlmod.draw_bf16(rng, (U, Hkv, D), std) for U in priv]
+    Vp = [wlmod.draw_bf16(rng, (U, Hkv, D), std) for U in priv]
+    q = wlmod.draw_bf16(rng, (len(lens), N, Hkv * G, D), std)
+    pool = binding.Pool(1, num_pages, Hkv, D, fill=np.int16(np.uint16(poison).view(np.int16)))
+    st = status_tensor()
+    for table, ks, vs, ls in ((bt, K, V, lens), (pbt, Kp, Vp, priv)):
+        kk, cu = wlmod.concat_rows(ks)
+        vv, _ = wlmod.concat_rows(vs)
+        if kk.shape[0]:
+            m = max(max(ls), 1)
+            binding.append(pool, 0, dev_bf16(kk), dev_bf16(vv), dev_i32(cu), dev_i32(table),
+                           dev_i32(np.zeros(len(ls))), max_new=m, max_seq_len=m, dev_status=st)
+    return dict(lens=list(lens), priv=list(priv), N=N, Hkv=Hkv, G=G, D=D, bt=bt, pbt=pbt,
+                num_pages=num_pages, K=K, V=V, Kp=Kp, Vp=Vp, q=q, pool=pool, status=st, layer=0)
+
+
+def run_decode_private(case, q_bits=None, priv=None, pbt=None, max_priv_len=None, scale=None):
+    import torch
+
+    q_bits = case["q"] if q_bits is None else q_bits
+    priv = case["priv"] if priv is None else priv
+    pbt = case["pbt"] if pbt is None else pbt
+    B, N, Hq, D = q_bits.shape
+    msl = max(max(case["lens"]), 1)
+    mpl = max(max(priv), 0) if max_priv_len is None else max_priv_len
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    ws = nan_workspace(binding.decode_workspace_bytes(B, N, Hq, case["Hkv"], D, msl))
+    out = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device="cuda")
+    binding.decode_private(case["pool"], 0, dev_bf16(q_bits), out, dev_i32(case["bt"]), dev_i32(case["lens"]),
+                           dev_i32(pbt), dev_i32(priv), msl, mpl, scale, ws, dev_status=case["status"])
     sync()
     return out

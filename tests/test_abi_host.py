@@ -32,7 +32,8 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol(L):
     names = header_functions()
-    assert {"kv_pool_append", "shared_kv_decode", "partial_prefill_extend", "kvs_pool_bytes",
+    assert {"kv_pool_append", "shared_kv_decode", "shared_kv_decode_private", "partial_prefill_extend",
+            "kvs_pool_bytes",
             "shared_kv_decode_workspace_bytes", "kvs_last_error", "kvs_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -86,6 +87,29 @@ def call_decode(L, p, layer=0, q=FAKE, out=FAKE, bt=FAKE, stride=4, lens=FAKE, b
 def test_decode_host_checks(L, kw, status):
     p = kw.pop("p")
     assert call_decode(L, p, **kw) == status
+    assert binding.last_error()
+
+
+def call_decode_private(L, p, q=FAKE, bt=FAKE, pbt=FAKE, pstride=2, plens=FAKE, N=2, Hq=8, msl=64, mpl=32,
+                        ws=FAKE, wsb=1 << 30):
+    return L.shared_kv_decode_private(ctypes.byref(p), 0, q, FAKE, bt, 4, FAKE, pbt, pstride, plens, 2, N, Hq,
+                                      msl, mpl, 0.125, ws, wsb, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=pool(), pbt=None), binding.KVS_EINVAL),
+    (dict(p=pool(), plens=None), binding.KVS_EINVAL),
+    (dict(p=pool(), q=None), binding.KVS_EINVAL),
+    (dict(p=pool(), pstride=0), binding.KVS_EINVAL),
+    (dict(p=pool(), mpl=-1), binding.KVS_EINVAL),
+    (dict(p=pool(), mpl=33), binding.KVS_ERANGE),            # > priv_bt_stride * 16
+    (dict(p=pool(), N=17), binding.KVS_EUNSUPPORTED),        # 17 * 4 rows per KV head > 64
+    (dict(p=pool(), msl=65), binding.KVS_ERANGE),
+    (dict(p=pool(), wsb=16), binding.KVS_EWORKSPACE),
+])
+def test_decode_private_host_checks(L, kw, status):
+    p = kw.pop("p")
+    assert call_decode_private(L, p, **kw) == status
     assert binding.last_error()
 
 

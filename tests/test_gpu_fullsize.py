@@ -87,7 +87,7 @@ def test_decode_full_size_sampled(name, layers, layer):
                    max_seq_len=maxL, dev_status=st)
     q = W.device_normal_bf16(B * N * Hq * D, wl.std, W.mix_seed(wl.seed, 12, layer)).view(B, N, Hq, D)
     out = torch.empty_like(q)
-    ws = torch.zeros(binding.decode_workspace_bytes(B, N, Hq, Hkv, D, maxL), dtype=torch.uint8, device="cuda")
+    ws = gu.nan_workspace(binding.decode_workspace_bytes(B, N, Hq, Hkv, D, maxL))
     binding.decode(pool, layer, q, out, bt_d, gu.dev_i32(lens), maxL, wl.scale, ws, dev_status=st)
     gu.sync()
     assert int(st.item()) == 0
