@@ -30,6 +30,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 DECODE_WORKLOAD = "qwen3_8b_n8"
 EXTEND_WORKLOAD = "extend_8k_512"
+PRIVATE_WORKLOAD = "qwen3_8b_n8_private"
 
 
 def log(msg):
@@ -43,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--extend-calls", type=int, default=40)
     ap.add_argument("--extend-warmup", type=int, default=50)
+    ap.add_argument("--private-calls", type=int, default=20)
+    ap.add_argument("--no-private", action="store_true", help="skip the private-suffix decode section")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -106,6 +109,15 @@ def decode_bytes(lens, B, N, Hq, Hkv, D):
     qo = 2 * B * N * Hq * D * 2
     bt = 4 * sum((L + 15) // 16 for L in lens)
     return kv + qo + bt + 4 * B
+
+
+def private_decode_bytes(lens, priv, B, N, Hq, Hkv, D):
+    """Algorithmic bytes of one shared_kv_decode_private call: the shared KV once, every
+    private KV once, q + out, both block tables and all lengths."""
+    kv = (sum(lens) + sum(priv)) * Hkv * D * 2 * 2
+    qo = 2 * B * N * Hq * D * 2
+    bt = 4 * (sum((L + 15) // 16 for L in lens) + sum((U + 15) // 16 for U in priv))
+    return kv + qo + bt + 4 * (B + B * N)
 
 
 def append_bytes(tokens, Hkv, D):
@@ -232,6 +244,67 @@ def extend_call(wl, st):
 
     binding.extend(st["pool"], 0, st["q"], st["kn"], st["vn"], st["out"], st["cu"], st["bt"], st["pre"],
                    st["max_new"], st["msl"], wl.scale)
+
+
+def private_section(calls):
+    """shared_kv_decode_private on the private-suffix workload, one layer."""
+    import torch
+
+    from cross_model_shared_amd import binding
+    from cross_model_shared_amd import workload as W
+
+    wl = W.make_workload(PRIVATE_WORKLOAD)
+    B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    bt, pbt, num_pages = W.build_private_tables(wl.lens, wl.priv, wl.seed)
+    pool = binding.Pool(1, num_pages, Hkv, D)
+    zero_b = torch.zeros(B * N, dtype=torch.int32, device="cuda")
+    for i, (table, lens) in enumerate(((bt, wl.lens), (pbt, wl.priv))):
+        total = sum(lens)
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+        k = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 30 + 2 * i)).view(total, Hkv, D)
+        v = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 31 + 2 * i)).view(total, Hkv, D)
+        binding.append(pool, 0, k, v, cu, torch.from_numpy(table).cuda(), zero_b[:len(lens)],
+                       max_new=max(lens), max_seq_len=max(lens))
+        del k, v
+    q = W.device_normal_bf16(B * N * Hq * D, wl.std, W.mix_seed(wl.seed, 34)).view(B, N, Hq, D)
+    out = torch.empty_like(q)
+    maxL, maxU = max(wl.lens), max(wl.priv)
+    ws = torch.zeros(binding.decode_workspace_bytes(B, N, Hq, Hkv, D, maxL), dtype=torch.uint8, device="cuda")
+    d_bt, d_pbt = torch.from_numpy(bt).cuda(), torch.from_numpy(pbt).cuda()
+    d_lens = torch.tensor(wl.lens, dtype=torch.int32, device="cuda")
+    d_priv = torch.tensor(wl.priv, dtype=torch.int32, device="cuda")
+
+    def call():
+        binding.decode_private(pool, 0, q, out, d_bt, d_lens, d_pbt, d_priv, maxL, maxU, wl.scale, ws)
+
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    t = EventTimer()
+    for _ in range(calls):
+        e = t.start()
+        call()
+        t.stop(e)
+    torch.cuda.synchronize()
+    ms = float(np.median(t.all_ms()))
+    nbytes = private_decode_bytes(wl.lens, wl.priv, B, N, Hq, Hkv, D)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] private-suffix decode call {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+    shared_gb = sum(wl.lens) * Hkv * D * 4 / 1e9
+    priv_gb = sum(wl.priv) * Hkv * D * 4 / 1e9
+    res = {
+        "workload": f"{PRIVATE_WORKLOAD}: the {DECODE_WORKLOAD} sessions (shared prefixes, sum {sum(wl.lens)}) "
+                    f"plus a private suffix per decoder (U[0,2048], sum {sum(wl.priv)}), one layer, "
+                    f"shared_kv_decode_private",
+        "value": round(gbs, 1), "unit": "GB/s", "ms_per_call": round(ms, 5), "bytes_per_call": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "footprint": {"shared_plus_private_GB": round(shared_gb + priv_gb, 3),
+                      "n_full_copies_GB": round(N * shared_gb + priv_gb, 3)},
+    }
+    del pool
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(wl, st, target_s):
@@ -364,6 +437,8 @@ def main():
     ext_tflops = flops / (ext_ms * 1e-3) / 1e12
     log(f"[bench] extend call {ext_ms:.3f} ms, {ext_tflops:.1f} TFLOP/s")
 
+    private = None if args.no_private else private_section(args.private_calls)
+
     res = {
         "metric": "shared-KV decode attn KV GB/s (% HBM peak) at N=8 decoders; extend TFLOP/s",
         "value": round(value, 2),
@@ -395,6 +470,7 @@ def main():
                            "ms_N1": round(n1_ms, 4)},
         "footprint": {"pool_GB": round(pool_gb, 2), "n_private_copies_GB": round(pool_gb * N, 2),
                       "ratio": N},
+        "private": private,
         "extend": {
             "workload": f"{EXTEND_WORKLOAD}: B=16, cached prefix 8192 + 512 new tokens, 32 q / 8 KV heads, "
                         f"D=128 (partial_prefill_extend = append chunk + causal attention)",

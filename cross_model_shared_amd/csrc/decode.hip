@@ -297,6 +297,11 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
   const int num_pages = a.pool.num_pages;
   uint32_t bad = 0;  // ring slots whose page id was out of range
 
+  // decoder of each of the lane's rows (one row group per KV head when PRIV)
+  int row_dec[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) row_dec[cb] = (cb * 16 + (lane & 15)) / (a.num_q_heads / Hkv);
+
   Walker iw = seek<PRIV>(a, cum_s, B, Ptot, tau0);
   Walker cw = iw;
   auto issue = [&](int slot) {
@@ -343,24 +348,22 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       for (int i = 0; i < D / 32; ++i) kf[i] = ring[wave][slot][k_run(i, lane >> 4, lane & 15)];
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) vf[i] = v2[2 * v_run(D, i, lane >> 5, lane & 15) + ((lane >> 4) & 1)];
-      int lim[NB];
+      int lim[NB], nvalid;
+      bool masked;
       if (PRIV && cw.page >= cw.nsh) {
-        // a private page of decoder pn: only its rows (r / G == pn) see it
-        const int nvalid = min(kPage, cw.plen - cw.pp * kPage);
-        const int G = a.num_q_heads / Hkv;
+        // a private page of decoder pn: only its rows see it
+        nvalid = min(kPage, cw.plen - cw.pp * kPage);
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) {
-          const int r = (cw.gr % RGs) * 16 * NB + cb * 16 + (lane & 15);
-          lim[cb] = (r / G == cw.pn) ? nvalid : 0;
-        }
-        attend_page<D, NB>(st, qf, kf, vf, a.scale_log2, true, lim, nvalid, lane);
+        for (int cb = 0; cb < NB; ++cb) lim[cb] = (row_dec[cb] == cw.pn) ? nvalid : 0;
+        masked = true;
       } else {
         const int L = clamp_len(load_uniform(a.seq_lens + cw.b), a.max_seq_len);
-        const int nvalid = min(kPage, L - cw.page * kPage);
+        nvalid = min(kPage, L - cw.page * kPage);
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) lim[cb] = nvalid;
-        attend_page<D, NB>(st, qf, kf, vf, a.scale_log2, nvalid < kPage, lim, nvalid, lane);
+        masked = nvalid < kPage;
       }
+      attend_page<D, NB>(st, qf, kf, vf, a.scale_log2, masked, lim, nvalid, lane);
     }
     const int cur_gr = cw.gr, cur_b = cw.b;
     advance<PRIV>(a, cw, cum_s, B);

@@ -147,3 +147,50 @@ def test_extend_full_size_sampled():
         print(f"[fullsize] extend session {b}: {len(rows)} rows, max-abs err {err:.3e}", flush=True)
         assert err <= TOL
     check_tiles(pool, bt, 0, picks[-1], kf, vf, Hkv, D)  # prefix + appended chunk of the last pick
+
+
+def test_private_decode_full_size_sampled():
+    """qwen3_8b_n8_private at full size (64 sessions, 8 decoders, private suffixes up to
+    2048 tokens), in the bench's launch configuration; 8 sampled sessions, every
+    decoder and head, against the oracle over prefix ++ suffix."""
+    import torch
+
+    wl = W.make_workload("qwen3_8b_n8_private")
+    B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    print(f"[fullsize] private: B={B} N={N} sum(L)={sum(wl.lens)} sum(U)={sum(wl.priv)}", flush=True)
+    bt, pbt, num_pages = W.build_private_tables(wl.lens, wl.priv, wl.seed)
+    pool = binding.Pool(1, num_pages, Hkv, D, fill=np.int16(np.uint16(gu.POISON_NAN).view(np.int16)))
+    st = gu.status_tensor()
+    logical = []
+    for i, (table, lens) in enumerate(((bt, wl.lens), (pbt, wl.priv))):
+        total = sum(lens)
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        k = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 30 + 2 * i)).view(total, Hkv, D)
+        v = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 31 + 2 * i)).view(total, Hkv, D)
+        binding.append(pool, 0, k, v, gu.dev_i32(cu), torch.from_numpy(table).cuda(),
+                       gu.dev_i32(np.zeros(len(lens))), max_new=max(lens), max_seq_len=max(lens), dev_status=st)
+        logical.append((k, v, cu))
+    q = W.device_normal_bf16(B * N * Hq * D, wl.std, W.mix_seed(wl.seed, 34)).view(B, N, Hq, D)
+    out = torch.empty_like(q)
+    maxL, maxU = max(wl.lens), max(wl.priv)
+    ws = gu.nan_workspace(binding.decode_workspace_bytes(B, N, Hq, Hkv, D, maxL))
+    binding.decode_private(pool, 0, q, out, torch.from_numpy(bt).cuda(), gu.dev_i32(wl.lens),
+                           torch.from_numpy(pbt).cuda(), gu.dev_i32(wl.priv), maxL, maxU, wl.scale, ws,
+                           dev_status=st)
+    gu.sync()
+    assert int(st.item()) == 0
+    got = gu.host_f64(out)
+    assert np.all(np.isfinite(got))
+    picks = sample_sessions(wl.lens, 8, wl.seed)
+    qh = host_rows(q)
+    (ks, vs, cus), (kp, vp, cup) = logical
+    err = 0.0
+    for b in picks:
+        for n in range(N):
+            r = b * N + n
+            K = np.concatenate([host_rows(ks[cus[b]:cus[b + 1]]), host_rows(kp[cup[r]:cup[r + 1]])])
+            V = np.concatenate([host_rows(vs[cus[b]:cus[b + 1]]), host_rows(vp[cup[r]:cup[r + 1]])])
+            want = oracle.decode_from_logical(qh[b:b + 1, n:n + 1], [K], [V], wl.scale)[0]
+            err = max(err, float(np.max(np.abs(got[b, n:n + 1] - want))))
+    print(f"[fullsize] private: sessions {picks} max-abs err {err:.3e}", flush=True)
+    assert err <= TOL
