@@ -156,6 +156,62 @@ def gather(pool: np.ndarray, shape: PoolShape, layer: int, bt_row, length: int):
     return K, V
 
 
+def fetch(pool: np.ndarray, shape: PoolShape, layer: int, block_table: np.ndarray, seq_lens):
+    """The logical K, V rows of every session, as bf16 bits [sum(seq_lens), H_kv, D].
+
+    The inverse of `append` (DroidSpeak, section 5.4: fetch reads what store
+    wrote): row cu[b] + p holds logical position p of session b, p < seq_lens[b].
+    """
+    H, D = shape.num_kv_heads, shape.head_dim
+    kt, vt = shape.index_tables()
+    total = sum(int(L) for L in seq_lens)
+    K = np.empty((total, H, D), dtype=np.uint16)
+    V = np.empty((total, H, D), dtype=np.uint16)
+    row = 0
+    for b in range(len(seq_lens)):
+        for p in range(int(seq_lens[b])):
+            page = int(block_table[b, p // PAGE])
+            slot = p % PAGE
+            for h in range(H):
+                base = tile_start(layer, page, h, shape.num_pages, H, D)
+                K[row, h] = pool[base + kt[slot]]
+                V[row, h] = pool[base + vt[slot]]
+            row += 1
+    return K, V
+
+
+# ---------------------------------------------------------------------------
+# Page handoff between pools (PrefillShare, section 3.3: the prefill worker
+# hands the cache it wrote, kept in fixed-size blocks, to the decode worker)
+# ---------------------------------------------------------------------------
+def pack(pool: np.ndarray, shape: PoolShape, layer_begin: int, num_layers: int, page_ids) -> np.ndarray:
+    """Transfer buffer [num_layers][len(page_ids)][H_kv][tile] of the listed pages' tiles."""
+    H, D = shape.num_kv_heads, shape.head_dim
+    te = tile_elems(D)
+    buf = np.empty((num_layers, len(page_ids), H, te), dtype=np.uint16)
+    for li in range(num_layers):
+        for i, pid in enumerate(page_ids):
+            for h in range(H):
+                base = tile_start(layer_begin + li, int(pid), h, shape.num_pages, H, D)
+                buf[li, i, h] = pool[base:base + te]
+    return buf
+
+
+def unpack(pool: np.ndarray, shape: PoolShape, layer_begin: int, num_layers: int, page_ids,
+           buf: np.ndarray) -> np.ndarray:
+    """Copy of `pool` with entry i of the transfer buffer written to page page_ids[i]."""
+    H, D = shape.num_kv_heads, shape.head_dim
+    te = tile_elems(D)
+    out = np.array(pool, dtype=np.uint16, copy=True)
+    buf = np.asarray(buf, dtype=np.uint16).reshape(num_layers, len(page_ids), H, te)
+    for li in range(num_layers):
+        for i, pid in enumerate(page_ids):
+            for h in range(H):
+                base = tile_start(layer_begin + li, int(pid), h, shape.num_pages, H, D)
+                out[base:base + te] = buf[li, i, h]
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Attention by definition
 # ---------------------------------------------------------------------------

@@ -375,6 +375,72 @@ def test_private_suffix_reaches_only_its_decoder():
 
 
 # ---------------------------------------------------------------------------
+# Fetch (the inverse of append) and page handoff between pools
+# ---------------------------------------------------------------------------
+def test_fetch_returns_the_logical_rows_that_were_appended():
+    lens = [37, 0, 16, 70]
+    shape, pool, bt, K, V = build_session_pool(lens, 2, 64, seed=51)
+    k, v = oracle.fetch(pool, shape, 0, bt, lens)
+    kk, _ = wlmod.concat_rows(K)
+    vv, _ = wlmod.concat_rows(V)
+    assert np.array_equal(k, kk) and np.array_equal(v, vv)
+
+
+def test_fetch_agrees_with_the_float_gather():
+    lens = [45, 17]
+    shape, pool, bt, _, _ = build_session_pool(lens, 2, 128, seed=52, layers=2, layer=1)
+    k, v = oracle.fetch(pool, shape, 1, bt, lens)
+    row = 0
+    for b, L in enumerate(lens):
+        Kg, Vg = oracle.gather(pool, shape, 1, bt[b], L)
+        assert np.array_equal(oracle.bf16_to_f64(k[row:row + L]), Kg)
+        assert np.array_equal(oracle.bf16_to_f64(v[row:row + L]), Vg)
+        row += L
+
+
+def test_handoff_to_another_pool_preserves_every_session():
+    """Pack a session's pages for all layers, unpack them into a pool of a different
+    size under new page ids: the new block table reads back the same logical rows."""
+    lens, Hkv, D, layers = [50, 33], 2, 64, 3
+    bt, num_pages = wlmod.build_block_table(lens, 53)
+    shape = oracle.PoolShape(layers, num_pages, Hkv, D)
+    rng = RNG(53)
+    pool = poison_pool(shape)
+    logical = []
+    for layer in range(layers):
+        K = [bits(rng, (L, Hkv, D)) for L in lens]
+        V = [bits(rng, (L, Hkv, D)) for L in lens]
+        kk, cu = wlmod.concat_rows(K)
+        vv, _ = wlmod.concat_rows(V)
+        pool = oracle.append(pool, shape, layer, kk, vv, cu, bt, np.zeros(2, np.int32))
+        logical.append((kk, vv))
+    ids = [int(x) for x in bt[1, :(lens[1] + 15) // 16]]          # session 1 only
+    buf = oracle.pack(pool, shape, 0, layers, ids)
+    dst_shape = oracle.PoolShape(layers, 11, Hkv, D)
+    dst_ids = [7, 2, 9][:len(ids)]
+    dst = oracle.unpack(np.zeros(dst_shape.elems, np.uint16), dst_shape, 0, layers, dst_ids, buf)
+    for layer in range(layers):
+        k, v = oracle.fetch(dst, dst_shape, layer, np.array([dst_ids], np.int32), [lens[1]])
+        kk, vv = logical[layer]
+        assert np.array_equal(k, kk[lens[0]:]) and np.array_equal(v, vv[lens[0]:])
+    # pages not listed are untouched
+    te = oracle.tile_elems(D) * Hkv
+    for layer in range(layers):
+        for pg in set(range(11)) - set(dst_ids):
+            start = oracle.tile_start(layer, pg, 0, 11, Hkv, D)
+            assert not dst[start:start + te].any()
+
+
+def test_pack_of_a_layer_range_is_a_slice_of_the_full_pack():
+    lens = [40]
+    shape, pool, bt, _, _ = build_session_pool(lens, 2, 64, seed=54, layers=4, layer=2)
+    ids = [int(x) for x in bt[0, :3]]
+    full = oracle.pack(pool, shape, 0, 4, ids)
+    assert np.array_equal(oracle.pack(pool, shape, 2, 1, ids)[0], full[2])
+    assert np.array_equal(oracle.pack(pool, shape, 1, 2, ids[::-1]), full[1:3, ::-1])
+
+
+# ---------------------------------------------------------------------------
 # Extend
 # ---------------------------------------------------------------------------
 def _extend_case(prefix, new, Hkv, G, D, seed):

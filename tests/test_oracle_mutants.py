@@ -54,6 +54,10 @@ MUTANTS = {
     "v_layout_slab": ("slab = d // 16 ", "slab = d // 32 "),
     "decode_prefix_off_by_one": ("K, V = gather(pool, shape, layer, block_table[b], L)",
                                  "K, V = gather(pool, shape, layer, block_table[b], max(L - 1, 0))"),
+    "fetch_v_from_k": ("                V[row, h] = pool[base + vt[slot]]", "                V[row, h] = pool[base + kt[slot]]"),
+    "pack_layer_offset": ("base = tile_start(layer_begin + li, int(pid), h, shape.num_pages, H, D)\n                buf[li, i, h]",
+                          "base = tile_start(li, int(pid), h, shape.num_pages, H, D)\n                buf[li, i, h]"),
+    "unpack_head_order": ("out[base:base + te] = buf[li, i, h]", "out[base:base + te] = buf[li, i, H - 1 - h]"),
     "private_row_order": ("priv_table[b * N + n], int(priv_lens[b * N + n])",
                           "priv_table[n * B + b], int(priv_lens[n * B + b])"),
     "private_suffix_dropped": ("K = np.concatenate([Ks, Kp])\n            V = np.concatenate([Vs, Vp])",
@@ -76,6 +80,9 @@ PIN_CHECKS = [
     lambda: pins.test_extend_equals_causal_sdpa_over_whole_sequence([40, 0, 16], [9, 20, 1]),
     pins.test_private_decode_matches_brute_force_over_prefix_then_suffix,
     pins.test_private_suffix_reaches_only_its_decoder,
+    pins.test_fetch_returns_the_logical_rows_that_were_appended,
+    pins.test_handoff_to_another_pool_preserves_every_session,
+    pins.test_pack_of_a_layer_range_is_a_slice_of_the_full_pack,
 ]
 
 
@@ -92,6 +99,7 @@ def test_pins_catch_mutant(name, monkeypatch):
     mod = _mutant_module(*MUTANTS[name])
     for attr in ("bf16_to_f64", "k_offset", "v_offset", "tile_start", "append", "gather", "attend",
                  "decode", "decode_private", "extend", "decode_from_logical", "extend_from_logical", "PoolShape",
+                 "fetch", "pack", "unpack",
                  "tile_elems", "pool_elems"):
         monkeypatch.setattr(oracle, attr, getattr(mod, attr))
     failed = []
