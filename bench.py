@@ -31,6 +31,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 DECODE_WORKLOAD = "qwen3_8b_n8"
 EXTEND_WORKLOAD = "extend_8k_512"
 PRIVATE_WORKLOAD = "qwen3_8b_n8_private"
+HANDOFF_WORKLOAD = "handoff_8k"
 
 
 def log(msg):
@@ -46,6 +47,7 @@ def parse():
     ap.add_argument("--extend-warmup", type=int, default=50)
     ap.add_argument("--private-calls", type=int, default=20)
     ap.add_argument("--no-private", action="store_true", help="skip the private-suffix decode section")
+    ap.add_argument("--no-handoff", action="store_true", help="skip the page handoff section")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -307,6 +309,72 @@ def private_section(calls):
     return res
 
 
+def handoff_section(reps):
+    """kv_pages_pack / kv_pages_unpack of every page of the handoff workload (all 36 layers) and
+    kv_pool_fetch of its rows (all layers); HBM bytes = what is read + what is written."""
+    import torch
+
+    from cross_model_shared_amd import binding
+    from cross_model_shared_amd import workload as W
+
+    wl = W.make_workload(HANDOFF_WORKLOAD)
+    B, Hkv, D, layers = wl.batch, wl.num_kv_heads, wl.head_dim, wl.num_layers
+    bt, num_pages = W.build_block_table(wl.lens, wl.seed)
+    src = binding.Pool(layers, num_pages, Hkv, D)
+    total = sum(wl.lens)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(wl.lens)]).astype(np.int32)).cuda()
+    d_bt = torch.from_numpy(bt).cuda()
+    zeros = torch.zeros(B, dtype=torch.int32, device="cuda")
+    for layer in range(layers):
+        k = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 40, layer)).view(total, Hkv, D)
+        v = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 41, layer)).view(total, Hkv, D)
+        binding.append(src, layer, k, v, cu, d_bt, zeros, max_new=max(wl.lens), max_seq_len=max(wl.lens))
+        del k, v
+    ids = torch.from_numpy(np.concatenate([bt[b, :(L + 15) // 16] for b, L in enumerate(wl.lens)])).cuda()
+    n = ids.numel()
+    buf = torch.empty(binding.pages_buffer_bytes(src, layers, n), dtype=torch.uint8, device="cuda")
+    dst = binding.Pool(layers, n, Hkv, D)
+    dst_ids = torch.randperm(n, generator=torch.Generator().manual_seed(wl.seed)).to(torch.int32).cuda()
+    k_out = torch.empty((total, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    v_out = torch.empty_like(k_out)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t = EventTimer()
+        for _ in range(reps):
+            e = t.start()
+            fn()
+            t.stop(e)
+        torch.cuda.synchronize()
+        return float(np.median(t.all_ms()))
+
+    ms_pack = timed(lambda: binding.pack(src, 0, layers, ids, buf))
+    ms_unpack = timed(lambda: binding.unpack(dst, 0, layers, dst_ids, buf))
+    d_lens = torch.tensor(wl.lens, dtype=torch.int32, device="cuda")
+    ms_fetch = timed(lambda: [binding.fetch(src, l, d_bt, d_lens, cu, max(wl.lens), k_out, v_out)
+                              for l in range(layers)])
+    moved = buf.numel()                              # bytes of tiles moved by pack or unpack
+    fetched = 2 * total * Hkv * D * 2 * layers       # K and V rows of every layer
+    res = {
+        "workload": f"{HANDOFF_WORKLOAD}: {B} sessions x {wl.lens[0]} tokens, 8 KV heads, D=128, {layers} layers "
+                    f"({n} pages, {moved / 1e9:.2f} GB of tiles)",
+        "pack": {"ms": round(ms_pack, 4), "GBps": round(2 * moved / (ms_pack * 1e-3) / 1e9, 1),
+                 "frac": round(2 * moved / (ms_pack * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "unpack": {"ms": round(ms_unpack, 4), "GBps": round(2 * moved / (ms_unpack * 1e-3) / 1e9, 1),
+                   "frac": round(2 * moved / (ms_unpack * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "fetch_all_layers": {"ms": round(ms_fetch, 4), "GBps": round(2 * fetched / (ms_fetch * 1e-3) / 1e9, 1),
+                             "frac": round(2 * fetched / (ms_fetch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "unit": "GB/s (read + written)",
+    }
+    log(f"[bench] handoff pack {res['pack']['GBps']} GB/s, unpack {res['unpack']['GBps']} GB/s, "
+        f"fetch {res['fetch_all_layers']['GBps']} GB/s")
+    del src, dst, buf
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, st, target_s):
     """Time the CPU oracle's decode on a bounded sample of sessions of layer 0."""
     import torch
@@ -438,6 +506,7 @@ def main():
     log(f"[bench] extend call {ext_ms:.3f} ms, {ext_tflops:.1f} TFLOP/s")
 
     private = None if args.no_private else private_section(args.private_calls)
+    handoff = None if args.no_handoff else handoff_section(10)
 
     res = {
         "metric": "shared-KV decode attn KV GB/s (% HBM peak) at N=8 decoders; extend TFLOP/s",
@@ -471,6 +540,7 @@ def main():
         "footprint": {"pool_GB": round(pool_gb, 2), "n_private_copies_GB": round(pool_gb * N, 2),
                       "ratio": N},
         "private": private,
+        "handoff": handoff,
         "extend": {
             "workload": f"{EXTEND_WORKLOAD}: B=16, cached prefix 8192 + 512 new tokens, 32 q / 8 KV heads, "
                         f"D=128 (partial_prefill_extend = append chunk + causal attention)",

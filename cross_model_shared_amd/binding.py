@@ -44,6 +44,10 @@ _SIGNATURES = {
                                                 _i32, _i32, _i32, _i32, _f, _vp, _sz, _vp, _vp]),
     "partial_prefill_extend": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                               _i32, _i32, _i32, _i32, _i32, _f, _vp, _vp]),
+    "kv_pages_buffer_bytes": (_sz, [_pool_p, _i32, _i32]),
+    "kv_pages_pack": (ctypes.c_int, [_pool_p, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "kv_pages_unpack": (ctypes.c_int, [_pool_p, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "kv_pool_fetch": (ctypes.c_int, [_pool_p, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "kvs_last_error": (ctypes.c_char_p, []),
     "kvs_version": (ctypes.c_char_p, []),
 }
@@ -208,3 +212,47 @@ def extend(pool: Pool, layer, q, k_new, v_new, out, cu_new, block_table, seq_len
         block_table.shape[1], _ptr(seq_lens, "seq_lens", torch.int32), batch, Hq, T, max_new,
         max_seq_len, float(scale), _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True),
         _stream(stream)))
+
+
+def pages_buffer_bytes(pool: Pool, num_layers, num_ids) -> int:
+    return load().kv_pages_buffer_bytes(pool.struct, num_layers, num_ids)
+
+
+def pack(pool: Pool, layer_begin, num_layers, page_ids, buf, dev_status=None, stream=None):
+    """All KV heads' tiles of the listed pages, layers [layer_begin, +num_layers), into buf
+    (a device tensor of pages_buffer_bytes bytes), as [layer][page][head][tile]."""
+    torch = _torch()
+    n = page_ids.numel()
+    need = pages_buffer_bytes(pool, num_layers, n)
+    if buf.numel() * buf.element_size() < need:
+        raise ValueError(f"buf must hold {need} bytes")
+    _check(load().kv_pages_pack(pool.struct, layer_begin, num_layers, _ptr(page_ids, "page_ids", torch.int32), n,
+                                _ptr(buf, "buf"), _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True),
+                                _stream(stream)))
+
+
+def unpack(pool: Pool, layer_begin, num_layers, page_ids, buf, dev_status=None, stream=None):
+    """The inverse of pack: buffer entry i goes to page page_ids[i] of `pool`."""
+    torch = _torch()
+    n = page_ids.numel()
+    need = pages_buffer_bytes(pool, num_layers, n)
+    if buf.numel() * buf.element_size() < need:
+        raise ValueError(f"buf must hold {need} bytes")
+    _check(load().kv_pages_unpack(pool.struct, layer_begin, num_layers, _ptr(page_ids, "page_ids", torch.int32),
+                                  n, _ptr(buf, "buf"),
+                                  _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True),
+                                  _stream(stream)))
+
+
+def fetch(pool: Pool, layer, block_table, seq_lens, cu_rows, max_seq_len, k_out, v_out, dev_status=None,
+          stream=None):
+    """Logical K/V rows of each session into k_out / v_out: bf16 [total_rows, H_kv, D]."""
+    torch = _torch()
+    batch = seq_lens.numel()
+    total = k_out.shape[0]
+    row = pool.num_kv_heads * pool.head_dim
+    _check(load().kv_pool_fetch(
+        pool.struct, layer, _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
+        _ptr(seq_lens, "seq_lens", torch.int32), _ptr(cu_rows, "cu_rows", torch.int32, batch + 1), batch, total,
+        max_seq_len, _ptr(k_out, "k_out", torch.bfloat16, total * row), _ptr(v_out, "v_out", torch.bfloat16, total * row),
+        _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True), _stream(stream)))

@@ -82,7 +82,33 @@ struct ExtendArgs {
   int32_t* dev_status;
 };
 
+// Page handoff: a contiguous transfer buffer [num_layers][num_ids][H_kv][tile].
+struct HandoffArgs {
+  PoolView pool;
+  int layer_begin, num_layers;
+  const int32_t* page_ids;
+  int num_ids;
+  uint16_t* buf;   // pack writes it, unpack reads it
+  int32_t* dev_status;
+};
+
+// Logical rows out of the pool (the inverse of append).
+struct FetchArgs {
+  PoolView pool;
+  int layer;
+  const int32_t* bt;
+  int bt_stride;
+  const int32_t* seq_lens;
+  const int32_t* cu_rows;
+  int batch, total_rows, max_seq_len;
+  uint16_t* k_out;
+  uint16_t* v_out;
+  int32_t* dev_status;
+};
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_pack(const HandoffArgs& a, bool unpack, hipStream_t stream);
+hipError_t launch_fetch(const FetchArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream);
 

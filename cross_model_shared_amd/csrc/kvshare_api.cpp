@@ -235,4 +235,60 @@ int partial_prefill_extend(const kvs_pool* pool, int32_t layer, const void* q, c
   return launched(kvs::launch_extend(a, stream), "partial_prefill_extend");
 }
 
+size_t kv_pages_buffer_bytes(const kvs_pool* pool, int32_t num_layers, int32_t num_ids) {
+  if (!pool || num_layers <= 0 || num_ids < 0 || pool->num_kv_heads <= 0 || pool->head_dim <= 0) return 0;
+  return size_t(num_layers) * size_t(num_ids) * size_t(pool->num_kv_heads) * 32 * size_t(pool->head_dim) * 2;
+}
+
+}  // extern "C"
+
+namespace {
+
+int pack_common(const char* name, bool unpack, const kvs_pool* pool, int32_t layer_begin, int32_t num_layers,
+                const int32_t* page_ids, int32_t num_ids, const void* buf, int32_t* dev_status,
+                hipStream_t stream) {
+  int s = check_pool(pool, layer_begin);
+  if (s) return s;
+  if (num_layers <= 0 || int64_t(layer_begin) + num_layers > pool->num_layers)
+    return fail(KVS_ERANGE, "%s: layers [%d, %d + %d) outside the pool's %d", name, layer_begin, layer_begin,
+                num_layers, pool->num_layers);
+  if (num_ids < 0) return fail(KVS_EINVAL, "%s: num_ids %d is negative", name, num_ids);
+  if (num_layers > 65535) return fail(KVS_EUNSUPPORTED, "%s: %d layers in one call (at most 65535)", name, num_layers);
+  if (num_ids > 0 && (!page_ids || !buf)) return fail(KVS_EINVAL, "%s: a required pointer is NULL", name);
+  kvs::HandoffArgs a{view(pool), layer_begin, num_layers, page_ids, num_ids,
+                     static_cast<uint16_t*>(const_cast<void*>(buf)), dev_status};
+  return launched(kvs::launch_pack(a, unpack, stream), name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_pages_pack(const kvs_pool* pool, int32_t layer_begin, int32_t num_layers, const int32_t* page_ids,
+                  int32_t num_ids, void* buf, int32_t* dev_status, hipStream_t stream) {
+  return pack_common("kv_pages_pack", false, pool, layer_begin, num_layers, page_ids, num_ids, buf, dev_status,
+                     stream);
+}
+
+int kv_pages_unpack(const kvs_pool* pool, int32_t layer_begin, int32_t num_layers, const int32_t* page_ids,
+                    int32_t num_ids, const void* buf, int32_t* dev_status, hipStream_t stream) {
+  return pack_common("kv_pages_unpack", true, pool, layer_begin, num_layers, page_ids, num_ids, buf, dev_status,
+                     stream);
+}
+
+int kv_pool_fetch(const kvs_pool* pool, int32_t layer, const int32_t* block_table, int32_t bt_stride,
+                  const int32_t* seq_lens, const int32_t* cu_rows, int32_t batch, int32_t total_rows,
+                  int32_t max_seq_len, void* k_out, void* v_out, int32_t* dev_status, hipStream_t stream) {
+  int s = check_pool(pool, layer);
+  if (s) return s;
+  if (!block_table || !seq_lens || !cu_rows || !k_out || !v_out)
+    return fail(KVS_EINVAL, "kv_pool_fetch: a required pointer is NULL");
+  if ((s = check_table(batch, bt_stride, max_seq_len))) return s;
+  if (total_rows < 0) return fail(KVS_EINVAL, "kv_pool_fetch: total_rows %d is negative", total_rows);
+  if (batch > 65535) return fail(KVS_EUNSUPPORTED, "kv_pool_fetch: batch %d above 65535", batch);
+  kvs::FetchArgs a{view(pool), layer, block_table, bt_stride, seq_lens, cu_rows, batch, total_rows, max_seq_len,
+                   static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out), dev_status};
+  return launched(kvs::launch_fetch(a, stream), "kv_pool_fetch");
+}
+
 }  // extern "C"

@@ -20,6 +20,8 @@ normal, no trained weights exist here):
 * qwen3_14b_long  — Qwen3-14B-shaped: 40 q / 8 KV heads, D=128, N=2, 8 sessions,
                     lengths truncated log-normal (sigma 1, mu 9.7869, truncated
                     to [4K, 128K], mean ~27K).
+* handoff_8k      — 4 sessions of 8K tokens, Qwen3-8B-shaped (8 KV heads, D=128),
+                    36 layers: the cache a prefill worker hands to a decode worker.
 * qwen3_8b_n8_private — qwen3_8b_n8's sessions and shared prefixes, plus a
                     private suffix per decoder (its own generated tokens),
                     lengths uniform in [0, 2048].
@@ -103,6 +105,9 @@ def make_workload(name: str, seed: int | None = None) -> Workload:
         priv = [int(x) for x in r.integers(0, 2048, size=base.batch * base.num_decoders, endpoint=True)]
         return Workload(name, base.batch, base.num_decoders, base.num_q_heads, base.num_kv_heads,
                         base.head_dim, 1, base.std, s, "decode", lens=base.lens, priv=priv)
+    if name == "handoff_8k":
+        s = 5 if seed is None else seed
+        return Workload(name, 4, 1, 32, 8, 128, 36, 1.0, s, "decode", lens=[8192] * 4)
     if name == "extend_8k_512":
         s = 3 if seed is None else seed
         return Workload(name, 16, 1, 32, 8, 128, 1, 1.0, s, "extend",
@@ -115,7 +120,8 @@ def make_workload(name: str, seed: int | None = None) -> Workload:
     raise KeyError(name)
 
 
-WORKLOADS = ("tiny", "llama8b_n4", "qwen3_8b_n8", "extend_8k_512", "qwen3_14b_long", "qwen3_8b_n8_private")
+WORKLOADS = ("tiny", "llama8b_n4", "qwen3_8b_n8", "extend_8k_512", "qwen3_14b_long", "qwen3_8b_n8_private",
+             "handoff_8k")
 
 
 # ---------------------------------------------------------------------------

@@ -16,6 +16,8 @@
  *   kv_pool_append         write new K/V rows into pages        (the cache "store")
  *   shared_kv_decode       N decoders x G GQA heads, one KV read (decode attention)
  *   shared_kv_decode_private  the same over a shared prefix + per-decoder private suffixes
+ *   kv_pages_pack / kv_pages_unpack   pages <-> contiguous transfer buffer (cache handoff)
+ *   kv_pool_fetch          logical K/V rows back out of the pool (inverse of kv_pool_append)
  *   partial_prefill_extend append a chunk, then causal attention of the chunk
  *                          over cached prefix + chunk           (partial prefill)
  *
@@ -227,6 +229,53 @@ int partial_prefill_extend(const kvs_pool* pool, int32_t layer, const void* q, c
                            int32_t batch, int32_t num_q_heads, int32_t total_new, int32_t max_new,
                            int32_t max_seq_len, float scale, int32_t* dev_status,
                            hipStream_t stream);
+
+/*
+ * kv_pages_pack / kv_pages_unpack — move whole pages between a pool and a
+ * contiguous transfer buffer: the on-GPU half of a cache handoff.
+ *
+ * PrefillShare, section 3.3: the prefill worker hands the KV it wrote, kept in
+ * fixed-size blocks, to the decode worker.  pack copies, for every layer in
+ * [layer_begin, layer_begin + num_layers) and every listed physical page, all
+ * KV heads' tiles of that page into
+ *     buf[layer - layer_begin][i][head][tile]      (i = index in page_ids),
+ * bit for bit; unpack writes such a buffer into the listed pages of a pool
+ * (which may be another pool, of any page count, with the same num_kv_heads and
+ * head_dim).  A (layer, page) entry is num_kv_heads * 32 * head_dim bf16
+ * elements (64 KiB at 8 KV heads, D=128); kv_pages_buffer_bytes gives the size.
+ *
+ *  page_ids    int32 [num_ids], device; ids outside [0, num_pages) are skipped
+ *              and reported with KVS_DEV_BAD_PAGE (their buffer entries, or
+ *              pages, are left as they were).  unpack with a page listed twice
+ *              leaves that page holding one of its entries.
+ *  buf         device buffer of kv_pages_buffer_bytes(...) bytes, owned by the
+ *              caller; it must not overlap the pool.
+ */
+size_t kv_pages_buffer_bytes(const kvs_pool* pool, int32_t num_layers, int32_t num_ids);
+int kv_pages_pack(const kvs_pool* pool, int32_t layer_begin, int32_t num_layers, const int32_t* page_ids,
+                  int32_t num_ids, void* buf, int32_t* dev_status, hipStream_t stream);
+int kv_pages_unpack(const kvs_pool* pool, int32_t layer_begin, int32_t num_layers, const int32_t* page_ids,
+                    int32_t num_ids, const void* buf, int32_t* dev_status, hipStream_t stream);
+
+/*
+ * kv_pool_fetch — the logical K/V rows of sessions, read back out of the pool
+ * into dense arrays: the inverse of kv_pool_append.
+ *
+ * DroidSpeak, section 5.4: fetch returns what store wrote.  For session b and
+ * position p < seq_lens[b]:
+ *     k_out[cu_rows[b] + p][head][:] = K of position p,   v_out likewise,
+ * bit for bit, read through block_table row b.  Used to hand a cache to a
+ * consumer that keeps another layout.
+ *
+ *  k_out, v_out  bf16 [total_rows][num_kv_heads][head_dim], device.
+ *  cu_rows       int32 [batch+1], device; cu_rows[b+1] - cu_rows[b] must equal
+ *                seq_lens[b] (a session that breaks this, or whose rows would
+ *                pass total_rows, is skipped and reported with KVS_DEV_BAD_LEN).
+ *  max_seq_len   host bound on seq_lens[b], <= bt_stride * 16.
+ */
+int kv_pool_fetch(const kvs_pool* pool, int32_t layer, const int32_t* block_table, int32_t bt_stride,
+                  const int32_t* seq_lens, const int32_t* cu_rows, int32_t batch, int32_t total_rows,
+                  int32_t max_seq_len, void* k_out, void* v_out, int32_t* dev_status, hipStream_t stream);
 
 /* Thread-local description of the last non-zero status returned on this thread. */
 const char* kvs_last_error(void);

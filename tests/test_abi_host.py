@@ -33,7 +33,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol(L):
     names = header_functions()
     assert {"kv_pool_append", "shared_kv_decode", "shared_kv_decode_private", "partial_prefill_extend",
-            "kvs_pool_bytes",
+            "kv_pages_pack", "kv_pages_unpack", "kv_pages_buffer_bytes", "kv_pool_fetch", "kvs_pool_bytes",
             "shared_kv_decode_workspace_bytes", "kvs_last_error", "kvs_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -155,6 +155,49 @@ def call_extend(L, p, q=FAKE, k=FAKE, v=FAKE, out=FAKE, cu=FAKE, bt=FAKE, stride
 def test_extend_host_checks(L, kw, status):
     p = kw.pop("p")
     assert call_extend(L, p, **kw) == status
+
+
+@pytest.mark.parametrize("unpack", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=pool(data=None)), binding.KVS_EINVAL),
+    (dict(p=pool(layers=2), lb=2), binding.KVS_ERANGE),
+    (dict(p=pool(layers=2), lb=1, nl=2), binding.KVS_ERANGE),
+    (dict(p=pool(), nl=0), binding.KVS_ERANGE),
+    (dict(p=pool(), n=-1), binding.KVS_EINVAL),
+    (dict(p=pool(), ids=None), binding.KVS_EINVAL),
+    (dict(p=pool(), buf=None), binding.KVS_EINVAL),
+    (dict(p=pool(dim=96)), binding.KVS_EUNSUPPORTED),
+])
+def test_pack_host_checks(L, unpack, kw, status):
+    kw = dict(kw)
+    p = kw.pop("p", pool())
+    args = dict(lb=0, nl=1, ids=FAKE, n=4, buf=FAKE)
+    args.update(kw)
+    fn = L.kv_pages_unpack if unpack else L.kv_pages_pack
+    assert fn(ctypes.byref(p), args["lb"], args["nl"], args["ids"], args["n"], args["buf"], None, None) == status
+    assert binding.last_error()
+
+
+def test_pages_buffer_bytes(L):
+    p = pool(layers=4, heads=8, dim=128)
+    assert L.kv_pages_buffer_bytes(ctypes.byref(p), 3, 10) == 3 * 10 * 8 * 32 * 128 * 2
+    assert L.kv_pages_buffer_bytes(ctypes.byref(p), 0, 10) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), binding.KVS_EINVAL),
+    (dict(cu=None), binding.KVS_EINVAL),
+    (dict(k=None), binding.KVS_EINVAL),
+    (dict(batch=0), binding.KVS_EINVAL),
+    (dict(msl=65), binding.KVS_ERANGE),
+    (dict(total=-1), binding.KVS_EINVAL),
+    (dict(layer=3), binding.KVS_ERANGE),
+])
+def test_fetch_host_checks(L, kw, status):
+    a = dict(layer=0, bt=FAKE, cu=FAKE, k=FAKE, batch=2, msl=64, total=10)
+    a.update(kw)
+    assert L.kv_pool_fetch(ctypes.byref(pool()), a["layer"], a["bt"], 4, FAKE, a["cu"], a["batch"], a["total"],
+                           a["msl"], a["k"], FAKE, None, None) == status
 
 
 def test_binding_refuses_cpu_tensors():
