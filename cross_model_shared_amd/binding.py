@@ -42,6 +42,8 @@ _SIGNATURES = {
                                         _f, _vp, _sz, _vp, _vp]),
     "shared_kv_decode_private": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32,
                                                 _i32, _i32, _i32, _i32, _f, _vp, _sz, _vp, _vp]),
+    "shared_kv_decode_cascade": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32,
+                                                _i32, _i32, _f, _vp, _sz, _vp, _vp]),
     "partial_prefill_extend": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                               _i32, _i32, _i32, _i32, _i32, _f, _vp, _vp]),
     "kv_pages_buffer_bytes": (_sz, [_pool_p, _i32, _i32]),
@@ -192,6 +194,23 @@ def decode_private(pool: Pool, layer, q, out, block_table, seq_lens, priv_block_
         _ptr(seq_lens, "seq_lens", torch.int32, B),
         _ptr(priv_block_table, "priv_block_table", torch.int32), priv_block_table.shape[1],
         _ptr(priv_lens, "priv_lens", torch.int32, B * N), B, N, Hq, max_seq_len, max_priv_len, float(scale),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True), _stream(stream)))
+
+
+def decode_cascade(pool: Pool, layer, q, out, block_table, seq_lens, group_id, group_prefix_pages, max_seq_len,
+                   scale, workspace, dev_status=None, stream=None):
+    """shared_kv_decode where adjacent sessions with equal group_id share their first
+    group_prefix_pages pages (int32 [B] each); q, out: bf16 [B, N, H_q, D]."""
+    torch = _torch()
+    B, N, Hq, D = q.shape
+    if D != pool.head_dim or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q/out shape does not match the pool")
+    _check(load().shared_kv_decode_cascade(
+        pool.struct, layer, _ptr(q, "q", torch.bfloat16), _ptr(out, "out", torch.bfloat16),
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
+        _ptr(seq_lens, "seq_lens", torch.int32, B), _ptr(group_id, "group_id", torch.int32, B),
+        _ptr(group_prefix_pages, "group_prefix_pages", torch.int32, B), B, N, Hq, max_seq_len, float(scale),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True), _stream(stream)))
 

@@ -23,6 +23,15 @@
 // is read once, by the wave that holds all of the KV head's rows, with the rows
 // of the other decoders masked out, so the shared prefix still streams once for
 // all N decoders and each suffix once for its own.
+//
+// Prefixes shared across sessions (cascade): sessions whose block tables start
+// with the same pages (a prefix cache hands the same physical pages to every
+// session with that prefix) are grouped into units of up to 64 / (N*G)
+// sessions by decode_cascade_plan_kernel; a unit's tile list is the common
+// prefix pages, read once for all its sessions' rows, followed by each
+// session's own remaining pages for that session's rows.
+#include <limits.h>
+
 #include "attn_core.h"
 #include "kvs_internal.h"
 
@@ -58,53 +67,99 @@ __device__ __forceinline__ void wait_ring(int pages_after) {
 
 __device__ __forceinline__ int clamp_len(int L, int max_len) { return L < 0 ? 0 : (L > max_len ? max_len : L); }
 
-// Position in the tile list: unit (gr = KV head * rowgroups + row group, session b), page.
-// With private suffixes, pages nsh.. of a unit are private: page pp of decoder pn
-// (pnpg pages, plen tokens).
+// Tile-list modes: plain (units are sessions), private (units are sessions,
+// followed by each decoder's private pages), cascade (units are groups of
+// sessions sharing prefix pages, followed by each session's own pages).
+enum { kPlain = 0, kPrivate = 1, kCascade = 2 };
+
+// Position in the tile list: unit (gr = KV head * rowgroups + row group, unit b), page.
+// Pages nsh.. of a unit belong to one owner at a time (private: a decoder;
+// cascade: a session of the group): page pp of owner pn (pnpg pages, plen tokens).
 struct Walker {
   int gr, b, page, npg;
   int nsh, pn, pp, pnpg, plen;
 };
 
-__device__ __forceinline__ int shared_pages(const DecodeArgs& a, int b) {
-  return (clamp_len(load_uniform(a.seq_lens + b), a.max_seq_len) + kPage - 1) / kPage;
+// Cascade unit tables in the workspace: first session, session count and
+// common prefix pages of each unit.
+__device__ __forceinline__ int unit_first(const DecodeArgs& a, int u) { return load_uniform(a.ws_units + u); }
+__device__ __forceinline__ int unit_count(const DecodeArgs& a, int u) {
+  return load_uniform(a.ws_units + a.batch + u);
+}
+__device__ __forceinline__ int unit_prefix(const DecodeArgs& a, int u) {
+  return load_uniform(a.ws_units + 2 * a.batch + u);
 }
 
-// Private tokens of decoder n of session b.
-__device__ __forceinline__ int priv_len(const DecodeArgs& a, int b, int n) {
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int b) {
+  return clamp_len(load_uniform(a.seq_lens + b), a.max_seq_len);
+}
+__device__ __forceinline__ int shared_pages(const DecodeArgs& a, int b) {
+  return (seq_len(a, b) + kPage - 1) / kPage;
+}
+
+// Pages of unit b before its first owner page.
+template <int MODE>
+__device__ __forceinline__ int head_pages(const DecodeArgs& a, int b) {
+  return MODE == kCascade ? unit_prefix(a, b) : shared_pages(a, b);
+}
+
+template <int MODE>
+__device__ __forceinline__ int owners(const DecodeArgs& a, int b) {
+  return MODE == kCascade ? unit_count(a, b) : a.num_decoders;
+}
+
+// Tokens of owner n of unit b.
+template <int MODE>
+__device__ __forceinline__ int owner_len(const DecodeArgs& a, int b, int n) {
+  if (MODE == kCascade) return max(seq_len(a, unit_first(a, b) + n) - unit_prefix(a, b) * kPage, 0);
   return clamp_len(load_uniform(a.plens + int64_t(b) * a.num_decoders + n), a.max_priv_len);
 }
 
-// First decoder at or after n with private pages (the caller knows one exists).
-__device__ __forceinline__ void first_priv(const DecodeArgs& a, Walker& w, int n) {
-  int U = priv_len(a, w.b, n);
-  while (U == 0 && n + 1 < a.num_decoders) U = priv_len(a, w.b, ++n);
+// Physical page at walker position w.
+template <int MODE>
+__device__ __forceinline__ int page_id(const DecodeArgs& a, const Walker& w) {
+  if (MODE == kCascade) {
+    const int first = unit_first(a, w.b);
+    if (w.page < w.nsh) return load_uniform(a.bt + int64_t(first) * a.bt_stride + w.page);
+    return load_uniform(a.bt + int64_t(first + w.pn) * a.bt_stride + w.nsh + w.pp);
+  }
+  if (MODE == kPrivate && w.page >= w.nsh)
+    return load_uniform(a.pbt + (int64_t(w.b) * a.num_decoders + w.pn) * a.pbt_stride + w.pp);
+  return load_uniform(a.bt + int64_t(w.b) * a.bt_stride + w.page);
+}
+
+// First owner at or after n with pages (the caller knows one exists).
+template <int MODE>
+__device__ __forceinline__ void first_owner(const DecodeArgs& a, Walker& w, int n) {
+  const int no = owners<MODE>(a, w.b);
+  int U = owner_len<MODE>(a, w.b, n);
+  while (U == 0 && n + 1 < no) U = owner_len<MODE>(a, w.b, ++n);
   w.pn = n;
   w.pp = 0;
   w.plen = U;
   w.pnpg = (U + kPage - 1) / kPage;
 }
 
-// Private sub-position after w.page moved to the next page of the same unit, or
+// Owner sub-position after w.page moved to the next page of the same unit, or
 // to page 0 of a new unit (w.nsh already set).
-template <bool PRIV>
+template <int MODE>
 __device__ __forceinline__ void enter_page(const DecodeArgs& a, Walker& w) {
-  if (!PRIV || w.page < w.nsh) return;
-  if (w.page == w.nsh) first_priv(a, w, 0);
-  else if (++w.pp == w.pnpg) first_priv(a, w, w.pn + 1);
+  if (MODE == kPlain || w.page < w.nsh) return;
+  if (w.page == w.nsh) first_owner<MODE>(a, w, 0);
+  else if (++w.pp == w.pnpg) first_owner<MODE>(a, w, w.pn + 1);
 }
 
 __device__ __forceinline__ int read_cum(const int* cum, int i) {
   return __builtin_amdgcn_readfirstlane(cum[i]);
 }
 
-// First nonempty session at or after b (B if none).
+// First nonempty unit at or after b (B if none).
 __device__ __forceinline__ int next_nonempty(const int* cum, int b, int B) {
   while (b < B && read_cum(cum, b + 1) == read_cum(cum, b)) ++b;
   return b;
 }
 
-template <bool PRIV>
+template <int MODE>
 __device__ __forceinline__ Walker seek(const DecodeArgs& a, const int* cum, int B, int Ptot, int64_t tau) {
   Walker w{};
   w.gr = int(tau / Ptot);
@@ -115,17 +170,18 @@ __device__ __forceinline__ Walker seek(const DecodeArgs& a, const int* cum, int 
     if (read_cum(cum, mid) <= r) lo = mid;
     else hi = mid;
   }
-  lo = next_nonempty(cum, lo, B);  // cum[b] <= r < cum[b+1] skips empty sessions
+  lo = next_nonempty(cum, lo, B);  // cum[b] <= r < cum[b+1] skips empty units
   w.b = lo;
   w.page = r - read_cum(cum, lo);
   w.npg = read_cum(cum, lo + 1) - read_cum(cum, lo);
-  if (PRIV && lo < B) {
-    w.nsh = shared_pages(a, lo);
-    if (w.page >= w.nsh) {  // find the decoder and page of private position page - nsh
+  if (MODE != kPlain && lo < B) {
+    w.nsh = head_pages<MODE>(a, lo);
+    if (w.page >= w.nsh) {  // find the owner and page of owner position page - nsh
       int q = w.page - w.nsh, n = 0;
+      const int no = owners<MODE>(a, lo);
       for (;; ++n) {
-        const int U = priv_len(a, lo, n), np = (U + kPage - 1) / kPage;
-        if (q < np || n + 1 == a.num_decoders) {
+        const int U = owner_len<MODE>(a, lo, n), np = (U + kPage - 1) / kPage;
+        if (q < np || n + 1 == no) {
           w.pn = n;
           w.pp = q;
           w.plen = U;
@@ -139,10 +195,10 @@ __device__ __forceinline__ Walker seek(const DecodeArgs& a, const int* cum, int 
   return w;
 }
 
-template <bool PRIV>
+template <int MODE>
 __device__ __forceinline__ void advance(const DecodeArgs& a, Walker& w, const int* cum, int B) {
   if (++w.page < w.npg) {
-    enter_page<PRIV>(a, w);
+    enter_page<MODE>(a, w);
     return;
   }
   w.page = 0;
@@ -153,42 +209,51 @@ __device__ __forceinline__ void advance(const DecodeArgs& a, Walker& w, const in
   }
   w.b = b;
   w.npg = b < B ? read_cum(cum, b + 1) - read_cum(cum, b) : 0;
-  if (PRIV && b < B) {
-    w.nsh = shared_pages(a, b);
-    enter_page<PRIV>(a, w);
+  if (MODE != kPlain && b < B) {
+    w.nsh = head_pages<MODE>(a, b);
+    enter_page<MODE>(a, w);
   }
+}
+
+// q / out row (index into [batch][N][H_q]) of row r of unit b and KV head g; -1
+// past the unit's rows.
+template <int MODE>
+__device__ __forceinline__ int64_t unit_row(const DecodeArgs& a, int b, int g, int r) {
+  const int G = a.num_q_heads / a.pool.num_kv_heads, NG = a.num_decoders * G;
+  if (MODE == kCascade) {
+    if (r >= unit_count(a, b) * NG) return -1;
+    const int s = unit_first(a, b) + r / NG, n = (r % NG) / G;
+    return (int64_t(s) * a.num_decoders + n) * a.num_q_heads + g * G + r % G;
+  }
+  if (r >= NG) return -1;
+  return (int64_t(b) * a.num_decoders + r / G) * a.num_q_heads + g * G + r % G;
 }
 
 __device__ __forceinline__ int64_t share_start(int k, int64_t T, int W) { return int64_t(k) * T / W; }
 
-template <int D, int NB>
+template <int D, int NB, int MODE>
 __device__ __forceinline__ void load_q(QFrag<D, NB>& qf, const DecodeArgs& a, int b, int g, int rg,
                                        int lane) {
-  const int G = a.num_q_heads / a.pool.num_kv_heads;
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
-    const int r = rg * 16 * NB + cb * 16 + (lane & 15);
-    const bool valid = r < a.plan.rows;
-    const int n = valid ? r / G : 0, h = valid ? g * G + r % G : 0;
-    const uint16_t* qrow = a.q + ((int64_t(b) * a.num_decoders + n) * a.num_q_heads + h) * D;
+    const int64_t row = unit_row<MODE>(a, b, g, rg * 16 * NB + cb * 16 + (lane & 15));
+    const uint16_t* qrow = a.q + (row < 0 ? 0 : row) * D;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
-      qf.q[cb][i] = valid ? *reinterpret_cast<const u32x4*>(qrow + 32 * i + 8 * (lane >> 4))
-                          : u32x4{0u, 0u, 0u, 0u};
+      qf.q[cb][i] = row >= 0 ? *reinterpret_cast<const u32x4*>(qrow + 32 * i + 8 * (lane >> 4))
+                             : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
-template <int D, int NB>
+template <int D, int NB, int MODE>
 __device__ __forceinline__ void write_rows(const DecodeArgs& a, const RowState<D, NB>& st, int b, int g,
                                            int rg, int lane) {
-  const int G = a.num_q_heads / a.pool.num_kv_heads;
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     const float l = wave_sum_across_quads(st.l[cb]);
-    const int r = rg * 16 * NB + cb * 16 + (lane & 15);
-    if (r >= a.plan.rows) continue;
-    const int n = r / G, h = g * G + r % G;
-    uint16_t* o = a.out + ((int64_t(b) * a.num_decoders + n) * a.num_q_heads + h) * D;
+    const int64_t row = unit_row<MODE>(a, b, g, rg * 16 * NB + cb * 16 + (lane & 15));
+    if (row < 0) continue;
+    uint16_t* o = a.out + row * D;
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
@@ -229,7 +294,7 @@ __device__ __forceinline__ int priv_pages(const DecodeArgs& a, int b) {
   return pages;
 }
 
-template <int D, int NB, int S, bool PRIV>
+template <int D, int NB, int S, int MODE>
 __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
   constexpr int SLABS = D / 16;  // 1 KiB slabs per (page, head) tile: K slabs then V slabs
   __shared__ u32x4 ring[kWaves][S][SLABS * 64];
@@ -238,8 +303,14 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: lets the compiler
-  const int B = a.batch, Hkv = a.pool.num_kv_heads, RGs = a.plan.rowgroups;  // use scalar loads
+  const int Hkv = a.pool.num_kv_heads, RGs = a.plan.rowgroups;  // use scalar loads
+  // units: sessions, or (cascade) the groups the plan kernel formed
+  const int B = MODE == kCascade ? load_uniform(a.ws_units + 3 * a.batch) : a.batch;
 
+  if (MODE == kCascade) {  // the plan kernel wrote the units' page prefix sum
+    for (int u = tid; u <= B; u += 256) cum_s[u] = a.ws_cum[u];
+    __syncthreads();
+  } else {
   // ---- pages per session and their exclusive prefix sum (every workgroup) ----
   const int chunk = (B + 255) / 256;
   int local = 0;
@@ -249,7 +320,7 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       const int L = a.seq_lens[b];
       if ((L < 0 || L > a.max_seq_len) && blockIdx.x == 0) flag_error(a.dev_status, KVS_DEV_BAD_LEN_BIT);
       local += (clamp_len(L, a.max_seq_len) + kPage - 1) / kPage;
-      if (PRIV) local += priv_pages(a, b);
+      if (MODE == kPrivate) local += priv_pages(a, b);
     }
   }
   part_s[tid] = local;
@@ -276,7 +347,7 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       if (b < B) {
         cum_s[b] = run;
         run += (clamp_len(a.seq_lens[b], a.max_seq_len) + kPage - 1) / kPage;
-        if (PRIV) run += priv_pages(a, b);
+        if (MODE == kPrivate) run += priv_pages(a, b);
       }
     }
     if (tid == 255) cum_s[B] = run;
@@ -284,6 +355,7 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
   __syncthreads();
   if (blockIdx.x == 0)
     for (int b = tid; b <= B; b += 256) a.ws_cum[b] = cum_s[b];
+  }
   __builtin_amdgcn_s_waitcnt(0);  // nothing outstanding before the ring starts
 
   const int Ptot = cum_s[B];
@@ -297,18 +369,18 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
   const int num_pages = a.pool.num_pages;
   uint32_t bad = 0;  // ring slots whose page id was out of range
 
-  // decoder of each of the lane's rows (one row group per KV head when PRIV)
-  int row_dec[NB];
+  // owner of each of the lane's rows (one row group per KV head in the owner
+  // modes): its decoder (private) or its session within the unit (cascade)
+  int row_owner[NB];
+  const int owner_rows = (MODE == kCascade ? a.num_decoders : 1) * (a.num_q_heads / Hkv);
 #pragma unroll
-  for (int cb = 0; cb < NB; ++cb) row_dec[cb] = (cb * 16 + (lane & 15)) / (a.num_q_heads / Hkv);
+  for (int cb = 0; cb < NB; ++cb) row_owner[cb] = (cb * 16 + (lane & 15)) / owner_rows;
 
-  Walker iw = seek<PRIV>(a, cum_s, B, Ptot, tau0);
+  Walker iw = seek<MODE>(a, cum_s, B, Ptot, tau0);
   Walker cw = iw;
   auto issue = [&](int slot) {
     const int g = iw.gr / RGs;
-    int pid = (PRIV && iw.page >= iw.nsh)
-                  ? load_uniform(a.pbt + (int64_t(iw.b) * a.num_decoders + iw.pn) * a.pbt_stride + iw.pp)
-                  : load_uniform(a.bt + int64_t(iw.b) * a.bt_stride + iw.page);
+    int pid = page_id<MODE>(a, iw);
     const bool ok = pid >= 0 && pid < num_pages;
     bad = ok ? (bad & ~(1u << slot)) : (bad | (1u << slot));
     if (!ok) {
@@ -322,13 +394,13 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + s * 64 + lane),
                                        (__attribute__((address_space(3))) void*)(&ring[wave][slot][s * 64]),
                                        16, 0, 0);
-    advance<PRIV>(a, iw, cum_s, B);
+    advance<MODE>(a, iw, cum_s, B);
   };
 
   QFrag<D, NB> qf;
   RowState<D, NB> st;
   st.init();
-  load_q<D, NB>(qf, a, cw.b, cw.gr / RGs, cw.gr % RGs, lane);
+  load_q<D, NB, MODE>(qf, a, cw.b, cw.gr / RGs, cw.gr % RGs, lane);
   __builtin_amdgcn_s_waitcnt(0);
   int64_t unit_begin = int64_t(cw.gr) * Ptot + cum_s[cw.b];  // first tile of the current unit
 
@@ -350,14 +422,14 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       for (int i = 0; i < D / 16; ++i) vf[i] = v2[2 * v_run(D, i, lane >> 5, lane & 15) + ((lane >> 4) & 1)];
       int lim[NB], nvalid;
       bool masked;
-      if (PRIV && cw.page >= cw.nsh) {
-        // a private page of decoder pn: only its rows see it
+      if (MODE != kPlain && cw.page >= cw.nsh) {
+        // a page of owner pn: only its rows see it
         nvalid = min(kPage, cw.plen - cw.pp * kPage);
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) lim[cb] = (row_dec[cb] == cw.pn) ? nvalid : 0;
+        for (int cb = 0; cb < NB; ++cb) lim[cb] = (row_owner[cb] == cw.pn) ? nvalid : 0;
         masked = true;
       } else {
-        const int L = clamp_len(load_uniform(a.seq_lens + cw.b), a.max_seq_len);
+        const int L = seq_len(a, MODE == kCascade ? unit_first(a, cw.b) : cw.b);
         nvalid = min(kPage, L - cw.page * kPage);
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) lim[cb] = nvalid;
@@ -366,20 +438,20 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       attend_page<D, NB>(st, qf, kf, vf, a.scale_log2, masked, lim, nvalid, lane);
     }
     const int cur_gr = cw.gr, cur_b = cw.b;
-    advance<PRIV>(a, cw, cum_s, B);
+    advance<MODE>(a, cw, cum_s, B);
     const bool last = (j == n - 1);
     if (last || cw.gr != cur_gr || cw.b != cur_b) {
       // unit (cur_gr, cur_b) ends here for this wave
       const int64_t unit_end = unit_begin + (cum_s[cur_b + 1] - cum_s[cur_b]);
       const bool before = unit_begin < tau0, after = unit_end > tau1;
       if (!before && !after) {
-        write_rows<D, NB>(a, st, cur_b, cur_gr / RGs, cur_gr % RGs, lane);
+        write_rows<D, NB, MODE>(a, st, cur_b, cur_gr / RGs, cur_gr % RGs, lane);
       } else {
         write_partial<D, NB>(a, st, k * 2 + (before ? 0 : 1), lane);
       }
       if (!last) {
         st.init();
-        load_q<D, NB>(qf, a, cw.b, cw.gr / RGs, cw.gr % RGs, lane);
+        load_q<D, NB, MODE>(qf, a, cw.b, cw.gr / RGs, cw.gr % RGs, lane);
         __builtin_amdgcn_s_waitcnt(0);  // stores and q loads drained before the ring resumes
         unit_begin = int64_t(cw.gr) * Ptot + cum_s[cw.b];
       }
@@ -389,28 +461,27 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
 
 // Merge the partial states of units that cross share boundaries:
 // m* = max m_s, out = sum_s 2^(m_s - m*) acc_s / sum_s 2^(m_s - m*) l_s.
-// Also writes zeros for empty sessions (softmax over nothing).  One thread per
+// Also writes zeros for empty units (softmax over nothing).  One thread per
 // (row, 4 head dims), all loads of a pass issued before any is used, so a unit
 // costs about two memory round trips.
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
-  const int B = a.batch, Hkv = a.pool.num_kv_heads, RGs = a.plan.rowgroups;
-  const int unit = blockIdx.x;  // (gr, b) with b fastest
-  const int b = unit % B, gr = unit / B;
+  const int Hkv = a.pool.num_kv_heads, RGs = a.plan.rowgroups;
+  const int B = MODE == kCascade ? load_uniform(a.ws_units + 3 * a.batch) : a.batch;
+  const int unit = blockIdx.x;  // (gr, b) with b fastest, over the launch's batch
+  const int b = unit % a.batch, gr = unit / a.batch;
+  if (b >= B) return;
   const int g = gr / RGs, rg = gr % RGs;
   const int RG = a.plan.rg_rows;
-  const int G = a.num_q_heads / Hkv;
   const int Ptot = load_uniform(a.ws_cum + B);
   const int cb0 = load_uniform(a.ws_cum + b);
   const int npg = load_uniform(a.ws_cum + b + 1) - cb0;
   const int W = a.plan.blocks * kWaves;
   if (npg == 0) {
     for (int e = threadIdx.x; e < RG * (D / 8); e += blockDim.x) {
-      const int r = rg * RG + e / (D / 8);
-      if (r >= a.plan.rows) continue;
-      const int n = r / G, h = g * G + r % G;
-      uint16_t* o = a.out + ((int64_t(b) * a.num_decoders + n) * a.num_q_heads + h) * D;
-      reinterpret_cast<u32x4*>(o)[e % (D / 8)] = u32x4{0u, 0u, 0u, 0u};
+      const int64_t row = unit_row<MODE>(a, b, g, rg * RG + e / (D / 8));
+      if (row < 0) continue;
+      reinterpret_cast<u32x4*>(a.out + row * D)[e % (D / 8)] = u32x4{0u, 0u, 0u, 0u};
     }
     return;
   }
@@ -425,8 +496,8 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
   const float* __restrict__ accp = a.ws_acc;
   for (int e = threadIdx.x; e < RG * (D / 4); e += blockDim.x) {
     const int rl = e / (D / 4), d4 = e % (D / 4);
-    const int r = rg * RG + rl;
-    if (r >= a.plan.rows) continue;
+    const int64_t row = unit_row<MODE>(a, b, g, rg * RG + rl);
+    if (row < 0) continue;
     // slot of share k: its "started before" slot (0) except the first share (1)
     float M = -INFINITY;
 #pragma unroll 8
@@ -446,25 +517,177 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
       num += w * as;
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    const int n = r / G, h = g * G + r % G;
-    uint16_t* o = a.out + ((int64_t(b) * a.num_decoders + n) * a.num_q_heads + h) * D;
-    reinterpret_cast<u32x2*>(o)[d4] = pack_bf16x4(num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
+    reinterpret_cast<u32x2*>(a.out + row * D)[d4] =
+        pack_bf16x4(num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
   }
 }
 
-template <int D, int NB>
-hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+// Inclusive scan (op = + or max) of one value per thread over a 1024-thread
+// workgroup.  On return buf[t] holds thread t's inclusive value.
+template <bool MAX>
+__device__ __forceinline__ int block_scan(int x, int* buf) {
+  const int tid = threadIdx.x;
+  buf[tid] = x;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int t = tid >= off ? buf[tid - off] : (MAX ? INT_MIN : 0);
+    __syncthreads();
+    x = MAX ? max(x, t) : x + t;
+    buf[tid] = x;
+    __syncthreads();
+  }
+  return x;
+}
+
+// Cascade plan.  Sessions with equal, non-negative group ids that are adjacent in
+// the batch share their first group_prefix[b] pages.  Runs of such sessions are
+// cut into units of at most `per_unit` sessions (all rows of a unit fit one
+// wave); each unit gets its first session, session count, common prefix pages
+// and its tile count (the prefix once, then every session's pages past it).
+// One workgroup of 1024 threads, 4 sessions per thread (batch <= 4096).
+// Flags: members whose group_prefix differs from the unit's first session's
+// (BAD_LEN), and shared-prefix block-table entries that differ from the first
+// session's (BAD_PAGE); the prefix read is always the first session's.
+__global__ __launch_bounds__(1024) void decode_cascade_plan_kernel(DecodeArgs a, int per_unit) {
+  constexpr int E = 4;
+  __shared__ int buf[1024];
+  __shared__ int gid_s[kDecodeMaxBatch];
+  __shared__ int ui_s[kDecodeMaxBatch];
+  __shared__ int first_s[kDecodeMaxBatch];
+  __shared__ int pref_s[kDecodeMaxBatch];
+  __shared__ int voff_s[kDecodeMaxBatch + 1];
+  const int B = a.batch, tid = threadIdx.x;
+  int L[E], us[E];
+  for (int i = 0; i < E; ++i) {
+    const int b = tid * E + i;
+    if (b < B) gid_s[b] = a.group_id[b];
+    L[i] = b < B ? clamp_len(a.seq_lens[b], a.max_seq_len) : 0;
+  }
+  __syncthreads();
+  // 1. run starts (a run: adjacent sessions of one non-negative group id)
+  int rs[E], loc = INT_MIN;
+  for (int i = 0; i < E; ++i) {
+    const int b = tid * E + i;
+    const bool start = b < B && (b == 0 || gid_s[b] < 0 || gid_s[b] != gid_s[b - 1]);
+    if (start) loc = b;
+    rs[i] = loc;
+  }
+  block_scan<true>(loc, buf);
+  const int carry = tid > 0 ? buf[tid - 1] : INT_MIN;
+  __syncthreads();
+  // 2. unit starts and unit indices
+  int cnt = 0;
+  for (int i = 0; i < E; ++i) {
+    const int b = tid * E + i;
+    const int r = max(rs[i], carry);
+    us[i] = (b < B && (b - r) % per_unit == 0) ? 1 : 0;
+    cnt += us[i];
+  }
+  const int incl = block_scan<false>(cnt, buf);
+  const int nu = buf[1023];
+  __syncthreads();
+  {
+    int run = incl - cnt;
+    for (int i = 0; i < E; ++i) {
+      const int b = tid * E + i;
+      run += us[i];
+      if (b < B) ui_s[b] = run - 1;
+      if (us[i]) first_s[run - 1] = b;
+    }
+  }
+  __syncthreads();
+  // 3. per unit: session count and common prefix pages
+  for (int i = 0; i < E; ++i) {
+    if (!us[i]) continue;
+    const int b = tid * E + i, u = ui_s[b];
+    const int count = (u + 1 < nu ? first_s[u + 1] : B) - b;
+    const int claim = gid_s[b] < 0 ? 0 : a.group_prefix[b];
+    int P = max(0, min(claim, L[i] / kPage));
+    for (int m = b + 1; m < b + count; ++m) {
+      if (a.group_prefix[m] != claim) flag_error(a.dev_status, KVS_DEV_BAD_LEN_BIT);
+      P = min(P, clamp_len(a.seq_lens[m], a.max_seq_len) / kPage);
+    }
+    pref_s[u] = P;
+    a.ws_units[u] = b;
+    a.ws_units[B + u] = count;
+    a.ws_units[2 * B + u] = P;
+  }
+  __syncthreads();
+  // 4. tiles per unit: the prefix once, then every session's pages past it
+  int c = 0, v = 0, cl[E], vl[E];
+  for (int i = 0; i < E; ++i) {
+    const int b = tid * E + i;
+    const int P = b < B ? pref_s[ui_s[b]] : 0;
+    cl[i] = b < B ? (L[i] + kPage - 1) / kPage - (us[i] ? 0 : P) : 0;
+    vl[i] = (b < B && !us[i]) ? P : 0;
+    c += cl[i];
+    v += vl[i];
+  }
+  const int incl_c = block_scan<false>(c, buf);
+  const int total = buf[1023];
+  __syncthreads();
+  {
+    int run = incl_c - c;
+    for (int i = 0; i < E; ++i) {
+      if (us[i]) a.ws_cum[ui_s[tid * E + i]] = run;
+      run += cl[i];
+    }
+  }
+  if (tid == 0) {
+    a.ws_cum[nu] = total;
+    a.ws_units[3 * B] = nu;
+  }
+  // 5. check the shared-prefix entries of every non-first session
+  const int incl_v = block_scan<false>(v, buf);
+  const int nv = buf[1023];
+  {
+    int run = incl_v - v;
+    for (int i = 0; i < E; ++i) {
+      const int b = tid * E + i;
+      if (b < B) voff_s[b] = run;
+      run += vl[i];
+    }
+    if (tid == 0) voff_s[B] = nv;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < nv; idx += 1024) {
+    int lo = 0, hi = B;  // largest b with voff_s[b] <= idx
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (voff_s[mid] <= idx) lo = mid;
+      else hi = mid;
+    }
+    const int p = idx - voff_s[lo];
+    const int f = first_s[ui_s[lo]];
+    if (a.bt[int64_t(lo) * a.bt_stride + p] != a.bt[int64_t(f) * a.bt_stride + p])
+      flag_error(a.dev_status, KVS_DEV_BAD_PAGE_BIT);
+  }
+}
+
+template <int D, int NB, int MODE>
+hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
   constexpr int S = D == 128 ? 4 : 8;  // 32 KiB of ring per wave
-  if (a.pbt)
-    hipLaunchKernelGGL((decode_stream_kernel<D, NB, S, true>), dim3(a.plan.blocks), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_stream_kernel<D, NB, S, false>), dim3(a.plan.blocks), dim3(256), 0, stream, a);
+  if (MODE == kCascade) {
+    const int G = a.num_q_heads / a.pool.num_kv_heads;
+    hipLaunchKernelGGL(decode_cascade_plan_kernel, dim3(1), dim3(1024), 0, stream, a,
+                       a.plan.rows / (a.num_decoders * G));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((decode_stream_kernel<D, NB, S, MODE>), dim3(a.plan.blocks), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units = a.pool.num_kv_heads * a.plan.rowgroups * a.batch;
   const int threads = min(1024, a.plan.rg_rows * (D / 4));
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(units), dim3(threads), 0, stream, a);
+  hipLaunchKernelGGL((decode_combine_kernel<D, MODE>), dim3(units), dim3(threads), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D, int NB>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  if (a.group_id) return launch_decode_mode<D, NB, kCascade>(a, stream);
+  if (a.pbt) return launch_decode_mode<D, NB, kPrivate>(a, stream);
+  return launch_decode_mode<D, NB, kPlain>(a, stream);
 }
 
 }  // namespace

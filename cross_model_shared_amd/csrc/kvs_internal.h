@@ -38,7 +38,7 @@ struct DecodePlan {
   int rg_rows;    // 16 * nb
   int rowgroups;  // ceil(rows / rg_rows)
   int blocks;     // workgroups of the persistent grid (one per CU)
-  size_t cum_offset, ml_offset, acc_offset, bytes;
+  size_t cum_offset, units_offset, ml_offset, acc_offset, bytes;
 };
 
 DecodePlan plan_decode(int batch, int num_decoders, int num_q_heads, int num_kv_heads, int head_dim,
@@ -61,6 +61,11 @@ struct DecodeArgs {
   int pbt_stride;
   const int32_t* plens;
   int max_priv_len;
+  // cascade (all null for the other calls): sessions with equal non-negative
+  // group_id adjacent in the batch share their first group_prefix[b] pages
+  const int32_t* group_id;
+  const int32_t* group_prefix;
+  int* ws_units;  // [3*batch+1] cascade units: first session, count, prefix pages; unit count
   int* ws_cum;    // [batch+1] page prefix sum, written by the decode kernel
   float* ws_ml;   // [4*blocks*2][rg_rows][2] partial (m, l)
   float* ws_acc;  // [4*blocks*2][rg_rows][D] partial acc

@@ -75,12 +75,15 @@ DecodePlan plan_decode(int batch, int num_decoders, int num_q_heads, int num_kv_
   p.rg_rows = 16 * p.nb;
   p.rowgroups = (p.rows + p.rg_rows - 1) / p.rg_rows;
   p.blocks = kDecodeBlocks;
-  const size_t slots = size_t(p.blocks) * 4 * 2;
+  // partial-state slots sized for 64-row groups, so one workspace serves every
+  // decode call with these bounds (a cascade unit may hold up to 64 rows)
+  const size_t slots = size_t(p.blocks) * 4 * 2, slot_rows = 64;
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };
   p.cum_offset = 0;
-  p.ml_offset = align(size_t(batch + 1) * sizeof(int));
-  p.acc_offset = p.ml_offset + align(slots * p.rg_rows * 2 * sizeof(float));
-  p.bytes = p.acc_offset + slots * p.rg_rows * head_dim * sizeof(float);
+  p.units_offset = align(size_t(batch + 1) * sizeof(int));
+  p.ml_offset = p.units_offset + align(size_t(3 * batch + 1) * sizeof(int));
+  p.acc_offset = p.ml_offset + align(slots * slot_rows * 2 * sizeof(float));
+  p.bytes = p.acc_offset + slots * slot_rows * head_dim * sizeof(float);
   return p;
 }
 
@@ -134,10 +137,10 @@ namespace {
 
 int decode_common(const char* name, const kvs_pool* pool, int32_t layer, const void* q, void* out,
                   const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
-                  const int32_t* pbt, int32_t pbt_stride, const int32_t* plens, int32_t batch,
-                  int32_t num_decoders, int32_t num_q_heads, int32_t max_seq_len, int32_t max_priv_len,
-                  float scale, void* workspace, size_t workspace_bytes, int32_t* dev_status,
-                  hipStream_t stream) {
+                  const int32_t* pbt, int32_t pbt_stride, const int32_t* plens, const int32_t* group_id,
+                  const int32_t* group_prefix, int32_t batch, int32_t num_decoders, int32_t num_q_heads,
+                  int32_t max_seq_len, int32_t max_priv_len, float scale, void* workspace,
+                  size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
   int s = check_pool(pool, layer);
   if (s) return s;
   if (!q || !out || !block_table || !seq_lens) return fail(KVS_EINVAL, "%s: a required pointer is NULL", name);
@@ -153,6 +156,22 @@ int decode_common(const char* name, const kvs_pool* pool, int32_t layer, const v
     return fail(KVS_EUNSUPPORTED, "%s: batch %d above %d", name, batch, kvs::kDecodeMaxBatch);
   kvs::DecodePlan plan = kvs::plan_decode(batch, num_decoders, num_q_heads, pool->num_kv_heads,
                                           pool->head_dim, max_seq_len);
+  if (group_id) {
+    // a unit holds as many whole sessions as fit 64 rows (at least one)
+    const int ng = num_decoders * (num_q_heads / pool->num_kv_heads);
+    if (ng > 64)
+      return fail(KVS_EUNSUPPORTED, "%s: %d query rows per KV head and session (num_decoders * group) above 64",
+                  name, ng);
+    const int per_unit = 64 / ng;
+    kvs::DecodePlan full = kvs::plan_decode(batch, per_unit * num_decoders, num_q_heads, pool->num_kv_heads,
+                                            pool->head_dim, max_seq_len);
+    full.bytes = plan.bytes;  // same workspace layout and size
+    full.cum_offset = plan.cum_offset;
+    full.units_offset = plan.units_offset;
+    full.ml_offset = plan.ml_offset;
+    full.acc_offset = plan.acc_offset;
+    plan = full;
+  }
   if (pbt) {
     if (pbt_stride <= 0) return fail(KVS_EINVAL, "%s: priv_bt_stride %d must be positive", name, pbt_stride);
     if (max_priv_len < 0) return fail(KVS_EINVAL, "%s: max_priv_len %d is negative", name, max_priv_len);
@@ -169,8 +188,8 @@ int decode_common(const char* name, const kvs_pool* pool, int32_t layer, const v
   char* ws = static_cast<char*>(workspace);
   kvs::DecodeArgs a{view(pool), layer, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
                     block_table, bt_stride, seq_lens, batch, num_decoders, num_q_heads, max_seq_len,
-                    scale * 1.4426950408889634f, pbt, pbt_stride, plens, max_priv_len,
-                    reinterpret_cast<int*>(ws + plan.cum_offset),
+                    scale * 1.4426950408889634f, pbt, pbt_stride, plens, max_priv_len, group_id, group_prefix,
+                    reinterpret_cast<int*>(ws + plan.units_offset), reinterpret_cast<int*>(ws + plan.cum_offset),
                     reinterpret_cast<float*>(ws + plan.ml_offset),
                     reinterpret_cast<float*>(ws + plan.acc_offset), plan, dev_status};
   return launched(kvs::launch_decode(a, stream), name);
@@ -186,8 +205,8 @@ int shared_kv_decode(const kvs_pool* pool, int32_t layer, const void* q, void* o
                      float scale, void* workspace, size_t workspace_bytes, int32_t* dev_status,
                      hipStream_t stream) {
   return decode_common("shared_kv_decode", pool, layer, q, out, block_table, bt_stride, seq_lens, nullptr, 0,
-                       nullptr, batch, num_decoders, num_q_heads, max_seq_len, 0, scale, workspace,
-                       workspace_bytes, dev_status, stream);
+                       nullptr, nullptr, nullptr, batch, num_decoders, num_q_heads, max_seq_len, 0, scale,
+                       workspace, workspace_bytes, dev_status, stream);
 }
 
 int shared_kv_decode_private(const kvs_pool* pool, int32_t layer, const void* q, void* out,
@@ -200,8 +219,22 @@ int shared_kv_decode_private(const kvs_pool* pool, int32_t layer, const void* q,
   if (!priv_block_table || !priv_lens)
     return fail(KVS_EINVAL, "shared_kv_decode_private: a required pointer is NULL");
   return decode_common("shared_kv_decode_private", pool, layer, q, out, block_table, bt_stride, seq_lens,
-                       priv_block_table, priv_bt_stride, priv_lens, batch, num_decoders, num_q_heads,
-                       max_seq_len, max_priv_len, scale, workspace, workspace_bytes, dev_status, stream);
+                       priv_block_table, priv_bt_stride, priv_lens, nullptr, nullptr, batch, num_decoders,
+                       num_q_heads, max_seq_len, max_priv_len, scale, workspace, workspace_bytes, dev_status,
+                       stream);
+}
+
+int shared_kv_decode_cascade(const kvs_pool* pool, int32_t layer, const void* q, void* out,
+                             const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                             const int32_t* group_id, const int32_t* group_prefix_pages, int32_t batch,
+                             int32_t num_decoders, int32_t num_q_heads, int32_t max_seq_len, float scale,
+                             void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                             hipStream_t stream) {
+  if (!group_id || !group_prefix_pages)
+    return fail(KVS_EINVAL, "shared_kv_decode_cascade: a required pointer is NULL");
+  return decode_common("shared_kv_decode_cascade", pool, layer, q, out, block_table, bt_stride, seq_lens,
+                       nullptr, 0, nullptr, group_id, group_prefix_pages, batch, num_decoders, num_q_heads,
+                       max_seq_len, 0, scale, workspace, workspace_bytes, dev_status, stream);
 }
 
 int partial_prefill_extend(const kvs_pool* pool, int32_t layer, const void* q, const void* k_new,

@@ -163,6 +163,43 @@ def build_private_tables(lens, priv_lens, seed: int, spare_frac: float = 0.02):
     return allbt[:B, :s1].copy(), allbt[B:, :s2].copy(), num_pages
 
 
+def build_prefix_groups(groups, seed: int, spare_frac: float = 0.02):
+    """Block tables for sessions that share block-aligned prefixes, as a prefix
+    cache hands them out: every session of a group starts with the same physical
+    pages for the group's prefix, then has pages of its own.
+
+    groups: list of (prefix_tokens, [session lengths]) with prefix_tokens a
+    multiple of 16 and every length >= prefix_tokens.  Returns (block_table int32
+    [B, S], lens, group_id int32 [B], prefix_pages int32 [B], num_pages); sessions
+    are numbered group by group, so each group's sessions are adjacent.
+    """
+    need = 0
+    for pre, lens in groups:
+        if pre % PAGE or any(L < pre for L in lens):
+            raise ValueError("prefixes must be whole pages and no longer than their sessions")
+        need += pre // PAGE + sum((L + PAGE - 1) // PAGE - pre // PAGE for L in lens)
+    spares = max(3, int(math.ceil(need * spare_frac)))
+    num_pages = need + spares
+    perm = _rng(seed, 2).permutation(num_pages).astype(np.int32)
+    lens_all = [L for _, lens in groups for L in lens]
+    stride = max(max((L + PAGE - 1) // PAGE for L in lens_all), 1)
+    bt = np.full((len(lens_all), stride), -1, dtype=np.int32)
+    gid = np.zeros(len(lens_all), np.int32)
+    pref = np.zeros(len(lens_all), np.int32)
+    pos, b = 0, 0
+    for g, (pre, lens) in enumerate(groups):
+        shared = perm[pos:pos + pre // PAGE]
+        pos += pre // PAGE
+        for L in lens:
+            own = (L + PAGE - 1) // PAGE - pre // PAGE
+            bt[b, :pre // PAGE] = shared
+            bt[b, pre // PAGE:pre // PAGE + own] = perm[pos:pos + own]
+            pos += own
+            gid[b], pref[b] = g, pre // PAGE
+            b += 1
+    return bt, lens_all, gid, pref, num_pages
+
+
 # ---------------------------------------------------------------------------
 # bf16 draws (float32 normal -> bf16 round-to-nearest-even), as raw uint16 bits
 # ---------------------------------------------------------------------------

@@ -16,6 +16,7 @@
  *   kv_pool_append         write new K/V rows into pages        (the cache "store")
  *   shared_kv_decode       N decoders x G GQA heads, one KV read (decode attention)
  *   shared_kv_decode_private  the same over a shared prefix + per-decoder private suffixes
+ *   shared_kv_decode_cascade  the same where sessions share prefix pages, each prefix read once
  *   kv_pages_pack / kv_pages_unpack   pages <-> contiguous transfer buffer (cache handoff)
  *   kv_pool_fetch          logical K/V rows back out of the pool (inverse of kv_pool_append)
  *   partial_prefill_extend append a chunk, then causal attention of the chunk
@@ -137,7 +138,8 @@ int kv_pool_append(const kvs_pool* pool, int32_t layer, const void* k_new, const
                    const int32_t* seq_lens, int32_t batch, int32_t total_new, int32_t max_new,
                    int32_t max_seq_len, int32_t* dev_status, hipStream_t stream);
 
-/* Workspace bytes needed by shared_kv_decode for these bounds. */
+/* Workspace bytes needed by shared_kv_decode, shared_kv_decode_private and
+ * shared_kv_decode_cascade for these bounds. */
 size_t shared_kv_decode_workspace_bytes(int32_t batch, int32_t num_decoders, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t max_seq_len);
@@ -203,6 +205,38 @@ int shared_kv_decode_private(const kvs_pool* pool, int32_t layer, const void* q,
                              int32_t num_q_heads, int32_t max_seq_len, int32_t max_priv_len,
                              float scale, void* workspace, size_t workspace_bytes,
                              int32_t* dev_status, hipStream_t stream);
+
+/*
+ * shared_kv_decode_cascade — shared_kv_decode for sessions that share prefix
+ * pages: the same result, with each shared prefix read once per group.
+ *
+ * Prefill-as-a-Service, component 3 (hybrid prefix cache pool): prefix-cache
+ * blocks are reused across requests when they are block-aligned and full, so
+ * every session with the same prefix gets the same physical pages (block-table
+ * rows of those sessions start with equal entries).  Sessions b with equal,
+ * non-negative group_id[b] that are adjacent in the batch form a group sharing
+ * their first group_prefix_pages[b] pages (the same value for all members);
+ * group_id[b] < 0 means no sharing.  Each group is read in units of up to
+ * 64 / (num_decoders * G) sessions: the common prefix pages are streamed once
+ * for all the unit's query rows, then each session's remaining pages for its own
+ * rows.  Outputs equal shared_kv_decode's over the same block tables (to
+ * rounding: the work is split differently).
+ *
+ *  group_id, group_prefix_pages  int32 [batch], device.  A member whose
+ *                prefix page count differs from its unit's first session, or
+ *                whose block-table entries for the prefix differ from the first
+ *                session's, is reported (KVS_DEV_BAD_LEN / KVS_DEV_BAD_PAGE);
+ *                the prefix pages read are always the first session's.  The
+ *                prefix is also cut to whole pages every member holds.
+ *  Needs num_decoders * (num_q_heads / num_kv_heads) <= 64.  Other arguments
+ *  and the workspace as for shared_kv_decode.
+ */
+int shared_kv_decode_cascade(const kvs_pool* pool, int32_t layer, const void* q, void* out,
+                             const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                             const int32_t* group_id, const int32_t* group_prefix_pages, int32_t batch,
+                             int32_t num_decoders, int32_t num_q_heads, int32_t max_seq_len, float scale,
+                             void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                             hipStream_t stream);
 
 /*
  * partial_prefill_extend — cached-prefix extension over the new tokens only.

@@ -32,7 +32,8 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol(L):
     names = header_functions()
-    assert {"kv_pool_append", "shared_kv_decode", "shared_kv_decode_private", "partial_prefill_extend",
+    assert {"kv_pool_append", "shared_kv_decode", "shared_kv_decode_private", "shared_kv_decode_cascade",
+            "partial_prefill_extend",
             "kv_pages_pack", "kv_pages_unpack", "kv_pages_buffer_bytes", "kv_pool_fetch", "kvs_pool_bytes",
             "shared_kv_decode_workspace_bytes", "kvs_last_error", "kvs_version"} <= set(names)
     for n in names:
@@ -110,6 +111,21 @@ def call_decode_private(L, p, q=FAKE, bt=FAKE, pbt=FAKE, pstride=2, plens=FAKE, 
 def test_decode_private_host_checks(L, kw, status):
     p = kw.pop("p")
     assert call_decode_private(L, p, **kw) == status
+    assert binding.last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(gid=None), binding.KVS_EINVAL),
+    (dict(pref=None), binding.KVS_EINVAL),
+    (dict(N=17), binding.KVS_EUNSUPPORTED),           # 17 decoders x 4 heads per KV head > 64 rows
+    (dict(msl=65), binding.KVS_ERANGE),
+    (dict(wsb=16), binding.KVS_EWORKSPACE),
+])
+def test_decode_cascade_host_checks(L, kw, status):
+    a = dict(gid=FAKE, pref=FAKE, N=2, msl=64, wsb=1 << 30)
+    a.update(kw)
+    assert L.shared_kv_decode_cascade(ctypes.byref(pool()), 0, FAKE, FAKE, FAKE, 4, FAKE, a["gid"], a["pref"], 2,
+                                      a["N"], 8, a["msl"], 0.125, FAKE, a["wsb"], None, None) == status
     assert binding.last_error()
 
 

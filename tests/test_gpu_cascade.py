@@ -1,0 +1,121 @@
+"""GPU parity of shared_kv_decode_cascade: sessions that a prefix cache gave the
+same prefix pages (Prefill-as-a-Service, component 3) decode with each shared
+prefix read once per unit of sessions.  The result is shared_kv_decode's: the
+float64 oracle's page walk over the same (aliasing) block tables, within 2e-2."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from cross_model_shared_amd import binding
+from cross_model_shared_amd import workload as wlmod
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+
+
+def make_case(groups, N, Hkv, G, D, seed):
+    """GPU pool holding grouped sessions: each group's prefix written once, then each
+    session's own tokens; logical K/V per session kept for the oracle."""
+    rng = np.random.default_rng(seed)
+    bt, lens, gid, pref, num_pages = wlmod.build_prefix_groups(groups, seed)
+    pool = binding.Pool(1, num_pages, Hkv, D, fill=np.int16(np.uint16(gu.POISON_NAN).view(np.int16)))
+    st = gu.status_tensor()
+    K, V, b = [], [], 0
+    msl = max(max(lens), 1)
+    for pre, ls in groups:
+        pk, pv = wlmod.draw_bf16(rng, (pre, Hkv, D), 1.0), wlmod.draw_bf16(rng, (pre, Hkv, D), 1.0)
+        for i, L in enumerate(ls):
+            ok, ov = wlmod.draw_bf16(rng, (L - pre, Hkv, D), 1.0), wlmod.draw_bf16(rng, (L - pre, Hkv, D), 1.0)
+            K.append(np.concatenate([pk, ok]))
+            V.append(np.concatenate([pv, ov]))
+            row = gu.dev_i32(bt[b:b + 1])
+            if i == 0 and pre:
+                binding.append(pool, 0, gu.dev_bf16(pk), gu.dev_bf16(pv), gu.dev_i32([0, pre]), row,
+                               gu.dev_i32([0]), max_new=msl, max_seq_len=msl, dev_status=st)
+            if L > pre:
+                binding.append(pool, 0, gu.dev_bf16(ok), gu.dev_bf16(ov), gu.dev_i32([0, L - pre]), row,
+                               gu.dev_i32([pre]), max_new=msl, max_seq_len=msl, dev_status=st)
+            b += 1
+    q = wlmod.draw_bf16(rng, (len(lens), N, Hkv * G, D), 1.0)
+    return dict(pool=pool, bt=bt, lens=lens, gid=gid, pref=pref, K=K, V=V, q=q, status=st, Hkv=Hkv, D=D,
+                num_pages=num_pages, layer=0)
+
+
+def run_cascade(c, gid=None, pref=None, bt=None):
+    import torch
+
+    B, N, Hq, D = c["q"].shape
+    msl = max(max(c["lens"]), 1)
+    ws = gu.nan_workspace(binding.decode_workspace_bytes(B, N, Hq, c["Hkv"], D, msl))
+    out = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device="cuda")
+    binding.decode_cascade(c["pool"], 0, gu.dev_bf16(c["q"]), out, gu.dev_i32(c["bt"] if bt is None else bt),
+                           gu.dev_i32(c["lens"]), gu.dev_i32(c["gid"] if gid is None else gid),
+                           gu.dev_i32(c["pref"] if pref is None else pref), msl, 1.0 / math.sqrt(D), ws,
+                           dev_status=c["status"])
+    gu.sync()
+    return out
+
+
+@pytest.mark.parametrize("groups,N,G,D", [
+    ([(64, [100, 64, 300]), (0, [17]), (32, [33, 48])], 8, 4, 128),       # 2 sessions per unit
+    ([(512, [512 + 7 * i for i in range(7)])], 2, 4, 64),                    # 8 per unit: one unit
+    ([(160, [200, 161, 999, 160, 400])], 4, 4, 128),                           # 4 per unit, a second unit
+    ([(48, [60, 70])], 16, 3, 128),                                           # 48 rows: 1 per unit
+    ([(0, [0, 30]), (16, [16]), (32, [32, 90, 33, 35])], 1, 5, 64),
+])
+def test_cascade_matches_oracle(groups, N, G, D):
+    print(f"[cascade] groups={groups} N={N} G={G} D={D}", flush=True)
+    c = make_case(groups, N, 2, G, D, seed=len(groups) * 7 + N + D)
+    out = gu.host_f64(run_cascade(c))
+    want = oracle.decode_from_logical(c["q"], c["K"], c["V"], 1.0 / math.sqrt(D))
+    err = float(np.max(np.abs(out - want)))
+    print(f"[cascade] max-abs err {err:.3e}", flush=True)
+    assert err <= TOL
+    assert int(c["status"].item()) == 0
+
+
+def test_cascade_matches_shared_decode_and_oracle_pool_walk():
+    groups = [(256, [300, 700, 256, 1000]), (0, [40]), (128, [129, 500])]
+    c = make_case(groups, 8, 2, 4, 128, seed=71)
+    casc = gu.host_f64(run_cascade(c))
+    plain = gu.host_f64(gu.run_decode(c, q_bits=c["q"], lens=c["lens"], bt=c["bt"]))
+    assert float(np.max(np.abs(casc - plain))) <= TOL
+    shape = oracle.PoolShape(1, c["num_pages"], 2, 128)
+    want = oracle.decode(gu.pool_bits(c["pool"]), shape, 0, c["q"], c["bt"], c["lens"], 1.0 / math.sqrt(128))
+    assert float(np.max(np.abs(casc - want))) <= TOL
+
+
+def test_no_groups_is_shared_decode():
+    groups = [(0, [100]), (0, [33]), (0, [0]), (0, [400])]
+    c = make_case(groups, 4, 2, 4, 128, seed=72)
+    gid = np.full(4, -1, np.int32)
+    casc = gu.host_f64(run_cascade(c, gid=gid))
+    want = oracle.decode_from_logical(c["q"], c["K"], c["V"], 1.0 / math.sqrt(128))
+    assert float(np.max(np.abs(casc - want))) <= TOL
+
+
+def test_cascade_reports_inconsistent_groups_without_faulting():
+    groups = [(64, [100, 80, 90])]
+    c = make_case(groups, 8, 2, 4, 128, seed=73)
+    pref = c["pref"].copy()
+    pref[1] = 2                                  # claims a shorter prefix than its unit's first session
+    run_cascade(c, pref=pref)
+    assert int(c["status"].item()) & binding.DEV_BAD_LEN
+    c["status"].zero_()
+    bt = c["bt"].copy()
+    bt[1, 0] = bt[0, 3] if bt[0, 3] >= 0 else 0  # a prefix entry that is not the first session's page
+    out = gu.host_f64(run_cascade(c, bt=bt))
+    assert int(c["status"].item()) & binding.DEV_BAD_PAGE
+    assert np.all(np.isfinite(out))

@@ -374,6 +374,33 @@ def test_private_suffix_reaches_only_its_decoder():
     assert not np.allclose(other[:, 1], base[:, 1])
 
 
+def test_sessions_sharing_prefix_pages_read_the_shared_prefix():
+    """Prefill-as-a-Service, component 3: sessions handed the same prefix pages by a
+    prefix cache attend that prefix followed by their own tokens; the oracle's page
+    walk over aliasing block tables matches attention over the logical sequences."""
+    groups = [(32, [40, 32, 70]), (0, [5]), (16, [16, 20])]
+    bt, lens, gid, pref, num_pages = wlmod.build_prefix_groups(groups, 55)
+    Hkv, D, N, G = 2, 64, 2, 2
+    shape = oracle.PoolShape(1, num_pages, Hkv, D)
+    rng = RNG(55)
+    pool = poison_pool(shape)
+    K, V, b = [], [], 0
+    for pre, ls in groups:
+        pk, pv = bits(rng, (pre, Hkv, D)), bits(rng, (pre, Hkv, D))
+        for i, L in enumerate(ls):
+            ok, ov = bits(rng, (L - pre, Hkv, D)), bits(rng, (L - pre, Hkv, D))
+            K.append(np.concatenate([pk, ok]))
+            V.append(np.concatenate([pv, ov]))
+            if i == 0:  # the prefix is written once, through the first session's table
+                pool = oracle.append(pool, shape, 0, pk, pv, [0, pre], bt[b:b + 1], [0])
+            pool = oracle.append(pool, shape, 0, ok, ov, [0, L - pre], bt[b:b + 1], [pre])
+            b += 1
+    q = bits(rng, (len(lens), N, Hkv * G, D))
+    got = oracle.decode(pool, shape, 0, q, bt, lens, 0.125)
+    want = oracle.decode_from_logical(q, K, V, 0.125)
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
 # ---------------------------------------------------------------------------
 # Fetch (the inverse of append) and page handoff between pools
 # ---------------------------------------------------------------------------
