@@ -32,6 +32,7 @@ DECODE_WORKLOAD = "qwen3_8b_n8"
 EXTEND_WORKLOAD = "extend_8k_512"
 PRIVATE_WORKLOAD = "qwen3_8b_n8_private"
 HANDOFF_WORKLOAD = "handoff_8k"
+CASCADE_WORKLOAD = "qwen3_8b_n8_cascade"
 
 
 def log(msg):
@@ -48,6 +49,7 @@ def parse():
     ap.add_argument("--private-calls", type=int, default=20)
     ap.add_argument("--no-private", action="store_true", help="skip the private-suffix decode section")
     ap.add_argument("--no-handoff", action="store_true", help="skip the page handoff section")
+    ap.add_argument("--no-cascade", action="store_true", help="skip the shared-prefix cascade section")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -309,6 +311,72 @@ def private_section(calls):
     return res
 
 
+def cascade_section(calls):
+    """shared_kv_decode_cascade against shared_kv_decode on sessions that share prefix pages."""
+    import torch
+
+    from cross_model_shared_amd import binding
+    from cross_model_shared_amd import workload as W
+
+    wl = W.make_workload(CASCADE_WORKLOAD)
+    B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    bt, lens, gid, pref, num_pages = W.build_prefix_groups(wl.groups, wl.seed)
+    pool = binding.Pool(1, num_pages, Hkv, D)
+    d_bt = torch.from_numpy(bt).cuda()
+    # the pages hold seeded values: each group's prefix written once, then every session's own tokens
+    own = [L - pre for pre, ls in wl.groups for L in ls]
+    first_rows = [b for b in range(B) if b == 0 or gid[b] != gid[b - 1]]
+    pre_tok = [wl.groups[gid[b]][0] for b in first_rows]
+    for i, (rows, lengths, before) in enumerate(((first_rows, pre_tok, [0] * len(first_rows)),
+                                                 (list(range(B)), own, [int(p) * 16 for p in pref]))):
+        total = sum(lengths)
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)).cuda()
+        k = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 50 + 2 * i)).view(total, Hkv, D)
+        v = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 51 + 2 * i)).view(total, Hkv, D)
+        binding.append(pool, 0, k, v, cu, d_bt[rows].contiguous(),
+                       torch.tensor(before, dtype=torch.int32, device="cuda"), max_new=max(max(lengths), 1),
+                       max_seq_len=max(lens))
+        del k, v
+    q = W.device_normal_bf16(B * N * Hq * D, wl.std, W.mix_seed(wl.seed, 54)).view(B, N, Hq, D)
+    out = torch.empty_like(q)
+    maxL = max(lens)
+    ws = torch.zeros(binding.decode_workspace_bytes(B, N, Hq, Hkv, D, maxL), dtype=torch.uint8, device="cuda")
+    d_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    d_gid, d_pref = torch.from_numpy(gid).cuda(), torch.from_numpy(pref).cuda()
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        t = EventTimer()
+        for _ in range(calls):
+            e = t.start()
+            fn()
+            t.stop(e)
+        torch.cuda.synchronize()
+        return float(np.median(t.all_ms()))
+
+    ms_c = timed(lambda: binding.decode_cascade(pool, 0, q, out, d_bt, d_lens, d_gid, d_pref, maxL, wl.scale, ws))
+    ms_p = timed(lambda: binding.decode(pool, 0, q, out, d_bt, d_lens, maxL, wl.scale, ws))
+    # unique KV bytes: every group's prefix once (units of 64 / (N G) = 2 sessions hold whole pairs here)
+    uniq_tokens = sum(pre + sum(L - pre for L in ls) for pre, ls in wl.groups)
+    nbytes = uniq_tokens * Hkv * D * 4 + 2 * B * N * Hq * D * 2 + 4 * (num_pages + 3 * B)
+    gbs = nbytes / (ms_c * 1e-3) / 1e9
+    res = {
+        "workload": f"{CASCADE_WORKLOAD}: 64 sessions in 32 pairs sharing 4K-8K-token prefix pages, own 0-8K "
+                    f"tokens each (sum of session lengths {sum(lens)}, unique tokens {uniq_tokens}), N=8, one layer",
+        "value": round(gbs, 1), "unit": "GB/s (unique KV bytes)", "ms_per_call": round(ms_c, 5),
+        "bytes_per_call": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "shared_kv_decode_ms_same_tables": round(ms_p, 5), "speedup": round(ms_p / ms_c, 3),
+    }
+    log(f"[bench] cascade decode {ms_c * 1e3:.1f} us ({gbs:.0f} GB/s unique), plain {ms_p * 1e3:.1f} us")
+    del pool
+    torch.cuda.empty_cache()
+    return res
+
+
 def handoff_section(reps):
     """kv_pages_pack / kv_pages_unpack of every page of the handoff workload (all 36 layers) and
     kv_pool_fetch of its rows (all layers); HBM bytes = what is read + what is written."""
@@ -507,6 +575,7 @@ def main():
 
     private = None if args.no_private else private_section(args.private_calls)
     handoff = None if args.no_handoff else handoff_section(10)
+    cascade = None if args.no_cascade else cascade_section(20)
 
     res = {
         "metric": "shared-KV decode attn KV GB/s (% HBM peak) at N=8 decoders; extend TFLOP/s",
@@ -541,6 +610,7 @@ def main():
                       "ratio": N},
         "private": private,
         "handoff": handoff,
+        "cascade": cascade,
         "extend": {
             "workload": f"{EXTEND_WORKLOAD}: B=16, cached prefix 8192 + 512 new tokens, 32 q / 8 KV heads, "
                         f"D=128 (partial_prefill_extend = append chunk + causal attention)",

@@ -22,6 +22,9 @@ normal, no trained weights exist here):
                     to [4K, 128K], mean ~27K).
 * handoff_8k      — 4 sessions of 8K tokens, Qwen3-8B-shaped (8 KV heads, D=128),
                     36 layers: the cache a prefill worker hands to a decode worker.
+* qwen3_8b_n8_cascade — Qwen3-8B-shaped N=8 decode of 64 sessions in 32 pairs;
+                    each pair shares a prefix-cached prefix of 4K-8K tokens (whole
+                    pages), and each session adds 0-8K tokens of its own.
 * qwen3_8b_n8_private — qwen3_8b_n8's sessions and shared prefixes, plus a
                     private suffix per decoder (its own generated tokens),
                     lengths uniform in [0, 2048].
@@ -54,6 +57,7 @@ class Workload:
     prefix: list = field(default_factory=list)    # extend: cached prefix
     new: list = field(default_factory=list)       # extend: new chunk sizes
     priv: list = field(default_factory=list)      # decode: private suffix of decoder n of session b at b*N + n
+    groups: list = field(default_factory=list)    # decode: (shared prefix tokens, [session lengths]) per group
 
     @property
     def group(self) -> int:
@@ -105,6 +109,15 @@ def make_workload(name: str, seed: int | None = None) -> Workload:
         priv = [int(x) for x in r.integers(0, 2048, size=base.batch * base.num_decoders, endpoint=True)]
         return Workload(name, base.batch, base.num_decoders, base.num_q_heads, base.num_kv_heads,
                         base.head_dim, 1, base.std, s, "decode", lens=base.lens, priv=priv)
+    if name == "qwen3_8b_n8_cascade":
+        s = 6 if seed is None else seed
+        r = _rng(s, 0)
+        groups = []
+        for _ in range(32):
+            pre = int(r.integers(256, 512, endpoint=True)) * PAGE
+            groups.append((pre, [pre + int(x) for x in r.integers(0, 8192, size=2, endpoint=True)]))
+        lens = [L for _, ls in groups for L in ls]
+        return Workload(name, 64, 8, 32, 8, 128, 1, 1.0, s, "decode", lens=lens, groups=groups)
     if name == "handoff_8k":
         s = 5 if seed is None else seed
         return Workload(name, 4, 1, 32, 8, 128, 36, 1.0, s, "decode", lens=[8192] * 4)
@@ -121,7 +134,7 @@ def make_workload(name: str, seed: int | None = None) -> Workload:
 
 
 WORKLOADS = ("tiny", "llama8b_n4", "qwen3_8b_n8", "extend_8k_512", "qwen3_14b_long", "qwen3_8b_n8_private",
-             "handoff_8k")
+             "handoff_8k", "qwen3_8b_n8_cascade")
 
 
 # ---------------------------------------------------------------------------
