@@ -29,7 +29,9 @@
 // session with that prefix) are grouped into units of up to 64 / (N*G)
 // sessions by decode_cascade_plan_kernel; a unit's tile list is the common
 // prefix pages, read once for all its sessions' rows, followed by each
-// session's own remaining pages for that session's rows.
+// session's own remaining pages for that session's rows.  Those units run on
+// wave pairs (decode_pair_kernel): 32 rows per wave keeps two waves per SIMD,
+// which a 64-row wave's registers would not allow.
 #include <limits.h>
 
 #include "attn_core.h"
@@ -149,31 +151,40 @@ __device__ __forceinline__ void enter_page(const DecodeArgs& a, Walker& w) {
   else if (++w.pp == w.pnpg) first_owner<MODE>(a, w, w.pn + 1);
 }
 
-__device__ __forceinline__ int read_cum(const int* cum, int i) {
-  return __builtin_amdgcn_readfirstlane(cum[i]);
-}
+// Page prefix sum over units: in LDS (plain and private, each workgroup builds
+// it) or in the workspace (cascade, built by the plan kernel; scalar loads, so
+// the LDS ring's vector-memory counter counts ring loads only).
+struct LdsCum {
+  const int* p;
+  __device__ __forceinline__ int operator()(int i) const { return __builtin_amdgcn_readfirstlane(p[i]); }
+};
+struct WsCum {
+  const int* p;
+  __device__ __forceinline__ int operator()(int i) const { return load_uniform(p + i); }
+};
 
 // First nonempty unit at or after b (B if none).
-__device__ __forceinline__ int next_nonempty(const int* cum, int b, int B) {
-  while (b < B && read_cum(cum, b + 1) == read_cum(cum, b)) ++b;
+template <class Cum>
+__device__ __forceinline__ int next_nonempty(const Cum& cum, int b, int B) {
+  while (b < B && cum(b + 1) == cum(b)) ++b;
   return b;
 }
 
-template <int MODE>
-__device__ __forceinline__ Walker seek(const DecodeArgs& a, const int* cum, int B, int Ptot, int64_t tau) {
+template <int MODE, class Cum>
+__device__ __forceinline__ Walker seek(const DecodeArgs& a, const Cum& cum, int B, int Ptot, int64_t tau) {
   Walker w{};
   w.gr = int(tau / Ptot);
   const int r = int(tau % Ptot);
   int lo = 0, hi = B;  // largest b with cum[b] <= r, among b < B
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (read_cum(cum, mid) <= r) lo = mid;
+    if (cum(mid) <= r) lo = mid;
     else hi = mid;
   }
   lo = next_nonempty(cum, lo, B);  // cum[b] <= r < cum[b+1] skips empty units
   w.b = lo;
-  w.page = r - read_cum(cum, lo);
-  w.npg = read_cum(cum, lo + 1) - read_cum(cum, lo);
+  w.page = r - cum(lo);
+  w.npg = cum(lo + 1) - cum(lo);
   if (MODE != kPlain && lo < B) {
     w.nsh = head_pages<MODE>(a, lo);
     if (w.page >= w.nsh) {  // find the owner and page of owner position page - nsh
@@ -195,8 +206,8 @@ __device__ __forceinline__ Walker seek(const DecodeArgs& a, const int* cum, int 
   return w;
 }
 
-template <int MODE>
-__device__ __forceinline__ void advance(const DecodeArgs& a, Walker& w, const int* cum, int B) {
+template <int MODE, class Cum>
+__device__ __forceinline__ void advance(const DecodeArgs& a, Walker& w, const Cum& cum, int B) {
   if (++w.page < w.npg) {
     enter_page<MODE>(a, w);
     return;
@@ -208,7 +219,7 @@ __device__ __forceinline__ void advance(const DecodeArgs& a, Walker& w, const in
     b = next_nonempty(cum, 0, B);
   }
   w.b = b;
-  w.npg = b < B ? read_cum(cum, b + 1) - read_cum(cum, b) : 0;
+  w.npg = b < B ? cum(b + 1) - cum(b) : 0;
   if (MODE != kPlain && b < B) {
     w.nsh = head_pages<MODE>(a, b);
     enter_page<MODE>(a, w);
@@ -296,6 +307,7 @@ __device__ __forceinline__ int priv_pages(const DecodeArgs& a, int b) {
 
 template <int D, int NB, int S, int MODE>
 __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
+  static_assert(MODE != kCascade, "cascade units run on decode_pair_kernel");
   constexpr int SLABS = D / 16;  // 1 KiB slabs per (page, head) tile: K slabs then V slabs
   __shared__ u32x4 ring[kWaves][S][SLABS * 64];
   __shared__ int cum_s[kDecodeMaxBatch + 1];
@@ -304,13 +316,8 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: lets the compiler
   const int Hkv = a.pool.num_kv_heads, RGs = a.plan.rowgroups;  // use scalar loads
-  // units: sessions, or (cascade) the groups the plan kernel formed
-  const int B = MODE == kCascade ? load_uniform(a.ws_units + 3 * a.batch) : a.batch;
+  const int B = a.batch;
 
-  if (MODE == kCascade) {  // the plan kernel wrote the units' page prefix sum
-    for (int u = tid; u <= B; u += 256) cum_s[u] = a.ws_cum[u];
-    __syncthreads();
-  } else {
   // ---- pages per session and their exclusive prefix sum (every workgroup) ----
   const int chunk = (B + 255) / 256;
   int local = 0;
@@ -355,7 +362,6 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
   __syncthreads();
   if (blockIdx.x == 0)
     for (int b = tid; b <= B; b += 256) a.ws_cum[b] = cum_s[b];
-  }
   __builtin_amdgcn_s_waitcnt(0);  // nothing outstanding before the ring starts
 
   const int Ptot = cum_s[B];
@@ -369,14 +375,14 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
   const int num_pages = a.pool.num_pages;
   uint32_t bad = 0;  // ring slots whose page id was out of range
 
-  // owner of each of the lane's rows (one row group per KV head in the owner
-  // modes): its decoder (private) or its session within the unit (cascade)
+  // decoder of each of the lane's rows (private mode: one row group per KV head)
   int row_owner[NB];
-  const int owner_rows = (MODE == kCascade ? a.num_decoders : 1) * (a.num_q_heads / Hkv);
+  const int G = a.num_q_heads / Hkv;
 #pragma unroll
-  for (int cb = 0; cb < NB; ++cb) row_owner[cb] = (cb * 16 + (lane & 15)) / owner_rows;
+  for (int cb = 0; cb < NB; ++cb) row_owner[cb] = (cb * 16 + (lane & 15)) / G;
 
-  Walker iw = seek<MODE>(a, cum_s, B, Ptot, tau0);
+  const LdsCum cum{cum_s};
+  Walker iw = seek<MODE>(a, cum, B, Ptot, tau0);
   Walker cw = iw;
   auto issue = [&](int slot) {
     const int g = iw.gr / RGs;
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + s * 64 + lane),
                                        (__attribute__((address_space(3))) void*)(&ring[wave][slot][s * 64]),
                                        16, 0, 0);
-    advance<MODE>(a, iw, cum_s, B);
+    advance<MODE>(a, iw, cum, B);
   };
 
   QFrag<D, NB> qf;
@@ -422,14 +428,14 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       for (int i = 0; i < D / 16; ++i) vf[i] = v2[2 * v_run(D, i, lane >> 5, lane & 15) + ((lane >> 4) & 1)];
       int lim[NB], nvalid;
       bool masked;
-      if (MODE != kPlain && cw.page >= cw.nsh) {
-        // a page of owner pn: only its rows see it
+      if (MODE == kPrivate && cw.page >= cw.nsh) {
+        // a private page of decoder pn: only its rows see it
         nvalid = min(kPage, cw.plen - cw.pp * kPage);
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) lim[cb] = (row_owner[cb] == cw.pn) ? nvalid : 0;
         masked = true;
       } else {
-        const int L = seq_len(a, MODE == kCascade ? unit_first(a, cw.b) : cw.b);
+        const int L = seq_len(a, cw.b);
         nvalid = min(kPage, L - cw.page * kPage);
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) lim[cb] = nvalid;
@@ -438,7 +444,7 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       attend_page<D, NB>(st, qf, kf, vf, a.scale_log2, masked, lim, nvalid, lane);
     }
     const int cur_gr = cw.gr, cur_b = cw.b;
-    advance<MODE>(a, cw, cum_s, B);
+    advance<MODE>(a, cw, cum, B);
     const bool last = (j == n - 1);
     if (last || cw.gr != cur_gr || cw.b != cur_b) {
       // unit (cur_gr, cur_b) ends here for this wave
@@ -454,6 +460,131 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
         load_q<D, NB, MODE>(qf, a, cw.b, cw.gr / RGs, cw.gr % RGs, lane);
         __builtin_amdgcn_s_waitcnt(0);  // stores and q loads drained before the ring resumes
         unit_begin = int64_t(cw.gr) * Ptot + cum_s[cw.b];
+      }
+    }
+  }
+}
+
+// Cascade units on wave pairs.  A unit's rows (its sessions x N x G, at most
+// 64) form two 32-row groups, one per wave of a 2-wave workgroup.  Both waves
+// walk the same share of the per-KV-head tile list (each unit: its common
+// prefix pages once, then every session's own pages) through one shared LDS
+// ring: each wave streams half of every page, paced by its own vector-memory
+// counter, and one s_barrier per page tells both that the whole page has
+// landed and that the slot read on the previous step may be refilled.  A wave
+// skips the page step on pages none of its rows see (the own pages of a
+// session whose rows sit in the other wave), so a prefix page is read once for
+// all the unit's rows, an own page serves its session's rows only, and every
+// wave keeps the 32-row register budget that lets two waves share a SIMD.
+template <int D, int S>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void decode_pair_kernel(DecodeArgs a) {
+  constexpr int MODE = kCascade, NB = 2, RG = 16 * NB;
+  constexpr int SLABS = D / 16, HALF = SLABS / 2;  // 1 KiB slabs per tile; each wave loads half
+  __shared__ u32x4 ring[S][SLABS * 64];
+
+  const int lane = threadIdx.x & 63;
+  const int rg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // this wave's row group
+  const int Hkv = a.pool.num_kv_heads, NG = a.num_decoders * (a.num_q_heads / Hkv);
+  const int B = load_uniform(a.ws_units + 3 * a.batch);
+  const WsCum cum{a.ws_cum};
+  const int Ptot = cum(B);
+  const int64_t T = int64_t(Ptot) * Hkv;
+  const int W = gridDim.x, k = blockIdx.x;
+  const int64_t tau0 = share_start(k, T, W), tau1 = share_start(k + 1, T, W);
+  if (tau0 >= tau1) return;  // both waves alike: no barriers follow
+  const int n = int(tau1 - tau0);
+
+  const int num_pages = a.pool.num_pages;
+  uint32_t bad = 0;  // ring slots whose page id was out of range (both waves agree)
+  // session (within the unit) of each of the lane's rows, and the sessions this
+  // wave holds rows of
+  int row_owner[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) row_owner[cb] = (rg * RG + cb * 16 + (lane & 15)) / NG;
+  const int own_lo = rg * RG / NG, own_hi = (rg * RG + RG - 1) / NG;
+
+  Walker iw = seek<MODE>(a, cum, B, Ptot, tau0);
+  Walker cw = iw;
+  auto issue = [&](int slot) {
+    int pid = page_id<MODE>(a, iw);
+    const bool ok = pid >= 0 && pid < num_pages;
+    bad = ok ? (bad & ~(1u << slot)) : (bad | (1u << slot));
+    if (!ok) {
+      if (rg == 0) flag_error(a.dev_status, KVS_DEV_BAD_PAGE_BIT);
+      __builtin_amdgcn_s_waitcnt(0);
+      pid = 0;  // stream a harmless in-range page, skip it at compute time
+    }
+    const u32x4* tile = reinterpret_cast<const u32x4*>(a.pool.data + tile_offset(a.layer, pid, iw.gr, num_pages, Hkv, D));
+#pragma unroll
+    for (int h = 0; h < HALF; ++h) {
+      const int s = rg * HALF + h;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + s * 64 + lane),
+                                       (__attribute__((address_space(3))) void*)(&ring[slot][s * 64]), 16, 0, 0);
+    }
+    advance<MODE>(a, iw, cum, B);
+  };
+
+  QFrag<D, NB> qf;
+  RowState<D, NB> st;
+  st.init();
+  load_q<D, NB, MODE>(qf, a, cw.b, cw.gr, rg, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  int64_t unit_begin = int64_t(cw.gr) * Ptot + cum(cw.b);  // first tile of the current unit
+
+#pragma unroll 1
+  for (int j = 0; j < S - 1 && j < n; ++j) issue(j);
+
+#pragma unroll 1
+  for (int j = 0; j < n; ++j) {
+    const int slot = j % S;
+    // this wave's half of page j has landed (pages j+1 .. j+S-2 may be in flight)
+    wait_ring<HALF, S>(min(S - 2, n - 1 - j));
+    // ... and the other wave's half; both are done reading page j-1's slot
+    __builtin_amdgcn_s_barrier();
+    if (j + S - 1 < n) issue((j + S - 1) % S);
+    const int rows = unit_count(a, cw.b) * NG;
+    const bool prefix = cw.page < cw.nsh;
+    const bool mine = rg * RG < rows && (prefix || (cw.pn >= own_lo && cw.pn <= own_hi));
+    if (mine && !((bad >> slot) & 1u)) {
+      u32x4 kf[D / 32];
+      u32x2 vf[D / 16];
+      const u32x2* v2 = reinterpret_cast<const u32x2*>(ring[slot]);
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) kf[i] = ring[slot][k_run(i, lane >> 4, lane & 15)];
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) vf[i] = v2[2 * v_run(D, i, lane >> 5, lane & 15) + ((lane >> 4) & 1)];
+      int lim[NB], nvalid;
+      bool masked;
+      if (!prefix) {  // an own page of session pn: only its rows see it
+        nvalid = min(kPage, cw.plen - cw.pp * kPage);
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) lim[cb] = (row_owner[cb] == cw.pn) ? nvalid : 0;
+        masked = own_lo != own_hi || nvalid < kPage;
+      } else {  // prefix pages are whole pages of every session of the unit
+        nvalid = kPage;
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) lim[cb] = kPage;
+        masked = false;
+      }
+      attend_page<D, NB>(st, qf, kf, vf, a.scale_log2, masked, lim, nvalid, lane);
+    }
+    const int cur_gr = cw.gr, cur_b = cw.b;
+    advance<MODE>(a, cw, cum, B);
+    const bool last = (j == n - 1);
+    if (last || cw.gr != cur_gr || cw.b != cur_b) {
+      // unit (cur_gr, cur_b) ends here for this pair
+      const int64_t unit_end = unit_begin + (cum(cur_b + 1) - cum(cur_b));
+      const bool before = unit_begin < tau0, after = unit_end > tau1;
+      if (!before && !after) {
+        write_rows<D, NB, MODE>(a, st, cur_b, cur_gr, rg, lane);
+      } else {
+        write_partial<D, NB>(a, st, (k * 2 + (before ? 0 : 1)) * 2 + rg, lane);
+      }
+      if (!last) {
+        st.init();
+        load_q<D, NB, MODE>(qf, a, cw.b, cw.gr, rg, lane);
+        __builtin_amdgcn_s_waitcnt(0);  // stores and q loads drained before the ring resumes
+        unit_begin = int64_t(cw.gr) * Ptot + cum(cw.b);
       }
     }
   }
@@ -476,6 +607,9 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
   const int Ptot = load_uniform(a.ws_cum + B);
   const int cb0 = load_uniform(a.ws_cum + b);
   const int npg = load_uniform(a.ws_cum + b + 1) - cb0;
+  // shares: one per wave (plain, private) or per wave pair (cascade: the tile
+  // list is per KV head, and each share's slots are split by row group)
+  constexpr bool kPair = MODE == kCascade;
   const int W = a.plan.blocks * kWaves;
   if (npg == 0) {
     for (int e = threadIdx.x; e < RG * (D / 8); e += blockDim.x) {
@@ -485,8 +619,8 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
     }
     return;
   }
-  const int64_t T = int64_t(Ptot) * Hkv * RGs;
-  const int64_t s_u = int64_t(gr) * Ptot + cb0, e_u = s_u + npg;
+  const int64_t T = int64_t(Ptot) * Hkv * (kPair ? 1 : RGs);
+  const int64_t s_u = int64_t(kPair ? g : gr) * Ptot + cb0, e_u = s_u + npg;
   // share of tile t: floor(((t + 1) W - 1) / T)
   const int k0 = int(((s_u + 1) * W - 1) / T), k1 = int((e_u * W - 1) / T);
   if (k0 == k1) return;  // written directly by its wave
@@ -499,16 +633,17 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
     const int64_t row = unit_row<MODE>(a, b, g, rg * RG + rl);
     if (row < 0) continue;
     // slot of share k: its "started before" slot (0) except the first share (1)
+    auto slot_of = [&](int k) { return int64_t(k * 2 + (k == k0)) * (kPair ? 2 : 1) + (kPair ? rg : 0); };
     float M = -INFINITY;
 #pragma unroll 8
     for (int k = k0; k <= k1; ++k)
-      if (!empty(k)) M = fmaxf(M, ml[(int64_t(k * 2 + (k == k0)) * RG + rl) * 2]);
+      if (!empty(k)) M = fmaxf(M, ml[(slot_of(k) * RG + rl) * 2]);
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
 #pragma unroll 4
     for (int k = k0; k <= k1; ++k) {
       if (empty(k)) continue;
-      const int64_t slot = k * 2 + (k == k0);
+      const int64_t slot = slot_of(k);
       const float ms = ml[(slot * RG + rl) * 2];
       const float ls = ml[(slot * RG + rl) * 2 + 1];
       const f32x4 as = reinterpret_cast<const f32x4*>(accp + (slot * RG + rl) * D)[d4];
@@ -542,7 +677,7 @@ __device__ __forceinline__ int block_scan(int x, int* buf) {
 // Cascade plan.  Sessions with equal, non-negative group ids that are adjacent in
 // the batch share their first group_prefix[b] pages.  Runs of such sessions are
 // cut into units of at most `per_unit` sessions (all rows of a unit fit one
-// wave); each unit gets its first session, session count, common prefix pages
+// wave pair); each unit gets its first session, session count, common prefix pages
 // and its tile count (the prefix once, then every session's pages past it).
 // One workgroup of 1024 threads, 4 sessions per thread (batch <= 4096).
 // Flags: members whose group_prefix differs from the unit's first session's
@@ -667,13 +802,6 @@ __global__ __launch_bounds__(1024) void decode_cascade_plan_kernel(DecodeArgs a,
 template <int D, int NB, int MODE>
 hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
   constexpr int S = D == 128 ? 4 : 8;  // 32 KiB of ring per wave
-  if (MODE == kCascade) {
-    const int G = a.num_q_heads / a.pool.num_kv_heads;
-    hipLaunchKernelGGL(decode_cascade_plan_kernel, dim3(1), dim3(1024), 0, stream, a,
-                       a.plan.rows / (a.num_decoders * G));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   hipLaunchKernelGGL((decode_stream_kernel<D, NB, S, MODE>), dim3(a.plan.blocks), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -683,9 +811,26 @@ hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Cascade: the plan kernel forms the units, then 4 wave pairs per CU (two waves
+// per SIMD) stream them, then the combine kernel merges split units.
+template <int D>
+hipError_t launch_decode_cascade(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int S = D == 128 ? 4 : 8;  // 32 KiB of ring per pair
+  const int G = a.num_q_heads / a.pool.num_kv_heads;
+  hipLaunchKernelGGL(decode_cascade_plan_kernel, dim3(1), dim3(1024), 0, stream, a,
+                     a.plan.rows / (a.num_decoders * G));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_pair_kernel<D, S>), dim3(a.plan.blocks * kWaves), dim3(128), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int units = a.pool.num_kv_heads * a.plan.rowgroups * a.batch;
+  hipLaunchKernelGGL((decode_combine_kernel<D, kCascade>), dim3(units), dim3(a.plan.rg_rows * (D / 4)), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D, int NB>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  if (a.group_id) return launch_decode_mode<D, NB, kCascade>(a, stream);
   if (a.pbt) return launch_decode_mode<D, NB, kPrivate>(a, stream);
   return launch_decode_mode<D, NB, kPlain>(a, stream);
 }
@@ -694,6 +839,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int D = a.pool.head_dim, nb = a.plan.nb;
+  if (a.group_id) return D == 128 ? launch_decode_cascade<128>(a, stream) : launch_decode_cascade<64>(a, stream);
   if (D == 128) {
     if (nb == 1) return launch_decode_t<128, 1>(a, stream);
     if (nb == 2) return launch_decode_t<128, 2>(a, stream);

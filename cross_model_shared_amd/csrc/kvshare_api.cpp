@@ -157,7 +157,8 @@ int decode_common(const char* name, const kvs_pool* pool, int32_t layer, const v
   kvs::DecodePlan plan = kvs::plan_decode(batch, num_decoders, num_q_heads, pool->num_kv_heads,
                                           pool->head_dim, max_seq_len);
   if (group_id) {
-    // a unit holds as many whole sessions as fit 64 rows (at least one)
+    // a unit holds as many whole sessions as fit 64 rows (at least one), split
+    // into two 32-row groups, one per wave of a pair
     const int ng = num_decoders * (num_q_heads / pool->num_kv_heads);
     if (ng > 64)
       return fail(KVS_EUNSUPPORTED, "%s: %d query rows per KV head and session (num_decoders * group) above 64",
@@ -165,6 +166,9 @@ int decode_common(const char* name, const kvs_pool* pool, int32_t layer, const v
     const int per_unit = 64 / ng;
     kvs::DecodePlan full = kvs::plan_decode(batch, per_unit * num_decoders, num_q_heads, pool->num_kv_heads,
                                             pool->head_dim, max_seq_len);
+    full.nb = 2;
+    full.rg_rows = 32;
+    full.rowgroups = 2;
     full.bytes = plan.bytes;  // same workspace layout and size
     full.cum_offset = plan.cum_offset;
     full.units_offset = plan.units_offset;

@@ -194,3 +194,53 @@ def test_private_decode_full_size_sampled():
             err = max(err, float(np.max(np.abs(got[b, n:n + 1] - want))))
     print(f"[fullsize] private: sessions {picks} max-abs err {err:.3e}", flush=True)
     assert err <= TOL
+
+
+def test_cascade_decode_full_size_sampled():
+    """qwen3_8b_n8_cascade at full size (64 sessions in 32 pairs sharing 4K-8K-token
+    prefix pages, own 0-8K tokens), in the bench's launch configuration; 8 sampled
+    sessions, every decoder and head, against the oracle over prefix ++ own tokens."""
+    import torch
+
+    wl = W.make_workload("qwen3_8b_n8_cascade")
+    B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    bt, lens, gid, pref, num_pages = W.build_prefix_groups(wl.groups, wl.seed)
+    print(f"[fullsize] cascade: B={B} N={N} sum(L)={sum(lens)} pages={num_pages}", flush=True)
+    pool = binding.Pool(1, num_pages, Hkv, D, fill=np.int16(np.uint16(gu.POISON_NAN).view(np.int16)))
+    st = gu.status_tensor()
+    d_bt = torch.from_numpy(bt).cuda()
+    firsts = [b for b in range(B) if b == 0 or gid[b] != gid[b - 1]]
+    pre_tok = [wl.groups[gid[b]][0] for b in firsts]
+    own = [L - int(p) * 16 for L, p in zip(lens, pref)]
+    logical = []
+    for i, (rows, ls, before) in enumerate(((firsts, pre_tok, [0] * len(firsts)),
+                                            (list(range(B)), own, [int(p) * 16 for p in pref]))):
+        total = sum(ls)
+        cu = np.concatenate([[0], np.cumsum(ls)]).astype(np.int32)
+        k = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 60 + 2 * i)).view(total, Hkv, D)
+        v = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 61 + 2 * i)).view(total, Hkv, D)
+        binding.append(pool, 0, k, v, gu.dev_i32(cu), d_bt[rows].contiguous(), gu.dev_i32(before),
+                       max_new=max(max(ls), 1), max_seq_len=max(lens), dev_status=st)
+        logical.append((k, v, cu))
+    q = W.device_normal_bf16(B * N * Hq * D, wl.std, W.mix_seed(wl.seed, 64)).view(B, N, Hq, D)
+    out = torch.empty_like(q)
+    maxL = max(lens)
+    ws = gu.nan_workspace(binding.decode_workspace_bytes(B, N, Hq, Hkv, D, maxL))
+    binding.decode_cascade(pool, 0, q, out, d_bt, gu.dev_i32(lens), torch.from_numpy(gid).cuda(),
+                           torch.from_numpy(pref).cuda(), maxL, wl.scale, ws, dev_status=st)
+    gu.sync()
+    assert int(st.item()) == 0
+    got = gu.host_f64(out)
+    assert np.all(np.isfinite(got))
+    picks = sample_sessions(lens, 8, wl.seed)
+    qh = host_rows(q)
+    (kp, vp, cup), (ko, vo, cuo) = logical
+    err = 0.0
+    for b in picks:
+        f = firsts.index(max(x for x in firsts if x <= b))
+        K = np.concatenate([host_rows(kp[cup[f]:cup[f + 1]]), host_rows(ko[cuo[b]:cuo[b + 1]])])
+        V = np.concatenate([host_rows(vp[cup[f]:cup[f + 1]]), host_rows(vo[cuo[b]:cuo[b + 1]])])
+        want = oracle.decode_from_logical(qh[b:b + 1], [K], [V], wl.scale)
+        err = max(err, float(np.max(np.abs(got[b:b + 1] - want))))
+    print(f"[fullsize] cascade: sessions {picks} max-abs err {err:.3e}", flush=True)
+    assert err <= TOL
