@@ -634,12 +634,9 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
     if (row < 0) continue;
     // slot of share k: its "started before" slot (0) except the first share (1)
     auto slot_of = [&](int k) { return int64_t(k * 2 + (k == k0)) * (kPair ? 2 : 1) + (kPair ? rg : 0); };
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int k = k0; k <= k1; ++k)
-      if (!empty(k)) M = fmaxf(M, ml[(slot_of(k) * RG + rl) * 2]);
+    // one pass, merging online: the shares' loads do not wait on a first max pass
+    float M = -INFINITY, den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
 #pragma unroll 4
     for (int k = k0; k <= k1; ++k) {
       if (empty(k)) continue;
@@ -647,9 +644,12 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
       const float ms = ml[(slot * RG + rl) * 2];
       const float ls = ml[(slot * RG + rl) * 2 + 1];
       const f32x4 as = reinterpret_cast<const f32x4*>(accp + (slot * RG + rl) * D)[d4];
-      const float w = (ms == -INFINITY) ? 0.f : exp2_fast(ms - M);
-      den += w * ls;
-      num += w * as;
+      if (ms == -INFINITY) continue;  // the share saw no key of this row
+      const float Mn = fmaxf(M, ms);
+      const float c = exp2_fast(M - Mn), w = exp2_fast(ms - Mn);  // exp2(-inf) = 0
+      den = den * c + w * ls;
+      num = num * c + w * as;
+      M = Mn;
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     reinterpret_cast<u32x2*>(a.out + row * D)[d4] =
@@ -785,18 +785,32 @@ __global__ __launch_bounds__(1024) void decode_cascade_plan_kernel(DecodeArgs a,
     if (tid == 0) voff_s[B] = nv;
   }
   __syncthreads();
-  for (int idx = tid; idx < nv; idx += 1024) {
-    int lo = 0, hi = B;  // largest b with voff_s[b] <= idx
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (voff_s[mid] <= idx) lo = mid;
-      else hi = mid;
+  // 8 entries per thread and pass, all loads issued before any compare
+  constexpr int V = 8;
+  bool mismatch = false;
+  for (int base = tid; base < nv; base += 1024 * V) {
+    int x[V], y[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      const int idx = base + u * 1024;
+      x[u] = y[u] = 0;
+      if (idx < nv) {
+        int lo = 0, hi = B;  // largest b with voff_s[b] <= idx
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (voff_s[mid] <= idx) lo = mid;
+          else hi = mid;
+        }
+        const int p = idx - voff_s[lo];
+        const int f = first_s[ui_s[lo]];
+        x[u] = a.bt[int64_t(lo) * a.bt_stride + p];
+        y[u] = a.bt[int64_t(f) * a.bt_stride + p];
+      }
     }
-    const int p = idx - voff_s[lo];
-    const int f = first_s[ui_s[lo]];
-    if (a.bt[int64_t(lo) * a.bt_stride + p] != a.bt[int64_t(f) * a.bt_stride + p])
-      flag_error(a.dev_status, KVS_DEV_BAD_PAGE_BIT);
+#pragma unroll
+    for (int u = 0; u < V; ++u) mismatch |= x[u] != y[u];
   }
+  if (mismatch) flag_error(a.dev_status, KVS_DEV_BAD_PAGE_BIT);
 }
 
 template <int D, int NB, int MODE>
