@@ -658,19 +658,24 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
 }
 
 // Inclusive scan (op = + or max) of one value per thread over a 1024-thread
-// workgroup.  On return buf[t] holds thread t's inclusive value.
+// workgroup: a shuffle scan inside each wave, then the 16 wave totals.  On
+// return buf[t] holds thread t's inclusive value.
 template <bool MAX>
 __device__ __forceinline__ int block_scan(int x, int* buf) {
-  const int tid = threadIdx.x;
-  buf[tid] = x;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int t = tid >= off ? buf[tid - off] : (MAX ? INT_MIN : 0);
-    __syncthreads();
-    x = MAX ? max(x, t) : x + t;
-    buf[tid] = x;
-    __syncthreads();
+  __shared__ int wave_total[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(x, off);
+    if (lane >= off) x = MAX ? max(x, t) : x + t;
   }
+  if (lane == 63) wave_total[w] = x;
+  __syncthreads();
+  int carry = MAX ? INT_MIN : 0;
+  for (int i = 0; i < w; ++i) carry = MAX ? max(carry, wave_total[i]) : carry + wave_total[i];
+  x = MAX ? max(x, carry) : x + carry;
+  buf[tid] = x;
+  __syncthreads();  // buf complete, and wave_total free for the next scan
   return x;
 }
 
