@@ -13,7 +13,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvshare.so")
 
-KVS_OK, KVS_EINVAL, KVS_ERANGE, KVS_EWORKSPACE, KVS_EUNSUPPORTED, KVS_EHIP = 0, -1, -2, -3, -4, -5
+KVS_OK, KVS_EINVAL, KVS_ERANGE, KVS_EWORKSPACE, KVS_EUNSUPPORTED, KVS_EHIP, KVS_ENOSPACE = 0, -1, -2, -3, -4, -5, -6
 DEV_BAD_PAGE, DEV_BAD_LEN = 1, 2
 PAGE = 16
 
@@ -50,6 +50,14 @@ _SIGNATURES = {
     "kv_pages_pack": (ctypes.c_int, [_pool_p, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
     "kv_pages_unpack": (ctypes.c_int, [_pool_p, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
     "kv_pool_fetch": (ctypes.c_int, [_pool_p, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "kvs_prefix_cache_create": (_vp, [_i32]),
+    "kvs_prefix_cache_destroy": (None, [_vp]),
+    "kvs_prefix_cache_admit": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp]),
+    "kvs_prefix_cache_publish": (ctypes.c_int, [_vp, _vp, _i32, _vp]),
+    "kvs_prefix_cache_release": (ctypes.c_int, [_vp, _vp, _i32]),
+    "kvs_prefix_cache_stats": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp]),
+    "kvs_prefix_cache_refcount": (ctypes.c_int, [_vp, _i32]),
+    "kvs_prefix_groups": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _vp]),
     "kvs_last_error": (ctypes.c_char_p, []),
     "kvs_version": (ctypes.c_char_p, []),
 }
@@ -275,3 +283,85 @@ def fetch(pool: Pool, layer, block_table, seq_lens, cu_rows, max_seq_len, k_out,
         _ptr(seq_lens, "seq_lens", torch.int32), _ptr(cu_rows, "cu_rows", torch.int32, batch + 1), batch, total,
         max_seq_len, _ptr(k_out, "k_out", torch.bfloat16, total * row), _ptr(v_out, "v_out", torch.bfloat16, total * row),
         _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Host-side prefix cache (kvs_prefix_cache.h): host int32 arrays, no GPU.
+# ---------------------------------------------------------------------------
+def _host_i32(x, n=None):
+    import numpy as np
+
+    a = np.ascontiguousarray(x, dtype=np.int32)
+    if n is not None and a.size < n:
+        raise ValueError(f"need at least {n} int32 values, got {a.size}")
+    return a
+
+
+def _aptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a.size else None
+
+
+class PrefixCache:
+    """Page allocator with a prefix cache of full 16-token blocks."""
+
+    def __init__(self, num_pages: int):
+        self._h = load().kvs_prefix_cache_create(int(num_pages))
+        if not self._h:
+            raise KvsError(KVS_EINVAL, last_error())
+        self.num_pages = int(num_pages)
+
+    def close(self):
+        if self._h:
+            load().kvs_prefix_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def admit(self, tokens):
+        """Page ids (int32 array of ceil(L/16)) and the count of reused leading pages."""
+        import numpy as np
+
+        t = _host_i32(tokens)
+        out = np.zeros(max((t.size + PAGE - 1) // PAGE, 1), np.int32)
+        matched = ctypes.c_int32(0)
+        _check(load().kvs_prefix_cache_admit(self._h, _aptr(t), int(t.size), _aptr(out), ctypes.byref(matched)))
+        return out[:(t.size + PAGE - 1) // PAGE], int(matched.value)
+
+    def publish(self, tokens, pages):
+        t = _host_i32(tokens)
+        p = _host_i32(pages, t.size // PAGE)
+        _check(load().kvs_prefix_cache_publish(self._h, _aptr(t), int(t.size), _aptr(p)))
+
+    def release(self, pages):
+        p = _host_i32(pages)
+        _check(load().kvs_prefix_cache_release(self._h, _aptr(p), int(p.size)))
+
+    def stats(self):
+        """(free, evictable, referenced, entries)"""
+        v = [ctypes.c_int32(0) for _ in range(4)]
+        _check(load().kvs_prefix_cache_stats(self._h, *[ctypes.byref(x) for x in v]))
+        return tuple(int(x.value) for x in v)
+
+    def refcount(self, page: int) -> int:
+        r = load().kvs_prefix_cache_refcount(self._h, int(page))
+        if r < 0:
+            _check(r)
+        return r
+
+
+def prefix_groups(block_table, seq_lens):
+    """(group_id, group_prefix_pages) int32 arrays for decode_cascade, from host tables."""
+    import numpy as np
+
+    bt = _host_i32(block_table)
+    lens = _host_i32(seq_lens)
+    B = lens.size
+    if bt.ndim != 2 or bt.shape[0] != B:
+        raise ValueError("block_table must be [batch, stride]")
+    gid, pref = np.zeros(B, np.int32), np.zeros(B, np.int32)
+    _check(load().kvs_prefix_groups(_aptr(bt), int(bt.shape[1]), _aptr(lens), int(B), _aptr(gid), _aptr(pref)))
+    return gid, pref

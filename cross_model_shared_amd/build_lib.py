@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvshare.so")
 ARCH = "gfx950"
 
-SOURCES = ["kvshare_api.cpp", "append.hip", "decode.hip", "extend.hip", "handoff.hip"]
+SOURCES = ["kvshare_api.cpp", "prefix_cache.cpp", "append.hip", "decode.hip", "extend.hip", "handoff.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

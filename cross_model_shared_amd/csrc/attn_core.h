@@ -84,11 +84,11 @@ __device__ __forceinline__ void attend_page(RowState<D, NB>& st, const QFrag<D, 
     const bool move = tmax > m_old + kLazyLog2;   // also true for the first seen key
     const float m_new = move ? tmax : m_old;
     any_move |= move;
-    alpha[cb] = move ? exp2f(m_old - m_new) : 1.f;  // exp2(-inf) = 0 on the first move
+    alpha[cb] = move ? exp2_fast(m_old - m_new) : 1.f;  // exp2(-inf) = 0 on the first move
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     float p[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = exp2f(x[j] - m_use);
+    for (int j = 0; j < 4; ++j) p[j] = exp2_fast(x[j] - m_use);
     st.l[cb] = st.l[cb] * alpha[cb] + ((p[0] + p[1]) + (p[2] + p[3]));
     st.m[cb] = m_new;
     pb[cb] = pack_bf16x4(p[0], p[1], p[2], p[3]);

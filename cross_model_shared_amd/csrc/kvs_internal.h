@@ -41,6 +41,9 @@ struct DecodePlan {
   size_t cum_offset, units_offset, ml_offset, acc_offset, bytes;
 };
 
+// Record a printf-style message for kvs_last_error() and return `status`.
+int set_error(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 DecodePlan plan_decode(int batch, int num_decoders, int num_q_heads, int num_kv_heads, int head_dim,
                        int max_seq_len);
 

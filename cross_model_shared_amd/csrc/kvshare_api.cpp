@@ -14,13 +14,18 @@ namespace {
 
 thread_local std::string g_last_error;
 
-int fail(int status, const char* fmt, ...) {
+int vfail(int status, const char* fmt, va_list ap) {
   char buf[512];
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  g_last_error = buf;
+  return status;
+}
+
+int fail(int status, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vfail(status, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return status;
 }
 
@@ -65,6 +70,14 @@ constexpr int kDecodeBlocks = 256;
 }  // namespace
 
 namespace kvs {
+
+int set_error(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vfail(status, fmt, ap);
+  va_end(ap);
+  return status;
+}
 
 DecodePlan plan_decode(int batch, int num_decoders, int num_q_heads, int num_kv_heads, int head_dim,
                        int max_seq_len) {

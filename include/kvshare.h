@@ -91,7 +91,8 @@ enum {
   KVS_ERANGE = -2,       /* a bound exceeds the block table / pool capacity   */
   KVS_EWORKSPACE = -3,   /* workspace missing or smaller than required        */
   KVS_EUNSUPPORTED = -4, /* page_size != 16, head_dim not in {64,128}, ...    */
-  KVS_EHIP = -5          /* a HIP launch failed; see kvs_last_error()         */
+  KVS_EHIP = -5,         /* a HIP launch failed; see kvs_last_error()         */
+  KVS_ENOSPACE = -6      /* (kvs_prefix_cache.h) not enough free pages        */
 };
 
 /* Bits OR-ed into *dev_status by the kernels. */

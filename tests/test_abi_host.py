@@ -35,7 +35,9 @@ def test_library_exports_every_declared_symbol(L):
     assert {"kv_pool_append", "shared_kv_decode", "shared_kv_decode_private", "shared_kv_decode_cascade",
             "partial_prefill_extend",
             "kv_pages_pack", "kv_pages_unpack", "kv_pages_buffer_bytes", "kv_pool_fetch", "kvs_pool_bytes",
-            "shared_kv_decode_workspace_bytes", "kvs_last_error", "kvs_version"} <= set(names)
+            "shared_kv_decode_workspace_bytes", "kvs_last_error", "kvs_version",
+            "kvs_prefix_cache_create", "kvs_prefix_cache_admit", "kvs_prefix_cache_publish",
+            "kvs_prefix_cache_release", "kvs_prefix_groups"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert b"gfx950" in L.kvs_version()

@@ -119,3 +119,58 @@ def test_cascade_reports_inconsistent_groups_without_faulting():
     out = gu.host_f64(run_cascade(c, bt=bt))
     assert int(c["status"].item()) & binding.DEV_BAD_PAGE
     assert np.all(np.isfinite(out))
+
+
+def test_cascade_over_allocator_tables():
+    """Sessions admitted through the prefix cache: the later sessions reuse the
+    published full blocks of a system prompt (their KV is not written again, only
+    the tokens past the reused pages are appended), the grouping comes from
+    kvs_prefix_groups, and the cascade decode equals the oracle over each
+    session's logical K/V."""
+    import torch
+
+    N, Hkv, G, D = 4, 2, 4, 128
+    rng = np.random.default_rng(81)
+    pc = binding.PrefixCache(64)
+    sys_a = [int(x) for x in rng.integers(0, 1000, 16 * 5 + 7)]
+    sys_b = [int(x) for x in rng.integers(0, 1000, 16 * 3)]
+    prompts = [sys_a + [1] * 30, sys_a + [2] * 3, sys_a + [3] * 50, sys_a, sys_b + [4] * 9, sys_b]
+    pool = binding.Pool(1, 64, Hkv, D, fill=np.int16(np.uint16(gu.POISON_NAN).view(np.int16)))
+    st = gu.status_tensor()
+    rows, K, V = [], [], []
+    first_kv = {}
+    for t in prompts:
+        pages, matched = pc.admit(t)
+        L, P = len(t), 16 * matched
+        key = tuple(t[:P])
+        if matched:
+            pk, pv = first_kv[key]
+        else:
+            pk = pv = np.zeros((0, Hkv, D), np.uint16)
+        ok = wlmod.draw_bf16(rng, (L - P, Hkv, D), 1.0)
+        ov = wlmod.draw_bf16(rng, (L - P, Hkv, D), 1.0)
+        kk, vv = np.concatenate([pk, ok]), np.concatenate([pv, ov])
+        for m in range(1, L // 16 + 1):          # what a later session could reuse of this one
+            first_kv.setdefault(tuple(t[:16 * m]), (kk[:16 * m], vv[:16 * m]))
+        if L > P:
+            binding.append(pool, 0, gu.dev_bf16(ok), gu.dev_bf16(ov), gu.dev_i32([0, L - P]),
+                           gu.dev_i32(np.asarray(pages, np.int32)[None]), gu.dev_i32([P]), max_new=L,
+                           max_seq_len=L, dev_status=st)
+        pc.publish(t, pages)
+        rows.append(pages)
+        K.append(kk)
+        V.append(vv)
+    lens = [len(t) for t in prompts]
+    bt = np.full((len(rows), max(len(r) for r in rows)), -1, np.int32)
+    for i, r in enumerate(rows):
+        bt[i, :len(r)] = r
+    gid, pref = binding.prefix_groups(bt, lens)
+    assert list(gid) == [0, 0, 0, 0, 4, 4] and list(pref) == [5, 5, 5, 5, 3, 3]
+    q = wlmod.draw_bf16(rng, (len(rows), N, Hkv * G, D), 1.0)
+    c = dict(pool=pool, bt=bt, lens=lens, gid=gid, pref=pref, q=q, status=st, Hkv=Hkv, D=D)
+    out = gu.host_f64(run_cascade(c))
+    want = oracle.decode_from_logical(q, K, V, 1.0 / math.sqrt(D))
+    err = float(np.max(np.abs(out - want)))
+    print(f"[cascade] allocator tables: max-abs err {err:.3e}", flush=True)
+    assert err <= TOL
+    assert int(st.item()) == 0
