@@ -1,4 +1,4 @@
-// The per-page attention step shared by decode and extend.
+// The per-page attention step of the decode kernels.
 //
 // One wave owns NB column blocks of 16 query rows.  For a 16-token page of one
 // KV head it forms S^T = K Q^T on the matrix cores (tokens on the M side, query
