@@ -30,8 +30,8 @@ constexpr int kDecodeMaxBatch = 4096;
 
 // How a decode call is cut into work: query rows per KV head are taken in row
 // groups of 16*nb (one wave holds them all); the (page, KV head, row group)
-// tiles of all sessions are shared out evenly among the 4*blocks waves of a
-// persistent grid.  Each wave has two partial-state slots in the workspace.
+// tiles of all sessions are shared out among the 4*blocks waves of a
+// persistent grid (evenly, up to a fixed weight per XCD).  Each wave has two partial-state slots in the workspace.
 struct DecodePlan {
   int rows;       // N * G query rows per KV head
   int nb;         // 16-row column blocks per wave (1, 2 or 4)
@@ -40,6 +40,12 @@ struct DecodePlan {
   int blocks;     // workgroups of the persistent grid (one per CU)
   size_t cum_offset, units_offset, ml_offset, acc_offset, bytes;
 };
+
+// Persistent decode grid: one 4-wave workgroup per CU of an MI355X (256 CUs),
+// so 1024 = 2^10 stream-K shares (waves, or wave pairs in the cascade).
+constexpr int kDecodeBlocks = 256;
+constexpr int kDecodeShareLog2 = 10;
+static_assert(kDecodeBlocks * 4 == 1 << kDecodeShareLog2, "share count");
 
 // Record a printf-style message for kvs_last_error() and return `status`.
 int set_error(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));

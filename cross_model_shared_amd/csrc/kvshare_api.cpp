@@ -64,8 +64,6 @@ int launched(hipError_t e, const char* what) {
   return KVS_OK;
 }
 
-// Workgroups of the persistent decode grid: one per CU of an MI355X (256 CUs).
-constexpr int kDecodeBlocks = 256;
 
 }  // namespace
 
