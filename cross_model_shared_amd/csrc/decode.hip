@@ -240,38 +240,41 @@ __device__ __forceinline__ int64_t unit_row(const DecodeArgs& a, int b, int g, i
   return (int64_t(b) * a.num_decoders + r / G) * a.num_q_heads + g * G + r % G;
 }
 
-// Stream-K share boundaries.
-//
-// Cascade (decode_pair_kernel): 2^10 equal shares, share k on workgroup k.
-__device__ __forceinline__ int64_t pair_share_start(int k, int64_t T) { return (int64_t(k) * T) >> kDecodeShareLog2; }
-
-// Stream kernel: share k runs on workgroup k/4, which the hardware places on
-// XCD (k/4) % 8.  Per-wave timestamps on MI355X show the odd XCDs streaming
-// KV pages about 10% slower than the even ones, so an even-XCD share weighs
-// 276 and an odd-XCD share 236 (32 consecutive shares weigh 8192, all 1024
-// weigh 2^18): the waves then finish closer together (2% faster calls
-// measured).  The weights only move boundaries; any split is correct.
-constexpr int64_t kShareEven = 276, kShareOdd = 236, kSharePeriod = 4 * 4 * (kShareEven + kShareOdd);
+// Stream-K share boundaries: 2^10 shares, WPG consecutive shares per
+// workgroup (4 waves in the stream kernel, one wave pair in the cascade), and
+// the hardware places workgroup i on XCD i % 8.  Per-wave timestamps on MI355X
+// show the odd XCDs streaming KV pages about 10% slower than the even ones, so
+// a share on an even XCD weighs 276 and one on an odd XCD 236 (all 1024 weigh
+// 2^18): the waves then finish closer together (calls 2% faster, measured).
+// The weights only move boundaries; any split is correct.
+constexpr int64_t kShareEven = 276, kShareOdd = 236;
 constexpr int kShareTotalLog2 = 18;
-static_assert(32 * kSharePeriod == int64_t(1) << kShareTotalLog2 && kDecodeShareLog2 == 10, "share weights");
+static_assert(512 * (kShareEven + kShareOdd) == int64_t(1) << kShareTotalLog2 && kDecodeShareLog2 == 10,
+              "share weights");
 
 // weight of shares 0 .. k-1
+template <int WPG>
 __device__ __forceinline__ int64_t share_weight_before(int k) {
-  const int r = k & 31, g = r >> 2;  // workgroup within the period of 8 = its XCD
+  static_assert(WPG == 1 || WPG == 4, "shares per workgroup");
+  constexpr int kPer = 8 * WPG;  // shares of one round of 8 workgroups
+  const int r = k % kPer, g = r / WPG;  // workgroup within the round = its XCD
   const int64_t prev = ((g + 1) >> 1) * kShareEven + (g >> 1) * kShareOdd;  // XCDs 0 .. g-1
-  return int64_t(k >> 5) * kSharePeriod + 4 * prev + int64_t(r & 3) * ((g & 1) ? kShareOdd : kShareEven);
+  return int64_t(k / kPer) * WPG * 4 * (kShareEven + kShareOdd) + WPG * prev +
+         int64_t(r % WPG) * ((g & 1) ? kShareOdd : kShareEven);
 }
+template <int WPG>
 __device__ __forceinline__ int64_t share_start(int k, int64_t T) {
-  return (share_weight_before(k) * T) >> kShareTotalLog2;
+  return (share_weight_before<WPG>(k) * T) >> kShareTotalLog2;
 }
 // the share holding tile t: the largest k with share_start(k) <= t, i.e. with
 // share_weight_before(k) * T < (t + 1) * 2^18
+template <int WPG>
 __device__ __forceinline__ int share_of(int64_t t, int64_t T) {
   const int64_t lim = (t + 1) << kShareTotalLog2;
   int lo = 0, hi = 1 << kDecodeShareLog2;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (share_weight_before(mid) * T < lim) lo = mid;
+    if (share_weight_before<WPG>(mid) * T < lim) lo = mid;
     else hi = mid;
   }
   return lo;
@@ -402,7 +405,7 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
   const int Ptot = cum_s[B];
   const int64_t T = int64_t(Ptot) * Hkv * RGs;
   const int k = blockIdx.x * kWaves + wave;  // the grid is kDecodeBlocks workgroups
-  const int64_t tau0 = share_start(k, T), tau1 = share_start(k + 1, T);
+  const int64_t tau0 = share_start<kWaves>(k, T), tau1 = share_start<kWaves>(k + 1, T);
   if (tau0 >= tau1) return;  // no barriers follow
   const int n = int(tau1 - tau0);
 
@@ -524,7 +527,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int Ptot = cum(B);
   const int64_t T = int64_t(Ptot) * Hkv;
   const int k = blockIdx.x;  // the grid is one pair per share
-  const int64_t tau0 = pair_share_start(k, T), tau1 = pair_share_start(k + 1, T);
+  const int64_t tau0 = share_start<1>(k, T), tau1 = share_start<1>(k + 1, T);
   if (tau0 >= tau1) return;  // both waves alike: no barriers follow
   const int n = int(tau1 - tau0);
 
@@ -644,7 +647,6 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
   // shares: one per wave (plain, private) or per wave pair (cascade: the tile
   // list is per KV head, and each share's slots are split by row group)
   constexpr bool kPair = MODE == kCascade;
-  constexpr int64_t W = int64_t(1) << kDecodeShareLog2;
   if (npg == 0) {
     for (int e = threadIdx.x; e < RG * (D / 8); e += blockDim.x) {
       const int64_t row = unit_row<MODE>(a, b, g, rg * RG + e / (D / 8));
@@ -655,14 +657,11 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
   }
   const int64_t T = int64_t(Ptot) * Hkv * (kPair ? 1 : RGs);
   const int64_t s_u = int64_t(kPair ? g : gr) * Ptot + cb0, e_u = s_u + npg;
-  // share of tile t: floor(((t + 1) W - 1) / T) for equal shares
-  const int k0 = kPair ? int(((s_u + 1) * W - 1) / T) : share_of(s_u, T);
-  const int k1 = kPair ? int((e_u * W - 1) / T) : share_of(e_u - 1, T);
+  constexpr int WPG = kPair ? 1 : kWaves;  // shares per workgroup of the streaming kernel
+  const int k0 = share_of<WPG>(s_u, T), k1 = share_of<WPG>(e_u - 1, T);
   if (k0 == k1) return;  // written directly by its wave
-  // shares between k0 and k1 that hold no tile (T < W) wrote nothing: skip them
-  auto empty = [&](int k) {
-    return kPair ? pair_share_start(k, T) == pair_share_start(k + 1, T) : share_start(k, T) == share_start(k + 1, T);
-  };
+  // shares between k0 and k1 that hold no tile (T < 1024) wrote nothing: skip them
+  auto empty = [&](int k) { return share_start<WPG>(k, T) == share_start<WPG>(k + 1, T); };
   const float* __restrict__ ml = a.ws_ml;
   const float* __restrict__ accp = a.ws_acc;
   for (int e = threadIdx.x; e < RG * (D / 4); e += blockDim.x) {
