@@ -629,11 +629,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
 
 // Merge the partial states of units that cross share boundaries:
 // m* = max m_s, out = sum_s 2^(m_s - m*) acc_s / sum_s 2^(m_s - m*) l_s.
-// Also writes zeros for empty units (softmax over nothing).  One thread per
-// (row, 4 head dims), all loads of a pass issued before any is used, so a unit
-// costs about two memory round trips.
+// Also writes zeros for empty units (softmax over nothing).  256 threads per
+// unit, each one row and 16 consecutive head dims (64 contiguous bytes of
+// every share's partial accumulator), merging the shares in one online pass.
 template <int D, int MODE>
-__global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int Hkv = a.pool.num_kv_heads, RGs = a.plan.rowgroups;
   const int B = MODE == kCascade ? load_uniform(a.ws_units + 3 * a.batch) : a.batch;
   const int unit = blockIdx.x;  // (gr, b) with b fastest, over the launch's batch
@@ -664,32 +664,38 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a) {
   auto empty = [&](int k) { return share_start<WPG>(k, T) == share_start<WPG>(k + 1, T); };
   const float* __restrict__ ml = a.ws_ml;
   const float* __restrict__ accp = a.ws_acc;
-  for (int e = threadIdx.x; e < RG * (D / 4); e += blockDim.x) {
-    const int rl = e / (D / 4), d4 = e % (D / 4);
+  // thread: one row, 16 consecutive head dims (D/16 threads per row)
+  constexpr int TPR = D / 16, RPP = 256 / TPR;
+  const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
+  auto slot_of = [&](int k) { return int64_t(k * 2 + (k == k0)) * (kPair ? 2 : 1) + (kPair ? rg : 0); };
+  for (int r0 = 0; r0 < RG; r0 += RPP) {
+    const int rl = r0 + tr;
+    if (rl >= RG) break;
     const int64_t row = unit_row<MODE>(a, b, g, rg * RG + rl);
     if (row < 0) continue;
-    // slot of share k: its "started before" slot (0) except the first share (1)
-    auto slot_of = [&](int k) { return int64_t(k * 2 + (k == k0)) * (kPair ? 2 : 1) + (kPair ? rg : 0); };
-    // one pass, merging online: the shares' loads do not wait on a first max pass
     float M = -INFINITY, den = 0.f;
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+    f32x4 num[4] = {};
+#pragma unroll 2
     for (int k = k0; k <= k1; ++k) {
       if (empty(k)) continue;
       const int64_t slot = slot_of(k);
-      const float ms = ml[(slot * RG + rl) * 2];
-      const float ls = ml[(slot * RG + rl) * 2 + 1];
-      const f32x4 as = reinterpret_cast<const f32x4*>(accp + (slot * RG + rl) * D)[d4];
-      if (ms == -INFINITY) continue;  // the share saw no key of this row
-      const float Mn = fmaxf(M, ms);
-      const float c = exp2_fast(M - Mn), w = exp2_fast(ms - Mn);  // exp2(-inf) = 0
-      den = den * c + w * ls;
-      num = num * c + w * as;
+      const f32x2 mlv = *reinterpret_cast<const f32x2*>(ml + (slot * RG + rl) * 2);
+      const f32x4* ap = reinterpret_cast<const f32x4*>(accp + (slot * RG + rl) * D) + 4 * tc;
+      f32x4 av[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = ap[i];
+      if (mlv[0] == -INFINITY) continue;  // the share saw no key of this row
+      const float Mn = fmaxf(M, mlv[0]);
+      const float c = exp2_fast(M - Mn), w = exp2_fast(mlv[0] - Mn);  // exp2(-inf) = 0
+      den = den * c + w * mlv[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) num[i] = num[i] * c + w * av[i];
       M = Mn;
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    reinterpret_cast<u32x2*>(a.out + row * D)[d4] =
-        pack_bf16x4(num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
+    u32x2* o = reinterpret_cast<u32x2*>(a.out + row * D) + 4 * tc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x4(num[i][0] * inv, num[i][1] * inv, num[i][2] * inv, num[i][3] * inv);
   }
 }
 
@@ -861,8 +867,7 @@ hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units = a.pool.num_kv_heads * a.plan.rowgroups * a.batch;
-  const int threads = min(1024, a.plan.rg_rows * (D / 4));
-  hipLaunchKernelGGL((decode_combine_kernel<D, MODE>), dim3(units), dim3(threads), 0, stream, a);
+  hipLaunchKernelGGL((decode_combine_kernel<D, MODE>), dim3(units), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -880,7 +885,7 @@ hipError_t launch_decode_cascade(const DecodeArgs& a, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units = a.pool.num_kv_heads * a.plan.rowgroups * a.batch;
-  hipLaunchKernelGGL((decode_combine_kernel<D, kCascade>), dim3(units), dim3(a.plan.rg_rows * (D / 4)), 0, stream, a);
+  hipLaunchKernelGGL((decode_combine_kernel<D, kCascade>), dim3(units), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
