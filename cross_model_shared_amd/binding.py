@@ -46,6 +46,8 @@ _SIGNATURES = {
                                                 _i32, _i32, _f, _vp, _sz, _vp, _vp]),
     "partial_prefill_extend": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                               _i32, _i32, _i32, _i32, _i32, _f, _vp, _vp]),
+    "partial_prefill_layers": (ctypes.c_int, [_pool_p, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                                              _i32, _i32, _i32, _i32, _i32, _f, _vp, _vp]),
     "kv_pages_buffer_bytes": (_sz, [_pool_p, _i32, _i32]),
     "kv_pages_pack": (ctypes.c_int, [_pool_p, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
     "kv_pages_unpack": (ctypes.c_int, [_pool_p, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
@@ -235,6 +237,24 @@ def extend(pool: Pool, layer, q, k_new, v_new, out, cu_new, block_table, seq_len
     _check(load().partial_prefill_extend(
         pool.struct, layer, _ptr(q, "q", torch.bfloat16), _ptr(k_new, "k_new", torch.bfloat16, T * row),
         _ptr(v_new, "v_new", torch.bfloat16, T * row), _ptr(out, "out", torch.bfloat16),
+        _ptr(cu_new, "cu_new", torch.int32, batch + 1), _ptr(block_table, "block_table", torch.int32),
+        block_table.shape[1], _ptr(seq_lens, "seq_lens", torch.int32), batch, Hq, T, max_new,
+        max_seq_len, float(scale), _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True),
+        _stream(stream)))
+
+
+def extend_layers(pool: Pool, layer_begin, q, k_new, v_new, out, cu_new, block_table, seq_lens, max_new,
+                  max_seq_len, scale, dev_status=None, stream=None):
+    """partial_prefill_layers: q, out bf16 [L, T, H_q, D]; k_new, v_new bf16 [L, T, H_kv, D]."""
+    torch = _torch()
+    L, T, Hq, D = q.shape
+    batch = seq_lens.numel()
+    row = pool.num_kv_heads * pool.head_dim
+    if D != pool.head_dim or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q/out shape does not match the pool")
+    _check(load().partial_prefill_layers(
+        pool.struct, layer_begin, L, _ptr(q, "q", torch.bfloat16), _ptr(k_new, "k_new", torch.bfloat16, L * T * row),
+        _ptr(v_new, "v_new", torch.bfloat16, L * T * row), _ptr(out, "out", torch.bfloat16),
         _ptr(cu_new, "cu_new", torch.int32, batch + 1), _ptr(block_table, "block_table", torch.int32),
         block_table.shape[1], _ptr(seq_lens, "seq_lens", torch.int32), batch, Hq, T, max_new,
         max_seq_len, float(scale), _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True),

@@ -18,7 +18,7 @@ template <int D>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int w = blockIdx.x;
   const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  const int b = blockIdx.z % a.batch, l = blockIdx.z / a.batch;  // session, layer of the range
   const int Hkv = a.pool.num_kv_heads;
   const int P = a.seq_lens[b];
   const int c0 = a.cu_new[b], c1 = a.cu_new[b + 1];
@@ -36,11 +36,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     if (threadIdx.x == 0) flag_error(a.dev_status, 1);
     return;
   }
-  uint16_t* tile = a.pool.data + tile_offset(a.layer, pid, h, a.pool.num_pages, Hkv, D);
+  uint16_t* tile = a.pool.data + tile_offset(a.layer + l, pid, h, a.pool.num_pages, Hkv, D);
   const int64_t row_stride = int64_t(Hkv) * D;
   // new row of logical position t is c0 + (t - P)
-  const uint16_t* ksrc = a.k_new + int64_t(h) * D;
-  const uint16_t* vsrc = a.v_new + int64_t(h) * D;
+  const uint16_t* ksrc = a.k_new + l * a.kv_lstride + int64_t(h) * D;
+  const uint16_t* vsrc = a.v_new + l * a.kv_lstride + int64_t(h) * D;
 
   // K: one thread per (slot, 8-value run)
   for (int e = threadIdx.x; e < kPage * (D / 8); e += 256) {
@@ -80,9 +80,22 @@ template <int D>
 hipError_t launch_append_t(const AppendArgs& a, hipStream_t stream) {
   // a window of new tokens starting mid-page can touch one page more
   const int windows = (a.max_new + kPage - 1) / kPage + 1;
-  dim3 grid(windows, a.pool.num_kv_heads, a.batch);
-  hipLaunchKernelGGL((append_kernel<D>), grid, dim3(256), 0, stream, a);
-  return hipGetLastError();
+  if (int64_t(a.batch) * a.num_layers <= 65535) {
+    dim3 grid(windows, a.pool.num_kv_heads, a.batch * a.num_layers);
+    hipLaunchKernelGGL((append_kernel<D>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  for (int l = 0; l < a.num_layers; ++l) {  // grid.z holds at most 65535 (session, layer) pairs
+    AppendArgs one = a;
+    one.layer = a.layer + l;
+    one.k_new = a.k_new + l * a.kv_lstride;
+    one.v_new = a.v_new + l * a.kv_lstride;
+    one.num_layers = 1;
+    hipLaunchKernelGGL((append_kernel<D>), dim3(windows, a.pool.num_kv_heads, a.batch), dim3(256), 0, stream, one);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace

@@ -245,13 +245,16 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
   __shared__ u32x4 ring[kStages][2 * TILE + kPad];
 
   const int Hkv = a.pool.num_kv_heads;
-  const int units = a.batch * Hkv;
+  const int units = a.num_layers * a.batch * Hkv;  // (layer, session, KV head), KV head fastest
   const int xcd = blockIdx.x % kXcds;
   const int kk = blockIdx.x / kXcds;
   const int unit = (kk / row_blocks) * kXcds + xcd;
   const int rb = kk % row_blocks;
   if (unit >= units) return;
-  const int b = unit / Hkv, g = unit % Hkv;
+  const int l = unit / (a.batch * Hkv), b = (unit / Hkv) % a.batch, g = unit % Hkv;
+  const int layer = a.layer + l;
+  const uint16_t* const qbase = a.q + l * a.q_lstride;
+  uint16_t* const obase = a.out + l * a.q_lstride;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.num_q_heads / Hkv;
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
     rvalid[cb] = r < rows;
     const int i = rvalid[cb] ? r / G : C - 1;
     lim_abs[cb] = P + i + 1;
-    const uint16_t* qrow = a.q + (int64_t(c0 + i) * a.num_q_heads + g * G + (rvalid[cb] ? r % G : 0)) * D;
+    const uint16_t* qrow = qbase + (int64_t(c0 + i) * a.num_q_heads + g * G + (rvalid[cb] ? r % G : 0)) * D;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
       qf[cb][s] = rvalid[cb] ? scale_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * (lane >> 4)),
@@ -306,7 +309,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
         __builtin_amdgcn_s_waitcnt(0);
         pid = 0;  // in-range stand-in; the session's output is unspecified
       }
-      const u32x4* tile = reinterpret_cast<const u32x4*>(a.pool.data + tile_offset(a.layer, pid, g, num_pages, Hkv, D));
+      const u32x4* tile = reinterpret_cast<const u32x4*>(a.pool.data + tile_offset(layer, pid, g, num_pages, Hkv, D));
       u32x4* dst = &ring[k % kStages][h * (TILE + kPad)];
 #pragma unroll
       for (int j = 0; j < PER_PAGE; ++j)
@@ -508,7 +511,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
     const int r = r0 + cb * 16 + (ln & 15);
     if (r >= rows) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* o = a.out + (int64_t(c0 + r / Gq) * a.num_q_heads + g * Gq + r % Gq) * D;
+    uint16_t* o = obase + (int64_t(c0 + r / Gq) * a.num_q_heads + g * Gq + r % Gq) * D;
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
       const f32x4 v = st.acc[cb][i] * inv;
@@ -522,9 +525,9 @@ hipError_t launch_extend_t(const ExtendArgs& a, hipStream_t stream) {
   constexpr int kRowsPerBlock = WAVES * 16 * NB;
   const int G = a.num_q_heads / a.pool.num_kv_heads;
   const int row_blocks = (a.max_new * G + kRowsPerBlock - 1) / kRowsPerBlock;
-  const int units = a.batch * a.pool.num_kv_heads;
-  const int unit_rounds = (units + kXcds - 1) / kXcds;
-  const int64_t blocks = int64_t(unit_rounds) * row_blocks * kXcds;
+  const int64_t units = int64_t(a.num_layers) * a.batch * a.pool.num_kv_heads;
+  const int64_t unit_rounds = (units + kXcds - 1) / kXcds;
+  const int64_t blocks = unit_rounds * row_blocks * kXcds;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((extend_kernel<D, NB, WAVES, STAGES, LOOK, PER_CU, PIPE>), dim3(unsigned(blocks)), dim3(64 * WAVES), 0,
                      stream, a, row_blocks);

@@ -23,6 +23,10 @@ struct AppendArgs {
   const int32_t* seq_lens;
   int batch, total_new, max_new, max_seq_len;
   int32_t* dev_status;
+  // a range of layers [layer, layer + num_layers): layer l's rows start
+  // l * kv_lstride elements into k_new / v_new
+  int num_layers = 1;
+  int64_t kv_lstride = 0;
 };
 
 // Largest batch a decode call accepts (the per-session page prefix sum lives in LDS).
@@ -94,6 +98,10 @@ struct ExtendArgs {
   int batch, num_q_heads, total_new, max_new, max_seq_len;
   float scale_log2;
   int32_t* dev_status;
+  // a range of layers [layer, layer + num_layers): layer l's q and out rows
+  // start l * q_lstride elements in
+  int num_layers = 1;
+  int64_t q_lstride = 0;
 };
 
 // Page handoff: a contiguous transfer buffer [num_layers][num_ids][H_kv][tile].

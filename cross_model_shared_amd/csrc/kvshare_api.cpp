@@ -252,35 +252,69 @@ int shared_kv_decode_cascade(const kvs_pool* pool, int32_t layer, const void* q,
                        max_seq_len, 0, scale, workspace, workspace_bytes, dev_status, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+int extend_common(const char* name, const kvs_pool* pool, int32_t layer, int32_t num_layers, const void* q,
+                  const void* k_new, const void* v_new, void* out, const int32_t* cu_new, const int32_t* block_table,
+                  int32_t bt_stride, const int32_t* seq_lens, int32_t batch, int32_t num_q_heads, int32_t total_new,
+                  int32_t max_new, int32_t max_seq_len, float scale, int32_t* dev_status, hipStream_t stream) {
+  int s = check_pool(pool, layer);
+  if (s) return s;
+  if (num_layers <= 0 || int64_t(layer) + num_layers > pool->num_layers)
+    return fail(KVS_ERANGE, "%s: layers [%d, %d + %d) outside the pool's %d", name, layer, layer, num_layers,
+                pool->num_layers);
+  if (!q || !k_new || !v_new || !out || !cu_new || !block_table || !seq_lens)
+    return fail(KVS_EINVAL, "%s: a required pointer is NULL", name);
+  if ((s = check_table(batch, bt_stride, max_seq_len))) return s;
+  if (num_q_heads <= 0 || max_new <= 0 || total_new < 0)
+    return fail(KVS_EINVAL, "%s: num_q_heads %d, max_new %d must be >= 1", name, num_q_heads, max_new);
+  if (max_new > max_seq_len)
+    return fail(KVS_ERANGE, "%s: max_new %d exceeds max_seq_len %d", name, max_new, max_seq_len);
+  if (num_q_heads % pool->num_kv_heads)
+    return fail(KVS_EUNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                pool->num_kv_heads);
+  if (!(scale > 0.f) || scale != scale) return fail(KVS_EINVAL, "%s: scale must be a positive number", name);
+  const int64_t units = int64_t(num_layers) * batch * pool->num_kv_heads;
+  if (units > (int64_t(1) << 30))
+    return fail(KVS_EUNSUPPORTED, "%s: %lld (layer, session, KV head) units in one call", name, (long long)units);
+  const int64_t kv_stride = int64_t(total_new) * pool->num_kv_heads * pool->head_dim;
+  const int64_t q_stride = int64_t(total_new) * num_q_heads * pool->head_dim;
+  kvs::AppendArgs ap{view(pool), layer, static_cast<const uint16_t*>(k_new),
+                     static_cast<const uint16_t*>(v_new), cu_new, block_table, bt_stride, seq_lens,
+                     batch, total_new, max_new, max_seq_len, dev_status, num_layers, kv_stride};
+  char what[96];
+  snprintf(what, sizeof what, "%s (append)", name);
+  if ((s = launched(kvs::launch_append(ap, stream), what))) return s;
+  kvs::ExtendArgs a{view(pool), layer, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+                    cu_new, block_table, bt_stride, seq_lens, batch, num_q_heads, total_new, max_new,
+                    max_seq_len, scale * 1.4426950408889634f, dev_status, num_layers, q_stride};
+  return launched(kvs::launch_extend(a, stream), name);
+}
+
+}  // namespace
+
+extern "C" {
+
 int partial_prefill_extend(const kvs_pool* pool, int32_t layer, const void* q, const void* k_new,
                            const void* v_new, void* out, const int32_t* cu_new,
                            const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
                            int32_t batch, int32_t num_q_heads, int32_t total_new, int32_t max_new,
                            int32_t max_seq_len, float scale, int32_t* dev_status, hipStream_t stream) {
-  int s = check_pool(pool, layer);
-  if (s) return s;
-  if (!q || !k_new || !v_new || !out || !cu_new || !block_table || !seq_lens)
-    return fail(KVS_EINVAL, "partial_prefill_extend: a required pointer is NULL");
-  if ((s = check_table(batch, bt_stride, max_seq_len))) return s;
-  if (num_q_heads <= 0 || max_new <= 0 || total_new < 0)
-    return fail(KVS_EINVAL, "partial_prefill_extend: num_q_heads %d, max_new %d must be >= 1",
-                num_q_heads, max_new);
-  if (max_new > max_seq_len)
-    return fail(KVS_ERANGE, "partial_prefill_extend: max_new %d exceeds max_seq_len %d", max_new,
-                max_seq_len);
-  if (num_q_heads % pool->num_kv_heads)
-    return fail(KVS_EUNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
-                pool->num_kv_heads);
-  if (!(scale > 0.f) || scale != scale)
-    return fail(KVS_EINVAL, "partial_prefill_extend: scale must be a positive number");
-  kvs::AppendArgs ap{view(pool), layer, static_cast<const uint16_t*>(k_new),
-                     static_cast<const uint16_t*>(v_new), cu_new, block_table, bt_stride, seq_lens,
-                     batch, total_new, max_new, max_seq_len, dev_status};
-  if ((s = launched(kvs::launch_append(ap, stream), "partial_prefill_extend (append)"))) return s;
-  kvs::ExtendArgs a{view(pool), layer, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
-                    cu_new, block_table, bt_stride, seq_lens, batch, num_q_heads, total_new, max_new,
-                    max_seq_len, scale * 1.4426950408889634f, dev_status};
-  return launched(kvs::launch_extend(a, stream), "partial_prefill_extend");
+  return extend_common("partial_prefill_extend", pool, layer, 1, q, k_new, v_new, out, cu_new, block_table,
+                       bt_stride, seq_lens, batch, num_q_heads, total_new, max_new, max_seq_len, scale, dev_status,
+                       stream);
+}
+
+int partial_prefill_layers(const kvs_pool* pool, int32_t layer_begin, int32_t num_layers, const void* q,
+                           const void* k_new, const void* v_new, void* out, const int32_t* cu_new,
+                           const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                           int32_t batch, int32_t num_q_heads, int32_t total_new, int32_t max_new,
+                           int32_t max_seq_len, float scale, int32_t* dev_status, hipStream_t stream) {
+  return extend_common("partial_prefill_layers", pool, layer_begin, num_layers, q, k_new, v_new, out, cu_new,
+                       block_table, bt_stride, seq_lens, batch, num_q_heads, total_new, max_new, max_seq_len, scale,
+                       dev_status, stream);
 }
 
 size_t kv_pages_buffer_bytes(const kvs_pool* pool, int32_t num_layers, int32_t num_ids) {

@@ -21,6 +21,8 @@
  *   kv_pool_fetch          logical K/V rows back out of the pool (inverse of kv_pool_append)
  *   partial_prefill_extend append a chunk, then causal attention of the chunk
  *                          over cached prefix + chunk           (partial prefill)
+ *   partial_prefill_layers the same over a contiguous range of layers in one launch
+ *                          (recompute of a layer group)
  *
  * ---------------------------------------------------------------------------
  * Conventions common to every entry point
@@ -264,6 +266,32 @@ int partial_prefill_extend(const kvs_pool* pool, int32_t layer, const void* q, c
                            int32_t batch, int32_t num_q_heads, int32_t total_new, int32_t max_new,
                            int32_t max_seq_len, float scale, int32_t* dev_status,
                            hipStream_t stream);
+
+/*
+ * partial_prefill_layers — partial_prefill_extend for the layers
+ * [layer_begin, layer_begin + num_layers) of the pool, in one launch.
+ *
+ * "DroidSpeak: KV Cache Sharing for Cross-LLM Communication and Multi-LLM
+ * Serving", sections 5.1 and 5.4: a receiving model reuses a sender's KV for most
+ * layers and recomputes one contiguous layer group (one transition point, so the
+ * layer inputs cross over once); its partial_prefill interface runs the prefill
+ * of that group.  The attention part of that prefill is this call: for every
+ * layer l of the range, the layer's new K/V rows are appended into pool layer
+ * layer_begin + l (through the same block table; recomputing a whole prompt is
+ * seq_lens = 0), then the rows attend as in partial_prefill_extend.  The
+ * projections that produce q, k and v from the layer inputs are the caller's.
+ *
+ *  q, out        bf16 [num_layers][total_new][num_q_heads][head_dim].
+ *  k_new, v_new  bf16 [num_layers][total_new][num_kv_heads][head_dim].
+ *  Other arguments as for partial_prefill_extend, shared by every layer.
+ *  KVS_ERANGE when the range leaves the pool.  The result equals num_layers
+ *  partial_prefill_extend calls, bit for bit.
+ */
+int partial_prefill_layers(const kvs_pool* pool, int32_t layer_begin, int32_t num_layers, const void* q,
+                           const void* k_new, const void* v_new, void* out, const int32_t* cu_new,
+                           const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                           int32_t batch, int32_t num_q_heads, int32_t total_new, int32_t max_new,
+                           int32_t max_seq_len, float scale, int32_t* dev_status, hipStream_t stream);
 
 /*
  * kv_pages_pack / kv_pages_unpack — move whole pages between a pool and a

@@ -33,7 +33,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol(L):
     names = header_functions()
     assert {"kv_pool_append", "shared_kv_decode", "shared_kv_decode_private", "shared_kv_decode_cascade",
-            "partial_prefill_extend",
+            "partial_prefill_extend", "partial_prefill_layers",
             "kv_pages_pack", "kv_pages_unpack", "kv_pages_buffer_bytes", "kv_pool_fetch", "kvs_pool_bytes",
             "shared_kv_decode_workspace_bytes", "kvs_last_error", "kvs_version",
             "kvs_prefix_cache_create", "kvs_prefix_cache_admit", "kvs_prefix_cache_publish",
@@ -173,6 +173,28 @@ def call_extend(L, p, q=FAKE, k=FAKE, v=FAKE, out=FAKE, cu=FAKE, bt=FAKE, stride
 def test_extend_host_checks(L, kw, status):
     p = kw.pop("p")
     assert call_extend(L, p, **kw) == status
+
+
+def call_layers(L, p, lb=0, nl=2, q=FAKE, k=FAKE, v=FAKE, out=FAKE, cu=FAKE, bt=FAKE, stride=4, lens=FAKE,
+                batch=2, Hq=8, total=10, max_new=8, msl=64, scale=0.125):
+    return L.partial_prefill_layers(ctypes.byref(p), lb, nl, q, k, v, out, cu, bt, stride, lens, batch, Hq, total,
+                                    max_new, msl, scale, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=pool(layers=3), lb=2, nl=2), binding.KVS_ERANGE),
+    (dict(p=pool(layers=3), lb=0, nl=0), binding.KVS_ERANGE),
+    (dict(p=pool(layers=3), lb=-1, nl=1), binding.KVS_ERANGE),
+    (dict(p=pool(layers=3), lb=3, nl=1), binding.KVS_ERANGE),
+    (dict(p=pool(layers=3), k=None), binding.KVS_EINVAL),
+    (dict(p=pool(layers=3), Hq=5), binding.KVS_EUNSUPPORTED),
+    (dict(p=pool(layers=3), msl=1000), binding.KVS_ERANGE),
+    (dict(p=pool(layers=3, dim=96)), binding.KVS_EUNSUPPORTED),
+])
+def test_extend_layers_host_checks(L, kw, status):
+    kw = dict(kw)
+    p = kw.pop("p")
+    assert call_layers(L, p, **kw) == status
 
 
 @pytest.mark.parametrize("unpack", [False, True])

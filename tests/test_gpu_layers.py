@@ -1,0 +1,123 @@
+"""GPU parity of partial_prefill_layers: the attention part of recomputing a
+contiguous layer group (DroidSpeak, sections 5.1 and 5.4), i.e. partial prefill
+over a range of pool layers in one launch.  Each layer's rows must match the
+float64 oracle within 2e-2, the whole call must equal one partial_prefill_extend
+per layer bit for bit (outputs and pool), and layers outside the range must not
+change."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from cross_model_shared_amd import binding
+from cross_model_shared_amd import workload as wlmod
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+
+
+def build(prefix, new, layers, Hkv, G, D, seed):
+    """A pool of `layers` layers whose sessions hold `prefix` tokens in every layer,
+    plus the per-layer chunks (logical K/V kept for the oracle)."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+    full = [p + c for p, c in zip(prefix, new)]
+    bt, num_pages = wlmod.build_block_table(full, seed)
+    pool = binding.Pool(layers, num_pages, Hkv, D, fill=np.int16(np.uint16(gu.POISON_NAN).view(np.int16)))
+    st = gu.status_tensor()
+    fk = [[wlmod.draw_bf16(rng, (L, Hkv, D), 1.0) for L in full] for _ in range(layers)]
+    fv = [[wlmod.draw_bf16(rng, (L, Hkv, D), 1.0) for L in full] for _ in range(layers)]
+    msl = max(full)
+    for l in range(layers):
+        pk, cu = wlmod.concat_rows([k[:p] for k, p in zip(fk[l], prefix)])
+        pv, _ = wlmod.concat_rows([v[:p] for v, p in zip(fv[l], prefix)])
+        if pk.shape[0]:
+            binding.append(pool, l, gu.dev_bf16(pk), gu.dev_bf16(pv), gu.dev_i32(cu), gu.dev_i32(bt),
+                           gu.dev_i32(np.zeros(len(prefix))), max_new=msl, max_seq_len=msl, dev_status=st)
+    cu_new = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    T = int(cu_new[-1])
+    kn = np.stack([wlmod.concat_rows([k[p:] for k, p in zip(fk[l], prefix)])[0] for l in range(layers)])
+    vn = np.stack([wlmod.concat_rows([v[p:] for v, p in zip(fv[l], prefix)])[0] for l in range(layers)])
+    q = wlmod.draw_bf16(rng, (layers, T, Hkv * G, D), 1.0)
+    gu.sync()
+    return dict(pool=pool, st=st, bt=bt, fk=fk, fv=fv, kn=kn, vn=vn, q=q, cu=cu_new, prefix=prefix, new=new,
+                msl=msl, D=D, layers=layers)
+
+
+@pytest.mark.parametrize("D,G", [(128, 4), (64, 1)])
+def test_layer_range_matches_oracle_and_per_layer_calls(D, G):
+    import torch
+
+    prefix, new, layers, lb, nl = [40, 0, 300, 16], [9, 70, 160, 1], 5, 1, 3
+    print(f"[layers] D={D} G={G} range [{lb}, {lb + nl})", flush=True)
+    c = build(prefix, new, layers, 2, G, D, seed=D + G)
+    twin = build(prefix, new, layers, 2, G, D, seed=D + G)
+    before = gu.pool_bits(c["pool"]).copy()
+    T, Hq = c["q"].shape[1], c["q"].shape[2]
+    scale = 1.0 / math.sqrt(D)
+    out = torch.empty((nl, T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    binding.extend_layers(c["pool"], lb, gu.dev_bf16(c["q"][lb:lb + nl]), gu.dev_bf16(c["kn"][lb:lb + nl]),
+                          gu.dev_bf16(c["vn"][lb:lb + nl]), out, gu.dev_i32(c["cu"]), gu.dev_i32(c["bt"]),
+                          gu.dev_i32(c["prefix"]), max(new), c["msl"], scale, dev_status=c["st"])
+    gu.sync()
+    assert int(c["st"].item()) == 0
+    got = gu.host_f64(out)
+    # the oracle, layer by layer
+    for i in range(nl):
+        l = lb + i
+        for b in range(len(prefix)):
+            rows = list(range(new[b]))
+            want = oracle.extend_from_logical(c["q"][l][c["cu"][b]:c["cu"][b + 1]], c["fk"][l][b], c["fv"][l][b],
+                                              prefix[b], rows, scale)
+            err = float(np.max(np.abs(got[i][c["cu"][b]:c["cu"][b + 1]] - want))) if rows else 0.0
+            assert err <= TOL, (l, b, err)
+    # one partial_prefill_extend per layer gives the same bits
+    for i in range(nl):
+        l = lb + i
+        o = torch.empty((T, Hq, D), dtype=torch.bfloat16, device="cuda")
+        binding.extend(twin["pool"], l, gu.dev_bf16(c["q"][l]), gu.dev_bf16(c["kn"][l]), gu.dev_bf16(c["vn"][l]), o,
+                       gu.dev_i32(c["cu"]), gu.dev_i32(c["bt"]), gu.dev_i32(c["prefix"]), max(new), c["msl"], scale,
+                       dev_status=twin["st"])
+        gu.sync()
+        assert np.array_equal(gu.host_bits(o), gu.host_bits(out[i])), l
+    after = gu.pool_bits(c["pool"])
+    assert np.array_equal(after, gu.pool_bits(twin["pool"]))
+    # layers outside the range did not change
+    per_layer = after.size // layers
+    for l in list(range(lb)) + list(range(lb + nl, layers)):
+        assert np.array_equal(after[l * per_layer:(l + 1) * per_layer], before[l * per_layer:(l + 1) * per_layer]), l
+
+
+def test_whole_prompt_recompute_of_a_layer_group():
+    """seq_lens = 0: every prompt token is new in every layer of the group (a
+    layer group recomputed from its inputs), 2 layers of a 4-layer pool."""
+    import torch
+
+    prefix, new, layers, lb, nl, D, G = [0, 0, 0], [200, 33, 129], 4, 2, 2, 128, 4
+    c = build(prefix, new, layers, 2, G, D, seed=5)
+    T, Hq = c["q"].shape[1], c["q"].shape[2]
+    scale = 1.0 / math.sqrt(D)
+    out = torch.empty((nl, T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    binding.extend_layers(c["pool"], lb, gu.dev_bf16(c["q"][lb:]), gu.dev_bf16(c["kn"][lb:]), gu.dev_bf16(c["vn"][lb:]),
+                          out, gu.dev_i32(c["cu"]), gu.dev_i32(c["bt"]), gu.dev_i32(prefix), max(new), c["msl"],
+                          scale, dev_status=c["st"])
+    gu.sync()
+    got = gu.host_f64(out)
+    for i in range(nl):
+        for b in range(len(new)):
+            want = oracle.extend_from_logical(c["q"][lb + i][c["cu"][b]:c["cu"][b + 1]], c["fk"][lb + i][b],
+                                              c["fv"][lb + i][b], 0, list(range(new[b])), scale)
+            assert float(np.max(np.abs(got[i][c["cu"][b]:c["cu"][b + 1]] - want))) <= TOL
+    assert int(c["st"].item()) == 0
