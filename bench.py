@@ -33,6 +33,7 @@ EXTEND_WORKLOAD = "extend_8k_512"
 PRIVATE_WORKLOAD = "qwen3_8b_n8_private"
 HANDOFF_WORKLOAD = "handoff_8k"
 CASCADE_WORKLOAD = "qwen3_8b_n8_cascade"
+LAYER_GROUP_WORKLOAD = "llama8b_layer_group"
 
 
 def log(msg):
@@ -50,6 +51,8 @@ def parse():
     ap.add_argument("--no-private", action="store_true", help="skip the private-suffix decode section")
     ap.add_argument("--no-handoff", action="store_true", help="skip the page handoff section")
     ap.add_argument("--no-cascade", action="store_true", help="skip the shared-prefix cascade section")
+    ap.add_argument("--no-layer-group", action="store_true", help="skip the layer-group recompute section")
+    ap.add_argument("--layer-group-calls", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -377,6 +380,67 @@ def cascade_section(calls):
     return res
 
 
+def layer_group_section(calls):
+    """partial_prefill_layers over a 4-layer group (full prompts, no cached prefix) against one
+    partial_prefill_extend per layer, on the same inputs."""
+    import torch
+
+    from cross_model_shared_amd import binding
+    from cross_model_shared_amd import workload as W
+
+    wl = W.make_workload(LAYER_GROUP_WORKLOAD)
+    B, Hq, Hkv, D = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    lb, nl = wl.layer_group
+    full = wl.total_lens()
+    bt, num_pages = W.build_block_table(full, wl.seed)
+    pool = binding.Pool(wl.num_layers, num_pages, Hkv, D)
+    btd = torch.from_numpy(bt).cuda()
+    T = sum(wl.new)
+    q = W.device_normal_bf16(nl * T * Hq * D, wl.std, W.mix_seed(wl.seed, 70)).view(nl, T, Hq, D)
+    kn = W.device_normal_bf16(nl * T * Hkv * D, wl.std, W.mix_seed(wl.seed, 71)).view(nl, T, Hkv, D)
+    vn = W.device_normal_bf16(nl * T * Hkv * D, wl.std, W.mix_seed(wl.seed, 72)).view(nl, T, Hkv, D)
+    out = torch.empty_like(q)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(wl.new)]), dtype=torch.int32, device="cuda")
+    pre = torch.tensor(wl.prefix, dtype=torch.int32, device="cuda")
+    mx, msl = max(wl.new), max(full)
+
+    def group():
+        binding.extend_layers(pool, lb, q, kn, vn, out, cu, btd, pre, mx, msl, wl.scale)
+
+    def per_layer():
+        for i in range(nl):
+            binding.extend(pool, lb + i, q[i], kn[i], vn[i], out[i], cu, btd, pre, mx, msl, wl.scale)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t = EventTimer()
+        for _ in range(calls):
+            e = t.start()
+            fn()
+            t.stop(e)
+        torch.cuda.synchronize()
+        return float(np.median(t.all_ms()))
+
+    ms_g = timed(group)
+    ms_l = timed(per_layer)
+    flops = nl * extend_flops(wl.prefix, wl.new, Hq, D)
+    tf = flops / (ms_g * 1e-3) / 1e12
+    res = {
+        "workload": f"{LAYER_GROUP_WORKLOAD}: layers [{lb}, {lb + nl}) of a {wl.num_layers}-layer pool recomputed "
+                    f"for {B} prompts of {wl.new[0]} tokens (no cached prefix), 32 q / 8 KV heads, D={D}",
+        "value": round(tf, 1), "unit": "TFLOP/s", "ms_per_call": round(ms_g, 4), "flops_per_call": flops,
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "per_layer_calls_ms": round(ms_l, 4), "speedup_over_per_layer_calls": round(ms_l / ms_g, 3),
+    }
+    log(f"[bench] layer group {ms_g:.3f} ms ({tf:.1f} TFLOP/s), {nl} per-layer calls {ms_l:.3f} ms")
+    del pool, q, kn, vn, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def handoff_section(reps):
     """kv_pages_pack / kv_pages_unpack of every page of the handoff workload (all 36 layers) and
     kv_pool_fetch of its rows (all layers); HBM bytes = what is read + what is written."""
@@ -576,6 +640,7 @@ def main():
     private = None if args.no_private else private_section(args.private_calls)
     handoff = None if args.no_handoff else handoff_section(10)
     cascade = None if args.no_cascade else cascade_section(20)
+    layer_group = None if args.no_layer_group else layer_group_section(args.layer_group_calls)
 
     res = {
         "metric": "shared-KV decode attn KV GB/s (% HBM peak) at N=8 decoders; extend TFLOP/s",
@@ -611,6 +676,7 @@ def main():
         "private": private,
         "handoff": handoff,
         "cascade": cascade,
+        "layer_group": layer_group,
         "extend": {
             "workload": f"{EXTEND_WORKLOAD}: B=16, cached prefix 8192 + 512 new tokens, 32 q / 8 KV heads, "
                         f"D=128 (partial_prefill_extend = append chunk + causal attention)",

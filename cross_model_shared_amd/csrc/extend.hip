@@ -249,7 +249,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
   const int xcd = blockIdx.x % kXcds;
   const int kk = blockIdx.x / kXcds;
   const int unit = (kk / row_blocks) * kXcds + xcd;
-  const int rb = kk % row_blocks;
+  const int rb = row_blocks - 1 - kk % row_blocks;  // heaviest (longest-key) row blocks first
   if (unit >= units) return;
   const int l = unit / (a.batch * Hkv), b = (unit / Hkv) % a.batch, g = unit % Hkv;
   const int layer = a.layer + l;

@@ -22,6 +22,9 @@ normal, no trained weights exist here):
                     to [4K, 128K], mean ~27K).
 * handoff_8k      — 4 sessions of 8K tokens, Qwen3-8B-shaped (8 KV heads, D=128),
                     36 layers: the cache a prefill worker hands to a decode worker.
+* llama8b_layer_group — Llama-3.1-8B-shaped (32 q / 8 KV heads, D=128, 32
+                    layers): 8 prompts of 4096 tokens recomputed in full (no cached
+                    prefix) in the 4-layer group [12, 16), one call for the group.
 * qwen3_8b_n8_cascade — Qwen3-8B-shaped N=8 decode of 64 sessions in 32 pairs;
                     each pair shares a prefix-cached prefix of 4K-8K tokens (whole
                     pages), and each session adds 0-8K tokens of its own.
@@ -58,6 +61,7 @@ class Workload:
     new: list = field(default_factory=list)       # extend: new chunk sizes
     priv: list = field(default_factory=list)      # decode: private suffix of decoder n of session b at b*N + n
     groups: list = field(default_factory=list)    # decode: (shared prefix tokens, [session lengths]) per group
+    layer_group: tuple = ()                       # extend: (first layer, layer count) recomputed together
 
     @property
     def group(self) -> int:
@@ -118,6 +122,10 @@ def make_workload(name: str, seed: int | None = None) -> Workload:
             groups.append((pre, [pre + int(x) for x in r.integers(0, 8192, size=2, endpoint=True)]))
         lens = [L for _, ls in groups for L in ls]
         return Workload(name, 64, 8, 32, 8, 128, 1, 1.0, s, "decode", lens=lens, groups=groups)
+    if name == "llama8b_layer_group":
+        s = 7 if seed is None else seed
+        return Workload(name, 8, 1, 32, 8, 128, 32, 1.0, s, "extend", prefix=[0] * 8, new=[4096] * 8,
+                        layer_group=(12, 4))
     if name == "handoff_8k":
         s = 5 if seed is None else seed
         return Workload(name, 4, 1, 32, 8, 128, 36, 1.0, s, "decode", lens=[8192] * 4)
@@ -134,7 +142,7 @@ def make_workload(name: str, seed: int | None = None) -> Workload:
 
 
 WORKLOADS = ("tiny", "llama8b_n4", "qwen3_8b_n8", "extend_8k_512", "qwen3_14b_long", "qwen3_8b_n8_private",
-             "handoff_8k", "qwen3_8b_n8_cascade")
+             "handoff_8k", "qwen3_8b_n8_cascade", "llama8b_layer_group")
 
 
 # ---------------------------------------------------------------------------
