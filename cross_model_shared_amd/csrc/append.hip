@@ -15,10 +15,11 @@ namespace kvs {
 namespace {
 
 template <int D>
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a, int z0) {
   const int w = blockIdx.x;
   const int h = blockIdx.y;
-  const int b = blockIdx.z % a.batch, l = blockIdx.z / a.batch;  // session, layer of the range
+  const int z = z0 + int(blockIdx.z);
+  const int b = z % a.batch, l = z / a.batch;  // session, layer of the range
   const int Hkv = a.pool.num_kv_heads;
   const int P = a.seq_lens[b];
   const int c0 = a.cu_new[b], c1 = a.cu_new[b + 1];
@@ -80,18 +81,11 @@ template <int D>
 hipError_t launch_append_t(const AppendArgs& a, hipStream_t stream) {
   // a window of new tokens starting mid-page can touch one page more
   const int windows = (a.max_new + kPage - 1) / kPage + 1;
-  if (int64_t(a.batch) * a.num_layers <= 65535) {
-    dim3 grid(windows, a.pool.num_kv_heads, a.batch * a.num_layers);
-    hipLaunchKernelGGL((append_kernel<D>), grid, dim3(256), 0, stream, a);
-    return hipGetLastError();
-  }
-  for (int l = 0; l < a.num_layers; ++l) {  // grid.z holds at most 65535 (session, layer) pairs
-    AppendArgs one = a;
-    one.layer = a.layer + l;
-    one.k_new = a.k_new + l * a.kv_lstride;
-    one.v_new = a.v_new + l * a.kv_lstride;
-    one.num_layers = 1;
-    hipLaunchKernelGGL((append_kernel<D>), dim3(windows, a.pool.num_kv_heads, a.batch), dim3(256), 0, stream, one);
+  // (layer, session) pairs on grid z, at most 65535 per launch
+  const int64_t zs = int64_t(a.batch) * a.num_layers;
+  for (int64_t z0 = 0; z0 < zs; z0 += 65535) {
+    const unsigned nz = unsigned(zs - z0 < 65535 ? zs - z0 : 65535);
+    hipLaunchKernelGGL((append_kernel<D>), dim3(windows, a.pool.num_kv_heads, nz), dim3(256), 0, stream, a, int(z0));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -121,3 +121,37 @@ def test_whole_prompt_recompute_of_a_layer_group():
                                               c["fv"][lb + i][b], 0, list(range(new[b])), scale)
             assert float(np.max(np.abs(got[i][c["cu"][b]:c["cu"][b + 1]] - want))) <= TOL
     assert int(c["st"].item()) == 0
+
+
+def test_more_than_65535_layer_session_pairs():
+    """33,000 one-token sessions over 2 layers: the append grid needs 66,000
+    (layer, session) pairs, more than one launch holds.  With one key each, every
+    row's output is its own V row exactly."""
+    import torch
+
+    B, L, Hkv, G, D = 33000, 2, 1, 2, 64
+    bt = np.arange(B, dtype=np.int32)[:, None]
+    pool = binding.Pool(L, B, Hkv, D, fill=np.int16(np.uint16(gu.POISON_NAN).view(np.int16)))
+    st = gu.status_tensor()
+    rng = np.random.default_rng(9)
+    kn = wlmod.draw_bf16(rng, (L, B, Hkv, D), 1.0)
+    vn = wlmod.draw_bf16(rng, (L, B, Hkv, D), 1.0)
+    q = wlmod.draw_bf16(rng, (L, B, Hkv * G, D), 1.0)
+    out = torch.empty((L, B, Hkv * G, D), dtype=torch.bfloat16, device="cuda")
+    binding.extend_layers(pool, 0, gu.dev_bf16(q), gu.dev_bf16(kn), gu.dev_bf16(vn), out,
+                          gu.dev_i32(np.arange(B + 1)), gu.dev_i32(bt), gu.dev_i32(np.zeros(B)), 1, 1,
+                          1.0 / math.sqrt(D), dev_status=st)
+    gu.sync()
+    assert int(st.item()) == 0
+    as_f32 = lambda bits: (bits.astype(np.uint32) << 16).view(np.float32)  # -0 equals +0 (0 + -0 = +0)
+    got = as_f32(gu.host_bits(out))
+    for h in range(G):
+        assert np.array_equal(got[:, :, h, :], as_f32(vn[:, :, 0, :]))
+    # the pool holds every session's K in both layers (slot 0 of its page)
+    bits = gu.pool_bits(pool)
+    shape = oracle.PoolShape(L, B, Hkv, D)
+    for l in range(L):
+        for b in (0, 1, 32767, 32768, B - 1):
+            base = oracle.tile_start(l, b, 0, B, Hkv, D)
+            row = np.array([bits[base + oracle.k_offset(0, d)] for d in range(D)], np.uint16)
+            assert np.array_equal(row, kn[l, b, 0]), (l, b)
