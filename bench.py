@@ -545,8 +545,16 @@ def cpu_baseline(wl, st, target_s):
         if spent >= target_s:
             break
     del k, v
+    cpu_model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
-            "blas_threads": blas_threads, "kind": "oracle",
+            "blas_threads": blas_threads, "cpu_model": cpu_model, "kind": "oracle",
             "sample": f"float64 oracle decode (gather + softmax) of {len(done)} of {B} sessions of layer 0 "
                       f"(lengths {done}), all {N} decoders x {Hq} heads; {spent:.1f}s CPU time"}
 
@@ -667,6 +675,8 @@ def main():
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
             "launch_ms": round(call_ms, 5),
+            "launch_ms_p10_p50_p90": [round(float(np.percentile(timer.all_ms(), x)), 5) for x in (10, 50, 90)],
+            "launches": len(timer.all_ms()),
         },
         "cpu_baseline": cpu,
         "decoder_concat": {"time_N8_over_N1": round(nN_ms / n1_ms, 3), "ms_N8": round(nN_ms, 4),
