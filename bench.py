@@ -69,12 +69,18 @@ PMC_SUMMARY = "profiles/decode_qwen3_8b_n8_hbm_counters.md"
 
 
 def kernel_source_hash(paths):
+    """Hash of the kernel sources' code: line comments and blank lines do not count,
+    so editing a comment does not retire the counter figures taken on the code."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            for line in f:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

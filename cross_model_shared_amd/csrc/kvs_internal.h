@@ -35,7 +35,8 @@ constexpr int kDecodeMaxBatch = 4096;
 // How a decode call is cut into work: query rows per KV head are taken in row
 // groups of 16*nb (one wave holds them all); the (page, KV head, row group)
 // tiles of all sessions are shared out among the 4*blocks waves of a
-// persistent grid (evenly, up to a fixed weight per XCD).  Each wave has two partial-state slots in the workspace.
+// persistent grid (evenly, up to a fixed weight per XCD).  Each wave has two
+// partial-state slots in the workspace.
 struct DecodePlan {
   int rows;       // N * G query rows per KV head
   int nb;         // 16-row column blocks per wave (1, 2 or 4)
