@@ -675,22 +675,32 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     if (row < 0) continue;
     float M = -INFINITY, den = 0.f;
     f32x4 num[4] = {};
-#pragma unroll 2
-    for (int k = k0; k <= k1; ++k) {
-      if (empty(k)) continue;
-      const int64_t slot = slot_of(k);
-      const f32x2 mlv = *reinterpret_cast<const f32x2*>(ml + (slot * RG + rl) * 2);
-      const f32x4* ap = reinterpret_cast<const f32x4*>(accp + (slot * RG + rl) * D) + 4 * tc;
-      f32x4 av[4];
+    // shares in batches of 8: every load of a batch is issued before any merge
+    // (a unit of a long session can span dozens of shares)
+    constexpr int KB = 8;
+#pragma unroll 1
+    for (int kb = k0; kb <= k1; kb += KB) {
+      f32x2 mlv[KB];
+      f32x4 av[KB][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = ap[i];
-      if (mlv[0] == -INFINITY) continue;  // the share saw no key of this row
-      const float Mn = fmaxf(M, mlv[0]);
-      const float c = exp2_fast(M - Mn), w = exp2_fast(mlv[0] - Mn);  // exp2(-inf) = 0
-      den = den * c + w * mlv[1];
+      for (int u = 0; u < KB; ++u) {
+        const int64_t slot = slot_of(min(kb + u, k1));
+        mlv[u] = *reinterpret_cast<const f32x2*>(ml + (slot * RG + rl) * 2);
+        const f32x4* ap = reinterpret_cast<const f32x4*>(accp + (slot * RG + rl) * D) + 4 * tc;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) num[i] = num[i] * c + w * av[i];
-      M = Mn;
+        for (int i = 0; i < 4; ++i) av[u][i] = ap[i];
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        // past k1, a share without tiles (nothing written), or one that saw no key of this row
+        if (kb + u > k1 || empty(kb + u) || mlv[u][0] == -INFINITY) continue;
+        const float Mn = fmaxf(M, mlv[u][0]);
+        const float c = exp2_fast(M - Mn), w = exp2_fast(mlv[u][0] - Mn);  // exp2(-inf) = 0
+        den = den * c + w * mlv[u][1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) num[i] = num[i] * c + w * av[u][i];
+        M = Mn;
+      }
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     u32x2* o = reinterpret_cast<u32x2*>(a.out + row * D) + 4 * tc;
