@@ -209,17 +209,29 @@ def setup_decode(wl, layers):
                 num_pages=num_pages, bt=bt)
 
 
-def decode_step(wl, st, layers, timer=None):
+# Layers per step whose decode call is bracketed by HIP events.  A timing event
+# costs the stream about 3 us, so bracketing all 36 calls would slow the step it
+# measures by about 1%; four spread layers per step, rotated from step to step,
+# sample every layer over the timed steps.
+TIMED_LAYERS_PER_STEP = 4
+
+
+def timed_layers(step, layers):
+    every = max(1, layers // TIMED_LAYERS_PER_STEP)
+    return {(step + every * j) % layers for j in range(min(TIMED_LAYERS_PER_STEP, layers))}
+
+
+def decode_step(wl, st, layers, timer=None, timed=()):
     from cross_model_shared_amd import binding
 
     d = st["dev"]
     for layer in range(layers):
         binding.append(st["pool"], layer, st["tok_k"][layer], st["tok_v"][layer], d["cu_one"], d["bt"],
                        d["before"], max_new=1, max_seq_len=st["maxL"])
-        e0 = timer.start() if timer else None
+        e0 = timer.start() if timer and layer in timed else None
         binding.decode(st["pool"], layer, st["q"][layer], st["out"], d["bt"], d["lens"], st["maxL"],
                        wl.scale, st["ws"])
-        if timer:
+        if e0 is not None:
             timer.stop(e0)
 
 
@@ -513,8 +525,8 @@ def handoff_section(reps):
     return res
 
 
-def cpu_baseline(wl, st, target_s):
-    """Time the CPU oracle's decode on a bounded sample of sessions of layer 0."""
+def cpu_baseline(wl, q, target_s):
+    """Time the CPU oracle's decode on a bounded sample of sessions of layer 0 (q: its queries, host uint16)."""
     import torch
 
     import oracle
@@ -533,7 +545,6 @@ def cpu_baseline(wl, st, target_s):
     total = int(cu[-1])
     k = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 10, 0)).view(total, Hkv, D)
     v = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 11, 0)).view(total, Hkv, D)
-    q = st["q"][0].view(torch.int16).cpu().numpy().view(np.uint16)
     spent, done_bytes, done = 0.0, 0, []
     for b in order:
         L = lens[b]
@@ -596,8 +607,8 @@ def main():
     timer = EventTimer()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        decode_step(wl, st, layers, timer)
+    for k in range(args.steps):
+        decode_step(wl, st, layers, timer, timed_layers(k, layers))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
@@ -626,10 +637,9 @@ def main():
     n1_ms = float(np.median(t1.all_ms()[2:]))
     nN_ms = float(np.median(tN.all_ms()[2:]))
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, st, args.cpu_seconds)
-        log(f"[bench] cpu baseline {cpu['value']} GB/s")
+    # layer 0's queries for the CPU baseline, which runs after the GPU sections
+    # (twelve seconds of an idle GPU would let its clocks drop before the extend timing)
+    q0_host = st["q"][0].view(torch.int16).cpu().numpy().view(np.uint16)
     pool_gb = st["pool"].nbytes / 1e9
     del st
     torch.cuda.empty_cache()
@@ -655,6 +665,11 @@ def main():
     handoff = None if args.no_handoff else handoff_section(10)
     cascade = None if args.no_cascade else cascade_section(20)
     layer_group = None if args.no_layer_group else layer_group_section(args.layer_group_calls)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, q0_host, args.cpu_seconds)
+        log(f"[bench] cpu baseline {cpu['value']} GB/s")
 
     res = {
         "metric": "shared-KV decode attn KV GB/s (% HBM peak) at N=8 decoders; extend TFLOP/s",

@@ -32,46 +32,54 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a, int z0) {
   const int lp = P / kPage + w;  // logical page written by this workgroup
   const int t0 = max(lp * kPage, P), t1 = min(lp * kPage + kPage, P + n);
   if (t0 >= t1) return;
+  const int64_t row_stride = int64_t(Hkv) * D;
+  // new row of logical position t is c0 + (t - P)
+  const uint16_t* ksrc = a.k_new + l * a.kv_lstride + int64_t(h) * D;
+  const uint16_t* vsrc = a.v_new + l * a.kv_lstride + int64_t(h) * D;
+
+  // The new rows are read before the page id, which they do not depend on, so
+  // the two loads overlap.  K: one thread per (slot, 8-value run).
+  static_assert(kPage * (D / 8) <= 256 && 2 * D <= 256, "one element per thread");
+  const int e = threadIdx.x;
+  const int kslot = e / (D / 8), krun = e % (D / 8);
+  const bool kact = e < kPage * (D / 8) && lp * kPage + kslot >= t0 && lp * kPage + kslot < t1;
+  u32x4 kval = {0u, 0u, 0u, 0u};
+  if (kact) kval = *reinterpret_cast<const u32x4*>(ksrc + int64_t(c0 + lp * kPage + kslot - P) * row_stride + krun * 8);
+  // V: one thread per (run of 8 slots, head-dim value)
+  const int vrun = e / D, vd = e % D;
+  const int base = lp * kPage + 8 * vrun;
+  const bool vact = e < 2 * D && base + 7 >= t0 && base < t1;
+  const bool vfull = base >= t0 && base + 7 < t1;
+  uint32_t vw[4] = {0u, 0u, 0u, 0u};
+  if (vact) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int t = base + c;
+      if (t >= t0 && t < t1) vw[c / 2] |= uint32_t(vsrc[int64_t(c0 + t - P) * row_stride + vd]) << (16 * (c % 2));
+    }
+  }
+
   const int pid = a.bt[int64_t(b) * a.bt_stride + lp];
   if (pid < 0 || pid >= a.pool.num_pages) {
     if (threadIdx.x == 0) flag_error(a.dev_status, 1);
     return;
   }
   uint16_t* tile = a.pool.data + tile_offset(a.layer + l, pid, h, a.pool.num_pages, Hkv, D);
-  const int64_t row_stride = int64_t(Hkv) * D;
-  // new row of logical position t is c0 + (t - P)
-  const uint16_t* ksrc = a.k_new + l * a.kv_lstride + int64_t(h) * D;
-  const uint16_t* vsrc = a.v_new + l * a.kv_lstride + int64_t(h) * D;
-
-  // K: one thread per (slot, 8-value run)
-  for (int e = threadIdx.x; e < kPage * (D / 8); e += 256) {
-    const int slot = e / (D / 8), run = e % (D / 8);
-    const int t = lp * kPage + slot;
-    if (t < t0 || t >= t1) continue;
-    const int d0 = run * 8;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(ksrc + int64_t(c0 + t - P) * row_stride + d0);
-    *reinterpret_cast<u32x4*>(tile + ((d0 / 32) * 64 + ((d0 % 32) / 8) * 16 + slot) * 8) = v;
+  if (kact) {
+    const int d0 = krun * 8;
+    *reinterpret_cast<u32x4*>(tile + ((d0 / 32) * 64 + ((d0 % 32) / 8) * 16 + kslot) * 8) = kval;
   }
-  // V: one thread per (run of 8 slots, head-dim value)
-  uint16_t* vt = tile + kPage * D;
-  for (int e = threadIdx.x; e < 2 * D; e += 256) {
-    const int run = e / D, d = e % D;
-    const int base = lp * kPage + 8 * run;
-    uint16_t* dst = vt + ((d / 16) * 32 + run * 16 + d % 16) * 8;
-    if (base >= t0 && base + 7 < t1) {
-      uint32_t w[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t lo = vsrc[int64_t(c0 + base + 2 * c - P) * row_stride + d];
-        const uint32_t hi = vsrc[int64_t(c0 + base + 2 * c + 1 - P) * row_stride + d];
-        w[c] = lo | (hi << 16);
-      }
-      *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+  // the V part of the tile holds 8 slots of one head-dim value side by side:
+  // written as one 16-byte run when all 8 are new, slot by slot otherwise
+  if (vact) {
+    uint16_t* dst = tile + kPage * D + ((vd / 16) * 32 + vrun * 16 + vd % 16) * 8;
+    if (vfull) {
+      *reinterpret_cast<u32x4*>(dst) = u32x4{vw[0], vw[1], vw[2], vw[3]};
     } else {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int t = base + c;
-        if (t >= t0 && t < t1) dst[c] = vsrc[int64_t(c0 + t - P) * row_stride + d];
+        if (t >= t0 && t < t1) dst[c] = uint16_t(vw[c / 2] >> (16 * (c % 2)));
       }
     }
   }
@@ -79,8 +87,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a, int z0) {
 
 template <int D>
 hipError_t launch_append_t(const AppendArgs& a, hipStream_t stream) {
-  // a window of new tokens starting mid-page can touch one page more
-  const int windows = (a.max_new + kPage - 1) / kPage + 1;
+  // n new tokens starting at slot o of a page touch ceil((o + n) / 16) pages,
+  // at most (n + 30) / 16 of them
+  const int windows = (a.max_new + 2 * kPage - 2) / kPage;
   // (layer, session) pairs on grid z, at most 65535 per launch
   const int64_t zs = int64_t(a.batch) * a.num_layers;
   for (int64_t z0 = 0; z0 < zs; z0 += 65535) {

@@ -326,8 +326,13 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
   const int voff = (lane >> 5) * (TILE + kPad) + v_run(D, 0, (lane >> 4) & 1, lane & 15);
 
   // PV of block k from stage stg: one V run per 16 head dims as the A operand,
-  // the bf16 weights pb as the B operand (32 keys per step).
-  auto pv_block = [&](const u32x4* stg, const u32x4 (&pb)[NB], int nv0, int nv1, bool vmask) {
+  // the bf16 weights pb as the B operand (32 keys per step).  The first VPRE
+  // runs come from vpre, read before the softmax.
+  constexpr int kVPre = 4;  // V runs read ahead of the softmax in the fast blocks
+  auto v_operand = [&](const u32x4* stg, int i) { return stg[voff + v_run(D, i, 0, 0) - v_run(D, 0, 0, 0)]; };
+  auto pv_block = [&](const u32x4* stg, const u32x4 (&pb)[NB], int nv0, int nv1, bool vmask, auto vpre_tag,
+                      const u32x4 (&vpre)[kVPre]) {
+    constexpr int VPRE = decltype(vpre_tag)::value;
     constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb)
@@ -335,12 +340,14 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
     const int nv = (lane >> 5) ? nv1 : nv0;
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
-      u32x4 va = stg[voff + v_run(D, i, 0, 0) - v_run(D, 0, 0, 0)];
+      u32x4 va = i < VPRE ? vpre[i < VPRE ? i : 0] : v_operand(stg, i);
       if (vmask) va = mask_v_run(va, 8 * ((fresh_lane() >> 4) & 1), nv);
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) st.acc[cb][i] = mma_16x16x32(va, pb[cb], st.acc[cb][i]);
     }
   };
+  using NoPre = std::integral_constant<int, 0>;
+  const u32x4 no_vpre[kVPre] = {};
 
   // Blocks below fast_end are seen in full by every row of the workgroup and are
   // followed by at least kLook more blocks: their steps have no masks and no
@@ -381,7 +388,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
         else softmax_fixed<D, NB, false>(st, cur, pb, kbase, lim_abs);
       }
       const int nv0 = total - kbase, nv1 = total - kbase - 16;
-      pv_block(ring[k % kStages], pb, nv0, nv1, nv1 < kPage);
+      pv_block(ring[k % kStages], pb, nv0, nv1, nv1 < kPage, NoPre{}, no_vpre);
     };
     // fast step: no masks, constant waits, unconditional prefetch
     auto fast_step = [&](int k, f32x4 (&cur)[2][NB], f32x4 (&nxt)[2][NB]) {
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
       qk_block<D, NB>(nxt, qf, ring[(k + 1) % kStages], koff, zero);
       u32x4 pb[NB];
       softmax_fixed<D, NB, false>(st, cur, pb, k * 32, lim_abs);
-      pv_block(ring[k % kStages], pb, kPage, kPage, false);
+      pv_block(ring[k % kStages], pb, kPage, kPage, false, NoPre{}, no_vpre);
     };
 #pragma unroll 1
     for (int k = 0; k < kLook && k < nblk; ++k) issue(k);
@@ -422,9 +429,14 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
         const int kbase = k * 32;
         u32x4 pb[NB];
         if (fast) {
+          // the first V runs are read now, so their LDS latency passes during the softmax
+          u32x4 vpre[kVPre];
+#pragma unroll
+          for (int i = 0; i < kVPre; ++i) vpre[i] = v_operand(ring[k % kStages], i);
+          __builtin_amdgcn_sched_barrier(0);
           softmax_shifted<NB>(sc, pb);
           __builtin_amdgcn_s_setprio(2);
-          pv_block(ring[k % kStages], pb, kPage, kPage, false);
+          pv_block(ring[k % kStages], pb, kPage, kPage, false, std::integral_constant<int, kVPre>{}, vpre);
           __builtin_amdgcn_s_setprio(0);
           return;
         }
@@ -441,7 +453,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
         }
         const int nv0 = total - kbase, nv1 = total - kbase - 16;
         __builtin_amdgcn_s_setprio(2);
-        pv_block(ring[k % kStages], pb, nv0, nv1, nv1 < kPage);
+        pv_block(ring[k % kStages], pb, nv0, nv1, nv1 < kPage, NoPre{}, no_vpre);
         __builtin_amdgcn_s_setprio(0);
       };
       seq_step(0, false);
