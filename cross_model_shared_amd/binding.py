@@ -40,6 +40,8 @@ _SIGNATURES = {
     "shared_kv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "shared_kv_decode": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                         _f, _vp, _sz, _vp, _vp]),
+    "shared_kv_decode_append": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                               _i32, _i32, _f, _vp, _sz, _vp, _vp]),
     "shared_kv_decode_private": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32,
                                                 _i32, _i32, _i32, _i32, _f, _vp, _sz, _vp, _vp]),
     "shared_kv_decode_cascade": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32,
@@ -182,6 +184,24 @@ def decode(pool: Pool, layer, q, out, block_table, seq_lens, max_seq_len, scale,
         raise ValueError("q/out shape does not match the pool")
     _check(load().shared_kv_decode(
         pool.struct, layer, _ptr(q, "q", torch.bfloat16), _ptr(out, "out", torch.bfloat16),
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
+        _ptr(seq_lens, "seq_lens", torch.int32, B), B, N, Hq, max_seq_len, float(scale),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True), _stream(stream)))
+
+
+def decode_append(pool: Pool, layer, k_new, v_new, q, out, block_table, seq_lens, max_seq_len, scale, workspace,
+                  dev_status=None, stream=None):
+    """Append the step's token (k_new, v_new: bf16 [B, H_kv, D], written at position seq_lens[b] - 1),
+    then decode over seq_lens[b] tokens, in one call.  q, out, workspace as for decode."""
+    torch = _torch()
+    B, N, Hq, D = q.shape
+    if D != pool.head_dim or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q/out shape does not match the pool")
+    n_kv = B * pool.num_kv_heads * D
+    _check(load().shared_kv_decode_append(
+        pool.struct, layer, _ptr(k_new, "k_new", torch.bfloat16, n_kv), _ptr(v_new, "v_new", torch.bfloat16, n_kv),
+        _ptr(q, "q", torch.bfloat16), _ptr(out, "out", torch.bfloat16),
         _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
         _ptr(seq_lens, "seq_lens", torch.int32, B), B, N, Hq, max_seq_len, float(scale),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),

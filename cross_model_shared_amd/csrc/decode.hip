@@ -343,9 +343,15 @@ __device__ __forceinline__ int priv_pages(const DecodeArgs& a, int b) {
   return pages;
 }
 
-template <int D, int NB, int S, int MODE>
+// APPEND (plain mode): the step's token of each session is written into its
+// slot, position seq_lens[b] - 1, by the wave that attends that page.  That
+// wave puts the new K row and V column into its LDS copy of the page after the
+// page has landed (so what the page load read of that slot does not matter), and
+// the wave of row group 0 also stores them to the pool for later calls.
+template <int D, int NB, int S, int MODE, bool APPEND>
 __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
   static_assert(MODE != kCascade, "cascade units run on decode_pair_kernel");
+  static_assert(!APPEND || MODE == kPlain, "the fused append is a plain-mode call");
   constexpr int SLABS = D / 16;  // 1 KiB slabs per (page, head) tile: K slabs then V slabs
   __shared__ u32x4 ring[kWaves][S][SLABS * 64];
   __shared__ int cum_s[kDecodeMaxBatch + 1];
@@ -440,10 +446,35 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
     advance<MODE>(a, iw, cum, B);
   };
 
+  // the step's token of the current unit (APPEND): 8 head dims of K on each of
+  // the first D/8 lanes, D/64 head dims of V on every lane
+  u32x4 knew = {0u, 0u, 0u, 0u};
+  uint16_t vnew[D / 64] = {};
+  auto load_new = [&](int b, int g) {
+    if constexpr (APPEND) {
+      if (b >= B) return;
+      const int64_t row = (int64_t(b) * Hkv + g) * D;
+      if (lane < D / 8) knew = reinterpret_cast<const u32x4*>(a.k_new + row)[lane];
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c) vnew[c] = a.v_new[row + lane + 64 * c];
+    }
+  };
+  // write the token into slot t of a page tile (LDS copy or pool)
+  auto put_token = [&](auto* tile, int t) {
+    uint16_t* t16 = reinterpret_cast<uint16_t*>(tile);
+    if (lane < D / 8) reinterpret_cast<u32x4*>(tile)[k_run(lane / 4, lane % 4, t)] = knew;
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) {
+      const int d = lane + 64 * c;
+      t16[v_run(D, d / 16, t / 8, d % 16) * 8 + t % 8] = vnew[c];
+    }
+  };
+
   QFrag<D, NB> qf;
   RowState<D, NB> st;
   st.init();
   load_q<D, NB, MODE>(qf, a, cw.b, cw.gr / RGs, cw.gr % RGs, lane);
+  load_new(cw.b, cw.gr / RGs);
   __builtin_amdgcn_s_waitcnt(0);
   int64_t unit_begin = int64_t(cw.gr) * Ptot + cum_s[cw.b];  // first tile of the current unit
 
@@ -456,6 +487,17 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
     if (j + S - 1 < n) issue((j + S - 1) % S);
     wait_ring<SLABS, S>(min(S - 1, n - 1 - j));
     if (!((bad >> slot) & 1u)) {
+      if constexpr (APPEND) {
+        const int L = load_uniform(a.seq_lens + cw.b);
+        if (cw.page == cw.npg - 1 && L >= 1 && L <= a.max_seq_len) {  // the page of position L - 1
+          const int t = (L - 1) % kPage;
+          put_token(ring[wave][slot], t);
+          if (cw.gr % RGs == 0) {
+            const int pid = load_uniform(a.bt + int64_t(cw.b) * a.bt_stride + cw.page);  // in range: slot not bad
+            put_token(a.pool.data + tile_offset(a.layer, pid, cw.gr / RGs, num_pages, Hkv, D), t);
+          }
+        }
+      }
       u32x4 kf[D / 32];
       u32x2 vf[D / 16];
       const u32x2* v2 = reinterpret_cast<const u32x2*>(ring[wave][slot]);
@@ -495,6 +537,7 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       if (!last) {
         st.init();
         load_q<D, NB, MODE>(qf, a, cw.b, cw.gr / RGs, cw.gr % RGs, lane);
+        load_new(cw.b, cw.gr / RGs);
         __builtin_amdgcn_s_waitcnt(0);  // stores and q loads drained before the ring resumes
         unit_begin = int64_t(cw.gr) * Ptot + cum_s[cw.b];
       }
@@ -870,10 +913,10 @@ __global__ __launch_bounds__(1024) void decode_cascade_plan_kernel(DecodeArgs a,
   if (mismatch) flag_error(a.dev_status, KVS_DEV_BAD_PAGE_BIT);
 }
 
-template <int D, int NB, int MODE>
+template <int D, int NB, int MODE, bool APPEND = false>
 hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
   constexpr int S = D == 128 ? 4 : 8;  // 32 KiB of ring per wave
-  hipLaunchKernelGGL((decode_stream_kernel<D, NB, S, MODE>), dim3(kDecodeBlocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_stream_kernel<D, NB, S, MODE, APPEND>), dim3(kDecodeBlocks), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units = a.pool.num_kv_heads * a.plan.rowgroups * a.batch;
@@ -902,6 +945,7 @@ hipError_t launch_decode_cascade(const DecodeArgs& a, hipStream_t stream) {
 template <int D, int NB>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   if (a.pbt) return launch_decode_mode<D, NB, kPrivate>(a, stream);
+  if (a.k_new) return launch_decode_mode<D, NB, kPlain, true>(a, stream);
   return launch_decode_mode<D, NB, kPlain>(a, stream);
 }
 

@@ -79,6 +79,11 @@ struct DecodeArgs {
   // group_id adjacent in the batch share their first group_prefix[b] pages
   const int32_t* group_id;
   const int32_t* group_prefix;
+  // fused append (null for the other calls): the step's token of session b,
+  // K/V head g at k_new / v_new + (b * H_kv + g) * D, is written at position
+  // seq_lens[b] - 1 before it is attended
+  const uint16_t* k_new;
+  const uint16_t* v_new;
   int* ws_units;  // [3*batch+1] cascade units: first session, count, prefix pages; unit count
   int* ws_cum;    // [batch+1] page prefix sum, written by the decode kernel
   float* ws_ml;   // [4*blocks*2][rg_rows][2] partial (m, l)

@@ -151,7 +151,8 @@ int decode_common(const char* name, const kvs_pool* pool, int32_t layer, const v
                   const int32_t* pbt, int32_t pbt_stride, const int32_t* plens, const int32_t* group_id,
                   const int32_t* group_prefix, int32_t batch, int32_t num_decoders, int32_t num_q_heads,
                   int32_t max_seq_len, int32_t max_priv_len, float scale, void* workspace,
-                  size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
+                  size_t workspace_bytes, int32_t* dev_status, hipStream_t stream, const void* k_new = nullptr,
+                  const void* v_new = nullptr) {
   int s = check_pool(pool, layer);
   if (s) return s;
   if (!q || !out || !block_table || !seq_lens) return fail(KVS_EINVAL, "%s: a required pointer is NULL", name);
@@ -204,6 +205,7 @@ int decode_common(const char* name, const kvs_pool* pool, int32_t layer, const v
   kvs::DecodeArgs a{view(pool), layer, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
                     block_table, bt_stride, seq_lens, batch, num_decoders, num_q_heads, max_seq_len,
                     scale * 1.4426950408889634f, pbt, pbt_stride, plens, max_priv_len, group_id, group_prefix,
+                    static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
                     reinterpret_cast<int*>(ws + plan.units_offset), reinterpret_cast<int*>(ws + plan.cum_offset),
                     reinterpret_cast<float*>(ws + plan.ml_offset),
                     reinterpret_cast<float*>(ws + plan.acc_offset), plan, dev_status};
@@ -222,6 +224,17 @@ int shared_kv_decode(const kvs_pool* pool, int32_t layer, const void* q, void* o
   return decode_common("shared_kv_decode", pool, layer, q, out, block_table, bt_stride, seq_lens, nullptr, 0,
                        nullptr, nullptr, nullptr, batch, num_decoders, num_q_heads, max_seq_len, 0, scale,
                        workspace, workspace_bytes, dev_status, stream);
+}
+
+int shared_kv_decode_append(const kvs_pool* pool, int32_t layer, const void* k_new, const void* v_new,
+                            const void* q, void* out, const int32_t* block_table, int32_t bt_stride,
+                            const int32_t* seq_lens, int32_t batch, int32_t num_decoders, int32_t num_q_heads,
+                            int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
+                            int32_t* dev_status, hipStream_t stream) {
+  if (!k_new || !v_new) return fail(KVS_EINVAL, "shared_kv_decode_append: a required pointer is NULL");
+  return decode_common("shared_kv_decode_append", pool, layer, q, out, block_table, bt_stride, seq_lens, nullptr,
+                       0, nullptr, nullptr, nullptr, batch, num_decoders, num_q_heads, max_seq_len, 0, scale,
+                       workspace, workspace_bytes, dev_status, stream, k_new, v_new);
 }
 
 int shared_kv_decode_private(const kvs_pool* pool, int32_t layer, const void* q, void* out,

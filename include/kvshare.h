@@ -15,6 +15,8 @@
  * Three operations:
  *   kv_pool_append         write new K/V rows into pages        (the cache "store")
  *   shared_kv_decode       N decoders x G GQA heads, one KV read (decode attention)
+ *   shared_kv_decode_append  the same, writing the step's own token into the
+ *                          pool in the same launch (append + decode fused)
  *   shared_kv_decode_private  the same over a shared prefix + per-decoder private suffixes
  *   shared_kv_decode_cascade  the same where sessions share prefix pages, each prefix read once
  *   kv_pages_pack / kv_pages_unpack   pages <-> contiguous transfer buffer (cache handoff)
@@ -176,6 +178,36 @@ int shared_kv_decode(const kvs_pool* pool, int32_t layer, const void* q, void* o
                      int32_t batch, int32_t num_decoders, int32_t num_q_heads,
                      int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
                      int32_t* dev_status, hipStream_t stream);
+
+/*
+ * shared_kv_decode_append — kv_pool_append of one token per session followed by
+ * shared_kv_decode, in one call.
+ *
+ * ICaRus, Method / overall framework: at step i the frozen base model writes
+ * the token's own K_i, V_i, and every decoder then attends K_{1:i}, V_{1:i}.
+ * This call does both: for every session b with 1 <= seq_lens[b] <= max_seq_len
+ * it writes the token's K/V (every KV head) at position seq_lens[b] - 1 through
+ * the block table, exactly as kv_pool_append with one new row would, and it
+ * returns what shared_kv_decode over seq_lens[b] tokens returns after that
+ * append, bit for bit.  The token is written by the wave that attends its page,
+ * which also patches the token into its on-chip copy of the page, so the write
+ * needs no launch of its own.
+ *
+ *  k_new, v_new  bf16 [batch][num_kv_heads][head_dim]: the step's token of
+ *                each session.
+ *  seq_lens      int32 [batch], tokens attended, counting the new one.  A
+ *                session with seq_lens[b] == 0 writes nothing and gets zeros.
+ *  Other arguments, the workspace and dev_status are those of shared_kv_decode.
+ *  The page that receives a session's token must not be read by another
+ *  session of the same call (a page shared between sessions holds full blocks
+ *  only, so this is the usual case).  Not combinable with private suffixes or
+ *  cascade groups.
+ */
+int shared_kv_decode_append(const kvs_pool* pool, int32_t layer, const void* k_new, const void* v_new,
+                            const void* q, void* out, const int32_t* block_table, int32_t bt_stride,
+                            const int32_t* seq_lens, int32_t batch, int32_t num_decoders,
+                            int32_t num_q_heads, int32_t max_seq_len, float scale, void* workspace,
+                            size_t workspace_bytes, int32_t* dev_status, hipStream_t stream);
 
 /*
  * shared_kv_decode_private — one decode step of N decoders over one shared

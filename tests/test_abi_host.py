@@ -32,7 +32,8 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol(L):
     names = header_functions()
-    assert {"kv_pool_append", "shared_kv_decode", "shared_kv_decode_private", "shared_kv_decode_cascade",
+    assert {"kv_pool_append", "shared_kv_decode", "shared_kv_decode_append", "shared_kv_decode_private",
+            "shared_kv_decode_cascade",
             "partial_prefill_extend", "partial_prefill_layers",
             "kv_pages_pack", "kv_pages_unpack", "kv_pages_buffer_bytes", "kv_pool_fetch", "kvs_pool_bytes",
             "shared_kv_decode_workspace_bytes", "kvs_last_error", "kvs_version",
@@ -90,6 +91,24 @@ def call_decode(L, p, layer=0, q=FAKE, out=FAKE, bt=FAKE, stride=4, lens=FAKE, b
 def test_decode_host_checks(L, kw, status):
     p = kw.pop("p")
     assert call_decode(L, p, **kw) == status
+    assert binding.last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), binding.KVS_EINVAL),
+    (dict(v=None), binding.KVS_EINVAL),
+    (dict(q=None), binding.KVS_EINVAL),
+    (dict(p=pool(dim=96)), binding.KVS_EUNSUPPORTED),
+    (dict(layer=1), binding.KVS_ERANGE),
+    (dict(Hq=7), binding.KVS_EUNSUPPORTED),
+    (dict(msl=65), binding.KVS_ERANGE),
+    (dict(wsb=16), binding.KVS_EWORKSPACE),
+])
+def test_decode_append_host_checks(L, kw, status):
+    a = dict(p=pool(), layer=0, k=FAKE, v=FAKE, q=FAKE, Hq=8, msl=64, wsb=1 << 30)
+    a.update(kw)
+    assert L.shared_kv_decode_append(ctypes.byref(a["p"]), a["layer"], a["k"], a["v"], a["q"], FAKE, FAKE, 4, FAKE,
+                                     2, 2, a["Hq"], a["msl"], 0.125, FAKE, a["wsb"], None, None) == status
     assert binding.last_error()
 
 
