@@ -593,9 +593,9 @@ def main():
     layers = args.layers or wl.num_layers
     B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     st = setup_decode(wl, layers)
-    per_call = decode_bytes(wl.lens, B, N, Hq, Hkv, D)
+    # one shared_kv_decode_append call: the decode's bytes plus the step's token rows read and written
+    per_call = decode_bytes(wl.lens, B, N, Hq, Hkv, D) + append_bytes(B, Hkv, D)
     step_bytes = layers * per_call
-    step_total_bytes = step_bytes + layers * append_bytes(B, Hkv, D)
 
     for _ in range(args.warmup):
         decode_step(wl, st, layers)
@@ -685,7 +685,7 @@ def main():
                         f"(shared_kv_decode_append per layer: the step's token written and attended), B={B} sessions, N={N}, "
                         f"32 q / 8 KV heads, D=128, page 16, lengths U[4096,16384] (sum {sum(wl.lens)})",
             "batch": B, "num_decoders": N, "layers": layers, "context_tokens": sum(wl.lens),
-            "step_algorithmic_bytes": step_total_bytes, "decode_bytes_per_layer": per_call,
+            "step_algorithmic_bytes": step_bytes, "decode_bytes_per_layer": per_call,
         },
         "roofline": {
             "bound": "hbm", "kernel": "shared_kv_decode_append (per-layer call)",
