@@ -108,6 +108,54 @@ def test_decode_full_size_sampled(name, layers, layer):
         check_tiles(pool, bt, layer, b, Ks[b], Vs[b], Hkv, D)
 
 
+def test_decode_append_full_size_sampled():
+    """The bench's decode step call (shared_kv_decode_append) on the full 8-decoder workload: the pool
+    holds every session's first L-1 tokens (NaN in the last slot), the call writes token L-1 and
+    attends all L."""
+    import torch
+
+    wl = W.make_workload("qwen3_8b_n8")
+    B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    lens, layer = wl.lens, 1
+    print(f"[fullsize] decode_append {wl.name}: B={B} N={N} sum(L)={sum(lens)}", flush=True)
+    bt, num_pages = W.build_block_table(lens, wl.seed)
+    pool = binding.Pool(2, num_pages, Hkv, D, fill=np.int16(np.uint16(gu.POISON_NAN).view(np.int16)))
+    total = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    k = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 10, layer)).view(total, Hkv, D)
+    v = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 11, layer)).view(total, Hkv, D)
+    last = torch.from_numpy(cu[1:] - 1).long().cuda()
+    keep = torch.ones(total, dtype=torch.bool, device="cuda")
+    keep[last] = False
+    st = gu.status_tensor()
+    maxL = max(lens)
+    bt_d = torch.from_numpy(bt).cuda()
+    cu_before = np.concatenate([[0], np.cumsum([L - 1 for L in lens])]).astype(np.int32)
+    binding.append(pool, layer, k[keep].contiguous(), v[keep].contiguous(), gu.dev_i32(cu_before), bt_d,
+                   gu.dev_i32(np.zeros(B)), max_new=maxL, max_seq_len=maxL, dev_status=st)
+    q = W.device_normal_bf16(B * N * Hq * D, wl.std, W.mix_seed(wl.seed, 12, layer)).view(B, N, Hq, D)
+    out = torch.empty_like(q)
+    ws = gu.nan_workspace(binding.decode_workspace_bytes(B, N, Hq, Hkv, D, maxL))
+    binding.decode_append(pool, layer, k[last].contiguous(), v[last].contiguous(), q, out, bt_d, gu.dev_i32(lens),
+                          maxL, wl.scale, ws, dev_status=st)
+    gu.sync()
+    assert int(st.item()) == 0
+    got = gu.host_f64(out)
+    assert np.all(np.isfinite(got))
+    picks = sample_sessions(lens, 8, wl.seed + 1)
+    qh = host_rows(q)
+    Ks, Vs = [None] * B, [None] * B
+    for b in picks:
+        Ks[b] = host_rows(k[cu[b]:cu[b + 1]])
+        Vs[b] = host_rows(v[cu[b]:cu[b + 1]])
+    want = oracle.decode_from_logical(qh, Ks, Vs, wl.scale)
+    err = max(float(np.max(np.abs(got[b] - want[b]))) for b in picks)
+    print(f"[fullsize] decode_append: sessions {picks} max-abs err {err:.3e}", flush=True)
+    assert err <= TOL
+    for b in sorted(picks, key=lambda b: lens[b])[:2]:   # every page, the new token's included
+        check_tiles(pool, bt, layer, b, Ks[b], Vs[b], Hkv, D)
+
+
 def test_extend_full_size_sampled():
     import torch
 

@@ -1,4 +1,5 @@
 """Seeded random sweep of shapes and lengths for every attention entry point
+(decode, the fused decode step, extend, private and cascade decode)
 against the float64 oracle (2e-2 max-abs).  Lengths mix the page-boundary cases
 (0, 1, 15, 16, 17, whole pages) with arbitrary ones; head dims 64 and 128; GQA
 groups 1-6; decoders 1-12."""
@@ -12,6 +13,7 @@ from cross_model_shared_amd import binding
 from cross_model_shared_amd import workload as wlmod
 from tests import gpu_util as gu
 from tests.test_gpu_cascade import make_case as make_cascade_case, run_cascade
+from tests.test_gpu_decode_append import expected_pool, make_step_case, run_fused
 from tests.test_gpu_parity import make_extend_case, run_extend
 
 pytestmark = pytest.mark.gpu
@@ -47,6 +49,28 @@ def test_random_decode(seed):
     print(f"[random] decode seed={seed} D={D} Hkv={Hkv} G={G} N={N} lens={lens}", flush=True)
     c = gu.make_decode_case(lens, N, Hkv, G, D, seed=2000 + seed, poison=gu.POISON_NAN)
     out = gu.host_f64(gu.run_decode(c))
+    want = oracle.decode_from_logical(c["q"], c["K"], c["V"], 1.0 / math.sqrt(D))
+    err = float(np.max(np.abs(out - want)))
+    print(f"[random] max-abs err {err:.3e}", flush=True)
+    assert err <= TOL
+    assert int(c["status"].item()) == 0
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_decode_append(seed):
+    rng = np.random.default_rng(5000 + seed)
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.integers(1, 7))
+    N = min(int(rng.integers(1, 13)), max(1, 96 // G))
+    B = int(rng.integers(1, 10))
+    lens = [draw_len(rng, 700) for _ in range(B)]
+    if max(lens) == 0:
+        lens[0] = 1
+    print(f"[random] decode_append seed={seed} D={D} Hkv={Hkv} G={G} N={N} lens={lens}", flush=True)
+    c = make_step_case(lens, N, Hkv, G, D, seed=6000 + seed)
+    out = gu.host_f64(run_fused(c))
+    assert np.array_equal(gu.pool_bits(c["pool"]), expected_pool(c))
     want = oracle.decode_from_logical(c["q"], c["K"], c["V"], 1.0 / math.sqrt(D))
     err = float(np.max(np.abs(out - want)))
     print(f"[random] max-abs err {err:.3e}", flush=True)
