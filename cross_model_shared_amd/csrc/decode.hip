@@ -670,13 +670,90 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
   }
 }
 
+constexpr int kCombineWideThreads = 1024;
+
+// The WIDE combine of one unit whose shares are k0..k1 (see decode_combine_kernel).
+template <int D, int MODE>
+__device__ __forceinline__ void combine_wide(const DecodeArgs& a, int b, int g, int rg, int RG, int k0, int k1,
+                                             int64_t T) {
+  constexpr bool kPair = MODE == kCascade;
+  constexpr int WPG = kPair ? 1 : kWaves;
+  constexpr int TPR = D / 16;                  // threads per row
+  const int rows_t = RG * TPR;                 // threads of one group: 64 .. 512
+  const int groups = kCombineWideThreads / rows_t;
+  const int grp = threadIdx.x / rows_t, w = threadIdx.x % rows_t;
+  const int rl = w / TPR, tc = w % TPR;
+  const int64_t row = unit_row<MODE>(a, b, g, rg * RG + rl);
+  auto empty = [&](int k) { return share_start<WPG>(k, T) == share_start<WPG>(k + 1, T); };
+  auto slot_of = [&](int k) { return int64_t(k * 2 + (k == k0)) * (kPair ? 2 : 1) + (kPair ? rg : 0); };
+  float M = -INFINITY, den = 0.f;
+  f32x4 num[4] = {};
+  if (row >= 0) {
+    // this group's shares in batches of KB: every load of a batch is issued before any merge
+    constexpr int KB = 4;
+#pragma unroll 1
+    for (int kb = k0 + grp; kb <= k1; kb += KB * groups) {
+      f32x2 mlv[KB];
+      f32x4 av[KB][4];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int64_t slot = slot_of(min(kb + u * groups, k1));
+        mlv[u] = *reinterpret_cast<const f32x2*>(a.ws_ml + (slot * RG + rl) * 2);
+        const f32x4* ap = reinterpret_cast<const f32x4*>(a.ws_acc + (slot * RG + rl) * D) + 4 * tc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[u][i] = ap[i];
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int k = kb + u * groups;
+        if (k > k1 || empty(k) || mlv[u][0] == -INFINITY) continue;
+        const float Mn = fmaxf(M, mlv[u][0]);
+        const float c = exp2_fast(M - Mn), wt = exp2_fast(mlv[u][0] - Mn);  // exp2(-inf) = 0
+        den = den * c + wt * mlv[u][1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) num[i] = num[i] * c + wt * av[u][i];
+        M = Mn;
+      }
+    }
+  }
+  // the groups' states, merged by group 0 (every thread reaches the barrier)
+  __shared__ float sm[kCombineWideThreads], sden[kCombineWideThreads];
+  __shared__ f32x4 snum[4][kCombineWideThreads];
+  sm[threadIdx.x] = M;
+  sden[threadIdx.x] = den;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) snum[i][threadIdx.x] = num[i];
+  __syncthreads();
+  if (grp != 0 || row < 0) return;
+  for (int j = 1; j < groups; ++j) {
+    const int t = j * rows_t + w;
+    const float mj = sm[t];
+    if (mj == -INFINITY) continue;
+    const float Mn = fmaxf(M, mj);
+    const float c = exp2_fast(M - Mn), wt = exp2_fast(mj - Mn);
+    den = den * c + wt * sden[t];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) num[i] = num[i] * c + wt * snum[i][t];
+    M = Mn;
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  u32x2* o = reinterpret_cast<u32x2*>(a.out + row * D) + 4 * tc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x4(num[i][0] * inv, num[i][1] * inv, num[i][2] * inv, num[i][3] * inv);
+}
+
 // Merge the partial states of units that cross share boundaries:
 // m* = max m_s, out = sum_s 2^(m_s - m*) acc_s / sum_s 2^(m_s - m*) l_s.
-// Also writes zeros for empty units (softmax over nothing).  256 threads per
-// unit, each one row and 16 consecutive head dims (64 contiguous bytes of
-// every share's partial accumulator), merging the shares in one online pass.
-template <int D, int MODE>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+// Also writes zeros for empty units (softmax over nothing).  A thread takes
+// one row and 16 consecutive head dims (64 contiguous bytes of every share's
+// partial accumulator) and merges shares in one online pass.
+//  - 256 threads per unit: the unit's rows in passes, all its shares per thread.
+//  - WIDE, for calls with few units (each then spans many shares, up to ~75
+//    for a 128K-token session): 1024 threads per unit, i.e. 1024 / (rows*D/16)
+//    groups, group j merging shares k0 + j, k0 + j + groups, ...; the groups'
+//    states are merged through LDS.  Fewer dependent loads per thread.
+template <int D, int MODE, bool WIDE>
+__global__ __launch_bounds__(WIDE ? kCombineWideThreads : 256) void decode_combine_kernel(DecodeArgs a) {
   const int Hkv = a.pool.num_kv_heads, RGs = a.plan.rowgroups;
   const int B = MODE == kCascade ? load_uniform(a.ws_units + 3 * a.batch) : a.batch;
   const int unit = blockIdx.x;  // (gr, b) with b fastest, over the launch's batch
@@ -707,6 +784,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   auto empty = [&](int k) { return share_start<WPG>(k, T) == share_start<WPG>(k + 1, T); };
   const float* __restrict__ ml = a.ws_ml;
   const float* __restrict__ accp = a.ws_acc;
+  if constexpr (WIDE) {
+    combine_wide<D, MODE>(a, b, g, rg, RG, k0, k1, T);
+    return;
+  }
   // thread: one row, 16 consecutive head dims (D/16 threads per row)
   constexpr int TPR = D / 16, RPP = 256 / TPR;
   const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
@@ -913,15 +994,26 @@ __global__ __launch_bounds__(1024) void decode_cascade_plan_kernel(DecodeArgs a,
   if (mismatch) flag_error(a.dev_status, KVS_DEV_BAD_PAGE_BIT);
 }
 
+// One combine workgroup per (KV head, row group, session).  With at most 128
+// of them (fewer than the CUs), each unit spans 8 or more of the 1024 shares
+// on average, and the wide variant spreads a unit's shares over 1024 threads.
+template <int D, int MODE>
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
+  const int units = a.pool.num_kv_heads * a.plan.rowgroups * a.batch;
+  if (units <= 128)
+    hipLaunchKernelGGL((decode_combine_kernel<D, MODE, true>), dim3(units), dim3(kCombineWideThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<D, MODE, false>), dim3(units), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D, int NB, int MODE, bool APPEND = false>
 hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
   constexpr int S = D == 128 ? 4 : 8;  // 32 KiB of ring per wave
   hipLaunchKernelGGL((decode_stream_kernel<D, NB, S, MODE, APPEND>), dim3(kDecodeBlocks), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int units = a.pool.num_kv_heads * a.plan.rowgroups * a.batch;
-  hipLaunchKernelGGL((decode_combine_kernel<D, MODE>), dim3(units), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_combine<D, MODE>(a, stream);
 }
 
 // Cascade: the plan kernel forms the units, then 4 wave pairs per CU (two waves
@@ -937,9 +1029,7 @@ hipError_t launch_decode_cascade(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_pair_kernel<D, S>), dim3(1 << kDecodeShareLog2), dim3(128), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int units = a.pool.num_kv_heads * a.plan.rowgroups * a.batch;
-  hipLaunchKernelGGL((decode_combine_kernel<D, kCascade>), dim3(units), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_combine<D, kCascade>(a, stream);
 }
 
 template <int D, int NB>

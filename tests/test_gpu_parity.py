@@ -113,6 +113,25 @@ def test_decode_row_layouts_and_splits(D, N, G):
     assert int(case["status"].item()) == 0
 
 
+@pytest.mark.parametrize("B,Hkv,N,G,D", [
+    (40, 4, 16, 6, 128),   # 320 units of 64-row groups (two per KV head): the 256-thread combine, row passes
+    (48, 2, 8, 4, 64),     # 96 units: the wide combine
+    (3, 2, 16, 6, 64),     # 12 units of 64 rows at D = 64: four share groups per unit
+])
+def test_decode_combine_paths(B, Hkv, N, G, D):
+    """Both combine variants (chosen by the unit count), each with units spanning several shares."""
+    rng = np.random.default_rng(B * 7 + D)
+    lens = [int(x) for x in rng.integers(1, 400, size=B)]
+    lens[0], lens[-1] = 16, 399
+    if B < 8:
+        lens = [6000, 4100, 33][:B]
+    case = gu.make_decode_case(lens, N, Hkv, G, D, seed=B + N + D, poison=gu.POISON_NAN)
+    out = gu.run_decode(case)
+    want = oracle.decode_from_logical(case["q"], case["K"], case["V"], 1.0 / math.sqrt(D))
+    assert max_err(out, want) <= TOL
+    assert int(case["status"].item()) == 0
+
+
 def test_decode_single_token_returns_v_exactly_and_empty_is_zero():
     lens = [1, 0, 1]
     case = gu.make_decode_case(lens, 3, 2, 4, 128, seed=5, poison=gu.POISON_NAN)
