@@ -10,8 +10,9 @@
 // session) unit are laid end to end — unit order (KV head, row group) then
 // session, pages in logical order — and the resulting list is cut into one
 // contiguous share per wave of a persistent grid (one 4-wave workgroup per CU;
-// shares weighted per XCD, see share_weight_before).  A wave streams its share through a per-wave LDS ring with direct
-// global->LDS 16-byte loads (S pages in flight, no registers held by loads),
+// shares weighted per XCD, see share_weight_before).  A wave streams its share
+// through a per-wave LDS ring with direct global->LDS 16-byte loads (S pages in
+// flight, no registers held by loads),
 // runs the page step of attn_core.h, and at every unit boundary either writes
 // the final output (unit wholly inside its share) or its partial softmax state
 // (m, l, acc) for decode_combine_kernel (unit crossing a share boundary).
