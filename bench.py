@@ -536,7 +536,7 @@ def cpu_baseline(wl, q, target_s):
         blas_threads = None
     B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     lens = wl.lens
-    order = sorted(range(B), key=lambda b: lens[b])[:: max(1, B // 16)]
+    order = sorted(range(B), key=lambda b: lens[b])[:: max(1, B // 32)]  # spread over the length mix
     cu = np.concatenate([[0], np.cumsum(lens)])
     total = int(cu[-1])
     k = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 10, 0)).view(total, Hkv, D)
