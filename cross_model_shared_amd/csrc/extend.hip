@@ -298,19 +298,24 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
   const int32_t* btrow = a.bt + int64_t(b) * a.bt_stride;
   const int num_pages = a.pool.num_pages;
   const int tid = threadIdx.x;
-  auto issue = [&](int k) {
+  // tile of page pid = lg_base + pid * page_stride (u32x4 units)
+  const u32x4* lg_base = reinterpret_cast<const u32x4*>(a.pool.data + tile_offset(layer, 0, g, num_pages, Hkv, D));
+  const uint32_t page_stride = uint32_t(Hkv) * (32 * D / 8);
+  auto issue_at = [&](int k, int stage) {
+    // both page ids of the block first, so their loads share one wait; with no
+    // second page the first is loaded again (never used unmasked)
+    int pid[2] = {load_uniform(btrow + 2 * k), load_uniform(btrow + (2 * k + 1 < npages ? 2 * k + 1 : 2 * k))};
+    if ((uint32_t(pid[0]) >= uint32_t(num_pages)) | (uint32_t(pid[1]) >= uint32_t(num_pages))) {
+      flag_error(a.dev_status, KVS_DEV_BAD_PAGE_BIT);
+      __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)  // in-range stand-in; the session's output is unspecified
+        if (uint32_t(pid[h]) >= uint32_t(num_pages)) pid[h] = 0;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      int p = 2 * k + h;
-      if (p >= npages) p = 2 * k;  // no second page: reload the first (never used unmasked)
-      int pid = load_uniform(btrow + p);
-      if (pid < 0 || pid >= num_pages) {
-        flag_error(a.dev_status, KVS_DEV_BAD_PAGE_BIT);
-        __builtin_amdgcn_s_waitcnt(0);
-        pid = 0;  // in-range stand-in; the session's output is unspecified
-      }
-      const u32x4* tile = reinterpret_cast<const u32x4*>(a.pool.data + tile_offset(layer, pid, g, num_pages, Hkv, D));
-      u32x4* dst = &ring[k % kStages][h * (TILE + kPad)];
+      const u32x4* tile = lg_base + uint64_t(uint32_t(pid[h])) * page_stride;
+      u32x4* dst = &ring[stage][h * (TILE + kPad)];
 #pragma unroll
       for (int j = 0; j < PER_PAGE; ++j)
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + j * THREADS + tid),
@@ -318,6 +323,7 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
                                          16, 0, 0);
     }
   };
+  auto issue = [&](int k) { issue_at(k, k % kStages); };
 
   ExtendState<D, NB> st;
   const float zero[NB] = {};
@@ -404,13 +410,15 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
     for (int k = 0; k < kLook && k < nblk; ++k) issue(k);
     if constexpr (!PIPE) {
       // one block at a time: prefetch k+kLook, wait for k, QK^T, softmax, PV
-      auto seq_step = [&](int k, bool fast) {
+      // stg: stage of block k; nxt: stage of block k + kLook (kept as counters)
+      auto seq_step = [&](int k, bool fast, int stg_i, int nxt) {
+        const u32x4* stg = ring[stg_i];
         f32x4 sc[2][NB];
         if (fast) {
-          issue(k + kLook);
+          issue_at(k + kLook, nxt);
           wait_vmcnt<PER_BLOCK * kLook>();
         } else {
-          if (k + kLook < nblk) issue(k + kLook);
+          if (k + kLook < nblk) issue_at(k + kLook, nxt);
           wait_blocks<PER_BLOCK>(min(nblk - 1, k + kLook) - k);
         }
         block_barrier();
@@ -421,9 +429,9 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
           float negm[NB];
 #pragma unroll
           for (int cb = 0; cb < NB; ++cb) negm[cb] = -st.m[cb];
-          qk_block<D, NB>(sc, qf, ring[k % kStages], koff, negm);
+          qk_block<D, NB>(sc, qf, stg, koff, negm);
         } else {
-          qk_block<D, NB>(sc, qf, ring[k % kStages], koff, zero);
+          qk_block<D, NB>(sc, qf, stg, koff, zero);
         }
         __builtin_amdgcn_s_setprio(0);
         const int kbase = k * 32;
@@ -432,11 +440,11 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
           // the first V runs are read now, so their LDS latency passes during the softmax
           u32x4 vpre[kVPre];
 #pragma unroll
-          for (int i = 0; i < kVPre; ++i) vpre[i] = v_operand(ring[k % kStages], i);
+          for (int i = 0; i < kVPre; ++i) vpre[i] = v_operand(stg, i);
           __builtin_amdgcn_sched_barrier(0);
           softmax_shifted<NB>(sc, pb);
           __builtin_amdgcn_s_setprio(2);
-          pv_block(ring[k % kStages], pb, kPage, kPage, false, std::integral_constant<int, kVPre>{}, vpre);
+          pv_block(stg, pb, kPage, kPage, false, std::integral_constant<int, kVPre>{}, vpre);
           __builtin_amdgcn_s_setprio(0);
           return;
         }
@@ -453,17 +461,38 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
         }
         const int nv0 = total - kbase, nv1 = total - kbase - 16;
         __builtin_amdgcn_s_setprio(2);
-        pv_block(ring[k % kStages], pb, nv0, nv1, nv1 < kPage, NoPre{}, no_vpre);
+        pv_block(stg, pb, nv0, nv1, nv1 < kPage, NoPre{}, no_vpre);
         __builtin_amdgcn_s_setprio(0);
       };
-      seq_step(0, false);
-      int k = 1;
+      auto bump = [](int x) { return x + 1 == kStages ? 0 : x + 1; };
+      seq_step(0, false, 0, kLook % kStages);
+      int k = 1, s_cur = 1 % kStages, s_nxt = (1 + kLook) % kStages;
       if (FAST) {
+        // up to a block whose stage is 0, then kStages blocks per iteration with constant stages
 #pragma unroll 1
-        for (; k < fast_end; ++k) seq_step(k, true);
+        for (; k < fast_end && s_cur != 0; ++k) {
+          seq_step(k, true, s_cur, s_nxt);
+          s_cur = bump(s_cur);
+          s_nxt = bump(s_nxt);
+        }
+#pragma unroll 1
+        for (; k + kStages <= fast_end; k += kStages) {
+#pragma unroll
+          for (int j = 0; j < kStages; ++j) seq_step(k + j, true, j, (j + kLook) % kStages);
+        }
+#pragma unroll 1
+        for (; k < fast_end; ++k) {
+          seq_step(k, true, s_cur, s_nxt);
+          s_cur = bump(s_cur);
+          s_nxt = bump(s_nxt);
+        }
       }
 #pragma unroll 1
-      for (; k < nblk; ++k) seq_step(k, false);
+      for (; k < nblk; ++k) {
+        seq_step(k, false, s_cur, s_nxt);
+        s_cur = bump(s_cur);
+        s_nxt = bump(s_nxt);
+      }
       return;
     }
     wait_blocks<PER_BLOCK>(min(kLook, nblk) - 1);
