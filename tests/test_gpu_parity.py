@@ -252,6 +252,22 @@ def test_extend_matches_oracle_ragged(D, G):
     assert np.array_equal(gu.pool_bits(c["pool"]), img)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_extend_bad_prefix_page_is_reported_without_faulting(D):
+    """An out-of-range page id in a cached prefix: flagged, no fault, the other sessions exact."""
+    prefix, new = [100, 60, 70], [20, 30, 1]
+    c = make_extend_case(prefix, new, 2, 4, D, seed=31 + D)
+    bt = c["bt"].copy()
+    bt[0, 1] = c["num_pages"] + 9      # prefix tokens 16..31 of session 0
+    out = gu.host_f64(run_extend(dict(c, bt=bt)))
+    assert int(c["status"].item()) & binding.DEV_BAD_PAGE
+    for b in (1, 2):
+        rows = slice(c["cu"][b], c["cu"][b + 1])
+        want = oracle.extend_from_logical(c["q"][rows], c["fk"][b], c["fv"][b], prefix[b], list(range(new[b])),
+                                          1.0 / math.sqrt(D))
+        assert float(np.max(np.abs(out[rows] - want))) <= TOL
+
+
 def test_extend_after_prefix_equals_full_prefill_and_chunked():
     prefix, new, G, D = [200], [150], 4, 128
     c = make_extend_case(prefix, new, 2, G, D, seed=31)
