@@ -576,7 +576,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path runs on a "
-              f"single MI355X; see the sharding notes in the design document)", file=sys.stderr)
+              f"single MI355X; sharding it over several GPUs is designed, not built)", file=sys.stderr)
         sys.exit(2)
     import torch
 
