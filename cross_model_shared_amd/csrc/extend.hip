@@ -540,7 +540,9 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
   for (int cb = 0; cb < NB; ++cb) bad |= !(st.lsum[cb][0] < kSafeSum);
   if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) redo = 1;
   __syncthreads();
-  if (redo) run(std::integral_constant<bool, false>{});
+  const bool do_redo = redo;
+  __syncthreads();  // every wave has read the flag before a rescaling pass reloads the ring over it
+  if (do_redo) run(std::integral_constant<bool, false>{});
 
   // the output rows are recomputed here from a fresh copy of the lane id, so that
   // no row address stays live (in registers or spilled) across the key walk
