@@ -66,6 +66,8 @@ def parse():
 DECODE_SOURCES = ["cross_model_shared_amd/csrc/decode.hip", "cross_model_shared_amd/csrc/attn_core.h",
                   "cross_model_shared_amd/csrc/kvs_device.h"]
 PMC_SUMMARY = "profiles/decode_qwen3_8b_n8_hbm_counters.md"
+EXTEND_SOURCES = ["cross_model_shared_amd/csrc/extend.hip", "cross_model_shared_amd/csrc/kvs_device.h"]
+EXTEND_PMC_SUMMARY = "profiles/extend_8k_512_counters.md"
 
 
 def kernel_source_hash(paths):
@@ -84,10 +86,10 @@ def kernel_source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed counter summary, if it was
+def summary_values(path, sources):
+    """The "Values read by bench.py" fields of a committed counter summary, if it was
     taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, PMC_SUMMARY)
+    path = os.path.join(ROOT, path)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -95,10 +97,29 @@ def measured_traffic():
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel_source_sha256") != kernel_source_hash(DECODE_SOURCES):
+    if fields.get("kernel_source_sha256") != kernel_source_hash(sources):
+        return None
+    return fields
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter summary (None if stale)."""
+    fields = summary_values(PMC_SUMMARY, DECODE_SOURCES)
+    try:
+        return float(fields["hbm_bytes_per_launch"]) if fields else None
+    except (KeyError, ValueError):
+        return None
+
+
+def extend_counters():
+    """Counter figures of one extend_8k_512 dispatch from the committed summary (None if stale)."""
+    fields = summary_values(EXTEND_PMC_SUMMARY, EXTEND_SOURCES)
+    if not fields:
         return None
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return {"hbm_bytes": float(fields["hbm_bytes_per_launch"]),
+                "mfma_flop_executed": float(fields["mfma_flop_per_launch"]),
+                "mfma_busy_frac": float(fields["mfma_busy_frac"])}
     except (KeyError, ValueError):
         return None
 
@@ -710,7 +731,10 @@ def main():
             "value": round(ext_tflops, 2), "unit": "TFLOP/s", "ms_per_call": round(ext_ms, 4),
             "flops": flops,
             "roofline": {"bound": "mfma", "achieved": round(ext_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(ext_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+                         "unit": "TFLOP/s", "frac": round(ext_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         # rocprofv3 counters of one dispatch (HBM bytes, matrix-core flop executed
+                         # and pipe-busy fraction), from the committed summary; null if stale
+                         "counters": extend_counters()},
         },
     }
     print(json.dumps(res), flush=True)
