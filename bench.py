@@ -34,6 +34,12 @@ PRIVATE_WORKLOAD = "qwen3_8b_n8_private"
 HANDOFF_WORKLOAD = "handoff_8k"
 CASCADE_WORKLOAD = "qwen3_8b_n8_cascade"
 LAYER_GROUP_WORKLOAD = "llama8b_layer_group"
+# the other decode workloads, one layer each: Llama-3.1-8B-shaped (N=4, 1K-8K tokens) and
+# Qwen3-14B-shaped long context (N=2, truncated log-normal lengths, mean 27K)
+CONFIG_DECODE_WORKLOADS = ("llama8b_n4", "qwen3_14b_long")
+# pool replicas a one-layer workload rotates over, so that no call finds its KV (or q, or
+# chunk rows) in the 256 MB infinity cache left there by the call before
+REPLICAS = 4
 
 
 def log(msg):
@@ -53,6 +59,14 @@ def parse():
     ap.add_argument("--no-cascade", action="store_true", help="skip the shared-prefix cascade section")
     ap.add_argument("--no-layer-group", action="store_true", help="skip the layer-group recompute section")
     ap.add_argument("--layer-group-calls", type=int, default=8)
+    ap.add_argument("--no-decode-configs", action="store_true",
+                    help="skip the llama8b_n4 and qwen3_14b_long decode sections")
+    ap.add_argument("--config-groups", type=int, default=40,
+                    help="timed groups of back-to-back calls per decode workload section")
+    ap.add_argument("--config-group-calls", type=int, default=5, help="calls per timed group")
+    ap.add_argument("--only", default=None,
+                    help="run one section alone and print its JSON (counter runs): a name in "
+                         "CONFIG_DECODE_WORKLOADS, or 'extend'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -66,6 +80,7 @@ def parse():
 DECODE_SOURCES = ["cross_model_shared_amd/csrc/decode.hip", "cross_model_shared_amd/csrc/attn_core.h",
                   "cross_model_shared_amd/csrc/kvs_device.h"]
 PMC_SUMMARY = "profiles/decode_qwen3_8b_n8_hbm_counters.md"
+CONFIG_PMC_SUMMARY = "profiles/decode_{}_hbm_counters.md"
 EXTEND_SOURCES = ["cross_model_shared_amd/csrc/extend.hip", "cross_model_shared_amd/csrc/kvs_device.h"]
 EXTEND_PMC_SUMMARY = "profiles/extend_8k_512_counters.md"
 
@@ -102,9 +117,9 @@ def summary_values(path, sources):
     return fields
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed counter summary (None if stale)."""
-    fields = summary_values(PMC_SUMMARY, DECODE_SOURCES)
+def measured_traffic(summary=PMC_SUMMARY):
+    """HBM bytes per decode launch from a committed counter summary (None if stale)."""
+    fields = summary_values(summary, DECODE_SOURCES)
     try:
         return float(fields["hbm_bytes_per_launch"]) if fields else None
     except (KeyError, ValueError):
@@ -253,6 +268,8 @@ def decode_step(wl, st, layers, timer=None, timed=()):
 
 
 def setup_extend(wl):
+    """REPLICAS layers of one pool, each holding every session's cached prefix, and a chunk
+    (q, k, v) per replica: call i extends layer i % REPLICAS with chunk i % REPLICAS."""
     import torch
 
     from cross_model_shared_amd import binding
@@ -261,31 +278,131 @@ def setup_extend(wl):
     B, Hq, Hkv, D = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     full = wl.total_lens()
     bt, num_pages = W.build_block_table(full, wl.seed)
-    pool = binding.Pool(1, num_pages, Hkv, D)
+    pool = binding.Pool(REPLICAS, num_pages, Hkv, D)
     btd = torch.from_numpy(bt).cuda()
     P = sum(wl.prefix)
     cu_p = torch.tensor(np.concatenate([[0], np.cumsum(wl.prefix)]), dtype=torch.int32, device="cuda")
-    kp = W.device_normal_bf16(P * Hkv * D, wl.std, W.mix_seed(wl.seed, 20)).view(P, Hkv, D)
-    vp = W.device_normal_bf16(P * Hkv * D, wl.std, W.mix_seed(wl.seed, 21)).view(P, Hkv, D)
-    binding.append(pool, 0, kp, vp, cu_p, btd, torch.zeros(B, dtype=torch.int32, device="cuda"),
-                   max_new=max(wl.prefix), max_seq_len=max(full))
+    for r in range(REPLICAS):
+        kp = W.device_normal_bf16(P * Hkv * D, wl.std, W.mix_seed(wl.seed, 20, r)).view(P, Hkv, D)
+        vp = W.device_normal_bf16(P * Hkv * D, wl.std, W.mix_seed(wl.seed, 21, r)).view(P, Hkv, D)
+        binding.append(pool, r, kp, vp, cu_p, btd, torch.zeros(B, dtype=torch.int32, device="cuda"),
+                       max_new=max(wl.prefix), max_seq_len=max(full))
+        del kp, vp
     T = sum(wl.new)
-    q = W.device_normal_bf16(T * Hq * D, wl.std, W.mix_seed(wl.seed, 22)).view(T, Hq, D)
-    kn = W.device_normal_bf16(T * Hkv * D, wl.std, W.mix_seed(wl.seed, 23)).view(T, Hkv, D)
-    vn = W.device_normal_bf16(T * Hkv * D, wl.std, W.mix_seed(wl.seed, 24)).view(T, Hkv, D)
+    q = [W.device_normal_bf16(T * Hq * D, wl.std, W.mix_seed(wl.seed, 22, r)).view(T, Hq, D) for r in range(REPLICAS)]
+    kn = [W.device_normal_bf16(T * Hkv * D, wl.std, W.mix_seed(wl.seed, 23, r)).view(T, Hkv, D) for r in range(REPLICAS)]
+    vn = [W.device_normal_bf16(T * Hkv * D, wl.std, W.mix_seed(wl.seed, 24, r)).view(T, Hkv, D) for r in range(REPLICAS)]
     cu = torch.tensor(np.concatenate([[0], np.cumsum(wl.new)]), dtype=torch.int32, device="cuda")
-    out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    out = [torch.empty((T, Hq, D), dtype=torch.bfloat16, device="cuda") for _ in range(REPLICAS)]
     pre = torch.tensor(wl.prefix, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
     return dict(pool=pool, bt=btd, q=q, kn=kn, vn=vn, cu=cu, out=out, pre=pre, max_new=max(wl.new),
                 msl=max(full))
 
 
-def extend_call(wl, st):
+def extend_call(wl, st, i=0):
     from cross_model_shared_amd import binding
 
-    binding.extend(st["pool"], 0, st["q"], st["kn"], st["vn"], st["out"], st["cu"], st["bt"], st["pre"],
+    r = i % REPLICAS
+    binding.extend(st["pool"], r, st["q"][r], st["kn"][r], st["vn"][r], st["out"][r], st["cu"], st["bt"], st["pre"],
                    st["max_new"], st["msl"], wl.scale)
+
+
+def fill_pool_layer(pool, layer, wl, lens, bt_dev, stream_key):
+    """Seeded N(0, std) K/V for every session's tokens, written into one pool layer with
+    kv_pool_append (device draws; the oracle checks such pools in the full-size tests)."""
+    import torch
+
+    from cross_model_shared_amd import binding
+    from cross_model_shared_amd import workload as W
+
+    B, Hkv, D = len(lens), wl.num_kv_heads, wl.head_dim
+    total = int(sum(lens))
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    k = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, stream_key, layer)).view(total, Hkv, D)
+    v = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, stream_key + 1, layer)).view(total, Hkv, D)
+    binding.append(pool, layer, k, v, cu, bt_dev, torch.zeros(B, dtype=torch.int32, device="cuda"),
+                   max_new=max(max(lens), 1), max_seq_len=max(max(lens), 1))
+    del k, v
+
+
+def grouped_call_ms(fn, groups, per_group, warmup=20):
+    """Per-call times of `fn(i)` run back to back: `groups` groups of `per_group` calls, one
+    pair of HIP events (on the current stream) around each group.  Returns the per-call
+    time of every group (group time / per_group), in ms."""
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t = EventTimer()
+    i = 0
+    for _ in range(groups):
+        e = t.start()
+        for _ in range(per_group):
+            fn(i)
+            i += 1
+        t.stop(e)
+    torch.cuda.synchronize()
+    return [ms / per_group for ms in t.all_ms()]
+
+
+def decode_config_section(name, groups, per_group):
+    """shared_kv_decode on one layer of a decode workload, rotating over REPLICAS pool
+    replicas (layers of one pool, each with its own queries); plus time(N)/time(1) at
+    fixed KV (one decoder's queries over the same pages)."""
+    import torch
+
+    from cross_model_shared_amd import binding
+    from cross_model_shared_amd import workload as W
+
+    wl = W.make_workload(name)
+    B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    lens = wl.lens
+    bt, num_pages = W.build_block_table(lens, wl.seed)
+    pool = binding.Pool(REPLICAS, num_pages, Hkv, D)
+    d_bt = torch.from_numpy(bt).cuda()
+    d_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    for r in range(REPLICAS):
+        fill_pool_layer(pool, r, wl, lens, d_bt, 10)
+    q = [W.device_normal_bf16(B * N * Hq * D, wl.std, W.mix_seed(wl.seed, 12, r)).view(B, N, Hq, D)
+         for r in range(REPLICAS)]
+    q1 = [x[:, :1].contiguous() for x in q]
+    out, out1 = torch.empty_like(q[0]), torch.empty_like(q1[0])
+    maxL = max(lens)
+    ws = binding.decode_workspace(B, N, Hq, Hkv, D, maxL)
+    ws1 = binding.decode_workspace(B, 1, Hq, Hkv, D, maxL)
+    torch.cuda.synchronize()
+
+    def call(i):
+        binding.decode(pool, i % REPLICAS, q[i % REPLICAS], out, d_bt, d_lens, maxL, wl.scale, ws)
+
+    def call1(i):
+        binding.decode(pool, i % REPLICAS, q1[i % REPLICAS], out1, d_bt, d_lens, maxL, wl.scale, ws1)
+
+    per = grouped_call_ms(call, groups, per_group)
+    per1 = grouped_call_ms(call1, groups, per_group)
+    ms, ms1 = float(np.median(per)), float(np.median(per1))
+    nbytes = decode_bytes(lens, B, N, Hq, Hkv, D)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] {name} decode call {ms * 1e3:.1f} us ({gbs:.0f} GB/s), N=1 {ms1 * 1e3:.1f} us")
+    res = {
+        "workload": f"{name}: one layer, B={B} sessions, N={N} decoders, {Hq} q / {Hkv} KV heads, D={D}, page 16, "
+                    f"lengths {'log-uniform [1024, 8192]' if name == 'llama8b_n4' else 'truncated log-normal mean 27K in [4096, 131072]'} "
+                    f"(sum {sum(lens)}, max {maxL}); shared_kv_decode rotating over {REPLICAS} pool replicas",
+        "value": round(gbs, 1), "unit": "GB/s", "ms_per_call": round(ms, 5), "bytes_per_call": nbytes,
+        "ms_per_call_p10_p50_p90": [round(float(np.percentile(per, x)), 5) for x in (10, 50, 90)],
+        "calls": groups * per_group,
+        "timing": f"{groups} groups of {per_group} back-to-back calls, HIP events around each group",
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(CONFIG_PMC_SUMMARY.format(name))},
+        "decoder_concat": {f"time_N{N}_over_N1": round(ms / ms1, 3), f"ms_N{N}": round(ms, 5),
+                           "ms_N1": round(ms1, 5)},
+    }
+    del pool, q, q1
+    torch.cuda.empty_cache()
+    return res
 
 
 def private_section(calls):
@@ -610,6 +727,21 @@ def main():
     binding.load()
     if args.calibrate_copy:
         calibrate_copy()
+    if args.only:  # one section alone (counter runs): its dispatches are the run's only ones of its kernel
+        if args.only in CONFIG_DECODE_WORKLOADS:
+            res = decode_config_section(args.only, args.config_groups, args.config_group_calls)
+        elif args.only == "extend":
+            ew = W.make_workload(EXTEND_WORKLOAD)
+            es = setup_extend(ew)
+            for i in range(args.extend_calls):
+                extend_call(ew, es, i)
+            torch.cuda.synchronize()
+            res = {"workload": EXTEND_WORKLOAD, "calls": args.extend_calls}
+        else:
+            print(f"--only {args.only}: unknown section", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"only": args.only, **res}), flush=True)
+        return
     wl = W.make_workload(DECODE_WORKLOAD)
     layers = args.layers or wl.num_layers
     B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
@@ -664,20 +796,26 @@ def main():
     # ---- extend ----
     ew = W.make_workload(EXTEND_WORKLOAD)
     es = setup_extend(ew)
-    for _ in range(args.extend_warmup):  # ~1 ms each: brings the clocks to their steady state
-        extend_call(ew, es)
+    for i in range(args.extend_warmup):  # ~1 ms each: brings the clocks to their steady state
+        extend_call(ew, es, i)
     torch.cuda.synchronize()
     et = EventTimer()
-    for _ in range(args.extend_calls):
+    for i in range(args.extend_calls):
         e = et.start()
-        extend_call(ew, es)
+        extend_call(ew, es, i)
         et.stop(e)
     torch.cuda.synchronize()
     ext_ms = float(np.median(et.all_ms()))
+    ext_p = [round(float(np.percentile(et.all_ms(), x)), 5) for x in (10, 50, 90)]
+    del es
+    torch.cuda.empty_cache()
     flops = extend_flops(ew.prefix, ew.new, ew.num_q_heads, ew.head_dim)
     ext_tflops = flops / (ext_ms * 1e-3) / 1e12
     log(f"[bench] extend call {ext_ms:.3f} ms, {ext_tflops:.1f} TFLOP/s")
 
+    configs = {} if args.no_decode_configs else {
+        name: decode_config_section(name, args.config_groups, args.config_group_calls)
+        for name in CONFIG_DECODE_WORKLOADS}
     private = None if args.no_private else private_section(args.private_calls)
     handoff = None if args.no_handoff else handoff_section(10)
     cascade = None if args.no_cascade else cascade_section(20)
@@ -721,6 +859,7 @@ def main():
                            "ms_N1": round(n1_ms, 4)},
         "footprint": {"pool_GB": round(pool_gb, 2), "n_private_copies_GB": round(pool_gb * N, 2),
                       "ratio": N},
+        "decode_configs": configs,
         "private": private,
         "handoff": handoff,
         "cascade": cascade,
@@ -729,6 +868,8 @@ def main():
             "workload": f"{EXTEND_WORKLOAD}: B=16, cached prefix 8192 + 512 new tokens, 32 q / 8 KV heads, "
                         f"D=128 (partial_prefill_extend = append chunk + causal attention)",
             "value": round(ext_tflops, 2), "unit": "TFLOP/s", "ms_per_call": round(ext_ms, 4),
+            "ms_per_call_p10_p50_p90": ext_p, "calls": args.extend_calls,
+            "timing": f"HIP events around each call; calls rotate over {REPLICAS} pool replicas and chunks",
             "flops": flops,
             "roofline": {"bound": "mfma", "achieved": round(ext_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(ext_tflops / MFMA_BF16_PEAK_TFLOPS, 4),

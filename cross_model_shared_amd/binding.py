@@ -38,6 +38,7 @@ _SIGNATURES = {
     "kv_pool_append": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                       _i32, _vp, _vp]),
     "shared_kv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "shared_kv_decode_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
     "shared_kv_decode": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                         _f, _vp, _sz, _vp, _vp]),
     "shared_kv_decode_append": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
@@ -173,6 +174,22 @@ def append(pool: Pool, layer, k_new, v_new, cu_new, block_table, seq_lens, max_n
 def decode_workspace_bytes(batch, num_decoders, num_q_heads, num_kv_heads, head_dim, max_seq_len) -> int:
     return load().shared_kv_decode_workspace_bytes(batch, num_decoders, num_q_heads, num_kv_heads,
                                                    head_dim, max_seq_len)
+
+
+def decode_workspace_init(workspace, stream=None):
+    """Zero a decode workspace's arrival counters (needed once, before its first call,
+    unless the buffer was allocated zero-filled)."""
+    _check(load().shared_kv_decode_workspace_init(_ptr(workspace, "workspace"),
+                                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def decode_workspace(batch, num_decoders, num_q_heads, num_kv_heads, head_dim, max_seq_len, device="cuda"):
+    """A zero-filled uint8 device tensor of decode_workspace_bytes: ready for every decode call."""
+    torch = _torch()
+    nbytes = decode_workspace_bytes(batch, num_decoders, num_q_heads, num_kv_heads, head_dim, max_seq_len)
+    if nbytes == 0:
+        raise ValueError("invalid decode bounds")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def decode(pool: Pool, layer, q, out, block_table, seq_lens, max_seq_len, scale, workspace,

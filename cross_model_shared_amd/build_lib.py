@@ -26,10 +26,11 @@ COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
     # packed fp32 arithmetic stays off in all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # no NaN canonicalization around max/min: masked scores are -inf, never NaN
-    "-fno-honor-nans",
     "-I", os.path.join(ROOT, "include"),
 ]
+# Kernel sources only: no NaN canonicalization around max/min (masked scores
+# are -inf, never NaN).  The host-side C ABI checks keep IEEE NaN semantics.
+KERNEL_FLAGS = ["-fno-honor-nans"]
 
 
 def hipcc() -> str:
@@ -44,6 +45,8 @@ def _compile(src: str) -> str:
     cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
+    else:
+        cmd[1:1] = KERNEL_FLAGS
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)  # host pass does not know the feature

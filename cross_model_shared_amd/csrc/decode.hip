@@ -15,7 +15,8 @@
 // flight, no registers held by loads),
 // runs the page step of attn_core.h, and at every unit boundary either writes
 // the final output (unit wholly inside its share) or its partial softmax state
-// (m, l, acc) for decode_combine_kernel (unit crossing a share boundary).
+// (m, l, acc) (unit crossing a share boundary); the last wave to finish a split
+// unit merges its shares' states (finish_split), so a call is one launch.
 //
 // Decoder-private suffixes (PrefillShare, section 3.3: each decoder extends
 // C_base with its own generated tokens; Eq. 9 keeps the prefix once and the
@@ -295,40 +296,179 @@ __device__ __forceinline__ void load_q(QFrag<D, NB>& qf, const DecodeArgs& a, in
   }
 }
 
+// Output rows of column block cb of a unit from a merged state: out = acc / den,
+// bf16 (den = 0: zeros).
+template <int D, int NB, int MODE>
+__device__ __forceinline__ void store_block(const DecodeArgs& a, const f32x4 (&acc)[D / 16], float den, int cb,
+                                            int b, int g, int rg, int lane) {
+  const int64_t row = unit_row<MODE>(a, b, g, rg * 16 * NB + cb * 16 + (lane & 15));
+  if (row < 0) return;
+  uint16_t* o = a.out + row * D;
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    const f32x4 v = acc[i] * inv;
+    *reinterpret_cast<u32x2*>(o + 16 * i + 4 * (lane >> 4)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// A unit held wholly by one wave: its state is final.
 template <int D, int NB, int MODE>
 __device__ __forceinline__ void write_rows(const DecodeArgs& a, const RowState<D, NB>& st, int b, int g,
                                            int rg, int lane) {
+  float den[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) den[cb] = wave_sum_across_quads(st.l[cb]);  // every lane takes part
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) store_block<D, NB, MODE>(a, st.acc[cb], den[cb], cb, b, g, rg, lane);
+}
+
+// Partial-state slot `slot` (16*NB rows): the accumulators in matrix-core
+// fragment order (fragment (cb, i) is a contiguous 1 KiB, lane-major), then
+// (m, l) per row.
+//
+// A partial state is written by a wave on one XCD and read, in the same
+// launch, by the merging wave, which may sit on another XCD with its own L2.
+// Both sides use device-scope buffer accesses (the sc1 cache-policy bit): the
+// store is written through to where every XCD sees it, the load does not hit a
+// stale line in its own L2.  The writer waits for its stores to complete before
+// it arrives at the unit's counter; the merger loads only after the counter
+// told it that every share has arrived.  No whole-L2 write-back or invalidate
+// is needed (agent-scope fences cost tens of microseconds per call here).
+constexpr int kDeviceScope = 16;       // sc1 in the buffer intrinsics' cache-policy argument
+constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer descriptor: raw 32-bit elements
+
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t acc_rsrc(const DecodeArgs& a) {
+  // 2 slots per share, up to 2 row groups of 32 per slot on wave pairs: 2^11 * 64 rows * D floats
+  return __builtin_amdgcn_make_buffer_rsrc(a.ws_acc, 0, int((2 << kDecodeShareLog2) * 64 * D * 4), kBufferWord3);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ml_rsrc(const DecodeArgs& a) {
+  return __builtin_amdgcn_make_buffer_rsrc(a.ws_ml, 0, int((2 << kDecodeShareLog2) * 64 * 2 * 4), kBufferWord3);
+}
+// Byte offset of fragment (cb, i) in slot `slot`: wave-uniform, so it goes in the
+// scalar offset of the buffer access (the lane's part, 16 * lane, is the vector
+// offset), which keeps the per-fragment offsets out of vector registers.
+template <int D, int NB>
+__device__ __forceinline__ int acc_soff(int64_t slot, int cb, int i) {
+  return __builtin_amdgcn_readfirstlane(int(slot * (16 * NB) * D * 4)) + (cb * (D / 16) + i) * kWave * 16;
+}
+template <int NB>
+__device__ __forceinline__ int ml_off(int64_t slot, int r) {
+  return int(slot * (16 * NB) * 2 * 4) + r * 8;
+}
+
+template <int D, int NB>
+__device__ __forceinline__ void write_partial(const DecodeArgs& a, const RowState<D, NB>& st, int64_t slot,
+                                              int lane) {
+  const __amdgpu_buffer_rsrc_t racc = acc_rsrc<D>(a), rml = ml_rsrc(a);
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     const float l = wave_sum_across_quads(st.l[cb]);
-    const int64_t row = unit_row<MODE>(a, b, g, rg * 16 * NB + cb * 16 + (lane & 15));
-    if (row < 0) continue;
-    uint16_t* o = a.out + row * D;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) {
-      const f32x4 v = st.acc[cb][i] * inv;
-      *reinterpret_cast<u32x2*>(o + 16 * i + 4 * (lane >> 4)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+    for (int i = 0; i < D / 16; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(st.acc[cb][i], racc, lane * 16, acc_soff<D, NB>(slot, cb, i),
+                                             kDeviceScope);
+    if (lane < 16) {  // two 4-byte stores: a vector built from st.m kept RowState in scratch
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(st.m[cb]), rml, ml_off<NB>(slot, cb * 16 + lane), 0,
+                                            kDeviceScope);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), rml, ml_off<NB>(slot, cb * 16 + lane) + 4, 0,
+                                            kDeviceScope);
     }
   }
 }
 
-template <int D, int NB>
-__device__ __forceinline__ void write_partial(const DecodeArgs& a, const RowState<D, NB>& st, int slot,
-                                              int lane) {
-  constexpr int RG = 16 * NB;
-  float* acc = a.ws_acc + int64_t(slot) * RG * D;
-  float* ml = a.ws_ml + int64_t(slot) * RG * 2;
-#pragma unroll
+// The end of a wave's part of a unit that other shares also hold.  The wave
+// has stored its partial state (m, l, acc) with write_partial; it waits for
+// those stores, then adds its tile count to the unit's arrival counter with a
+// vector atomic; the wave whose addition completes the unit's npg tiles merges
+// the states of all the unit's shares k0..k1, in share order:
+//   m* = max m_s,  out = sum_s 2^(m_s - m*) acc_s / sum_s 2^(m_s - m*) l_s.
+// The order is fixed, so the result does not depend on which wave arrives
+// last.  The merging wave puts the counter back to zero, so every counter is
+// zero again when the call ends.  A share begins at most one unit that it does
+// not finish, so a split unit's counter is indexed by its first share k0:
+// counter k0*mul + add, and share k's partial slot (2k + x)*mul + add, x = 0
+// for the unit a share continues, 1 for the one it begins (mul = 1, add = 0 on
+// the stream kernel; mul = 2, add = the row group on wave pairs).
+template <int D, int NB, int MODE, int WPG, int KB>
+__device__ __forceinline__ void finish_split(const DecodeArgs& a, int k, bool before, int mul, int add, int mine,
+                                             int npg, int64_t s_u, int64_t T, int b, int g, int rg, int lane) {
+  const int k0 = before ? share_of<WPG>(s_u, T) : k;
+  int* ctr = a.ws_cnt + k0 * mul + add;
+  // the partial state has reached device scope before the arrival does
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(ctr, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __builtin_amdgcn_readlane(old, 0);
+  if (old + mine != npg) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const int k1 = share_of<WPG>(s_u + npg - 1, T);
+  const __amdgpu_buffer_rsrc_t racc = acc_rsrc<D>(a), rml = ml_rsrc(a);
+  // one 16-row column block at a time (fewer live registers); shares in
+  // batches of KB, every load of a batch issued before any merge
+#pragma unroll 1
   for (int cb = 0; cb < NB; ++cb) {
-    const float l = wave_sum_across_quads(st.l[cb]);
-    const int r = cb * 16 + (lane & 15);
+    float M = -INFINITY, den = 0.f;
+    f32x4 acc[D / 16];
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i)
-      *reinterpret_cast<f32x4*>(acc + r * D + 16 * i + 4 * (lane >> 4)) = st.acc[cb][i];
-    if (lane < 16) {
-      ml[r * 2 + 0] = st.m[cb];
-      ml[r * 2 + 1] = l;
+    for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int kb = k0; kb <= k1; kb += KB) {
+      f32x2 mlv[KB];
+      f32x4 av[KB][D / 16];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int kk = min(kb + u, k1);
+        const int64_t slot = int64_t(kk * 2 + (kk == k0 ? 1 : 0)) * mul + add;
+        const u32x2 mlb = __builtin_amdgcn_raw_buffer_load_b64(rml, ml_off<NB>(slot, cb * 16 + (lane & 15)), 0,
+                                                               kDeviceScope);
+        mlv[u] = f32x2{__uint_as_float(mlb[0]), __uint_as_float(mlb[1])};
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i)
+          av[u][i] = __builtin_amdgcn_raw_buffer_load_b128(racc, lane * 16, acc_soff<D, NB>(slot, cb, i), kDeviceScope);
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int kk = kb + u;
+        // past k1, a share without tiles (it wrote nothing), or one that saw no key of this row
+        if (kk > k1 || share_start<WPG>(kk, T) == share_start<WPG>(kk + 1, T) || mlv[u][0] == -INFINITY) continue;
+        const float Mn = fmaxf(M, mlv[u][0]);
+        const float c = exp2_fast(M - Mn), w = exp2_fast(mlv[u][0] - Mn);  // exp2(-inf) = 0
+        den = den * c + w * mlv[u][1];
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) acc[i] = acc[i] * c + w * av[u][i];
+        M = Mn;
+      }
+    }
+    store_block<D, NB, MODE>(a, acc, den, cb, b, g, rg, lane);
+  }
+  if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Loads of a batch's padding (shares past k1) are never consumed: wait for
+  // them here, or the compiler waits for every outstanding load before the
+  // ring's next LDS read, on every page, to protect their registers.
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Zeros for the rows of units without tiles (softmax over nothing): units
+// idx = first, first + step, ... of nunits; unit idx is (gr = idx / nb_units,
+// b = idx % nb_units), empty(b) tells whether it has no tiles.
+template <int D, int NB, int MODE, class Empty>
+__device__ __forceinline__ void zero_empty_units(const DecodeArgs& a, int nunits, int nb_units, int rowgroups,
+                                                 int rg_fixed, int first, int step, const Empty& empty,
+                                                 int lane) {
+  constexpr int RG = 16 * NB, CH = D / 8;  // 16-byte chunks per row
+#pragma unroll 1
+  for (int idx = first; idx < nunits; idx += step) {
+    const int b = idx % nb_units, gr = idx / nb_units;
+    if (!empty(b)) continue;
+    const int g = rg_fixed >= 0 ? gr : gr / rowgroups, rg = rg_fixed >= 0 ? rg_fixed : gr % rowgroups;
+#pragma unroll 1
+    for (int e = lane; e < RG * CH; e += kWave) {
+      const int64_t row = unit_row<MODE>(a, b, g, rg * RG + e / CH);
+      if (row >= 0) reinterpret_cast<u32x4*>(a.out + row * D)[e % CH] = u32x4{0u, 0u, 0u, 0u};
     }
   }
 }
@@ -405,13 +545,16 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
     if (tid == 255) cum_s[B] = run;
   }
   __syncthreads();
-  if (blockIdx.x == 0)
-    for (int b = tid; b <= B; b += 256) a.ws_cum[b] = cum_s[b];
-  __builtin_amdgcn_s_waitcnt(0);  // nothing outstanding before the ring starts
 
   const int Ptot = cum_s[B];
   const int64_t T = int64_t(Ptot) * Hkv * RGs;
   const int k = blockIdx.x * kWaves + wave;  // the grid is kDecodeBlocks workgroups
+  zero_empty_units<D, NB, MODE>(a, Hkv * RGs * B, B, RGs, -1, k, kWaves * kDecodeBlocks,
+                                [&](int b) { return cum_s[b + 1] == cum_s[b]; }, lane);
+  // Nothing outstanding before the ring starts.  (Without this wait the
+  // compiler also waits for every outstanding load before a ring page's LDS
+  // reads, on every page.)
+  __builtin_amdgcn_s_waitcnt(0);
   const int64_t tau0 = share_start<kWaves>(k, T), tau1 = share_start<kWaves>(k + 1, T);
   if (tau0 >= tau1) return;  // no barriers follow
   const int n = int(tau1 - tau0);
@@ -471,6 +614,9 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
     }
   };
 
+  // Queries (and the step's token) are waited for before the ring (re)starts:
+  // a q load still in flight at the loop head would make the compiler wait for
+  // every outstanding load before each page's first matrix step.
   QFrag<D, NB> qf;
   RowState<D, NB> st;
   st.init();
@@ -528,12 +674,15 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
     const bool last = (j == n - 1);
     if (last || cw.gr != cur_gr || cw.b != cur_b) {
       // unit (cur_gr, cur_b) ends here for this wave
-      const int64_t unit_end = unit_begin + (cum_s[cur_b + 1] - cum_s[cur_b]);
+      const int npg_u = cum_s[cur_b + 1] - cum_s[cur_b];
+      const int64_t unit_end = unit_begin + npg_u;
       const bool before = unit_begin < tau0, after = unit_end > tau1;
       if (!before && !after) {
         write_rows<D, NB, MODE>(a, st, cur_b, cur_gr / RGs, cur_gr % RGs, lane);
       } else {
         write_partial<D, NB>(a, st, k * 2 + (before ? 0 : 1), lane);
+        finish_split<D, NB, MODE, kWaves, (NB >= 4 ? 1 : 4 / NB)>(a, k, before, 1, 0, int(min(unit_end, tau1) - max(unit_begin, tau0)),
+                                             npg_u, unit_begin, T, cur_b, cur_gr / RGs, cur_gr % RGs, lane);
       }
       if (!last) {
         st.init();
@@ -571,6 +720,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int Ptot = cum(B);
   const int64_t T = int64_t(Ptot) * Hkv;
   const int k = blockIdx.x;  // the grid is one pair per share
+  // each wave zeroes its own rows of units without tiles
+  zero_empty_units<D, NB, MODE>(a, Hkv * B, B, 1, rg, k, 1 << kDecodeShareLog2,
+                                [&](int u) { return cum(u + 1) == cum(u); }, lane);
   const int64_t tau0 = share_start<1>(k, T), tau1 = share_start<1>(k + 1, T);
   if (tau0 >= tau1) return;  // both waves alike: no barriers follow
   const int n = int(tau1 - tau0);
@@ -654,12 +806,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
     const bool last = (j == n - 1);
     if (last || cw.gr != cur_gr || cw.b != cur_b) {
       // unit (cur_gr, cur_b) ends here for this pair
-      const int64_t unit_end = unit_begin + (cum(cur_b + 1) - cum(cur_b));
+      const int npg_u = cum(cur_b + 1) - cum(cur_b);
+      const int64_t unit_end = unit_begin + npg_u;
       const bool before = unit_begin < tau0, after = unit_end > tau1;
       if (!before && !after) {
         write_rows<D, NB, MODE>(a, st, cur_b, cur_gr, rg, lane);
-      } else {
+      } else {  // each wave of the pair merges its own row group
         write_partial<D, NB>(a, st, (k * 2 + (before ? 0 : 1)) * 2 + rg, lane);
+        finish_split<D, NB, MODE, 1, 1>(a, k, before, 2, rg, int(min(unit_end, tau1) - max(unit_begin, tau0)),
+                                        npg_u, unit_begin, T, cur_b, cur_gr, rg, lane);
       }
       if (!last) {
         st.init();
@@ -668,169 +823,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
         unit_begin = int64_t(cw.gr) * Ptot + cum(cw.b);
       }
     }
-  }
-}
-
-constexpr int kCombineWideThreads = 1024;
-
-// The WIDE combine of one unit whose shares are k0..k1 (see decode_combine_kernel).
-template <int D, int MODE>
-__device__ __forceinline__ void combine_wide(const DecodeArgs& a, int b, int g, int rg, int RG, int k0, int k1,
-                                             int64_t T) {
-  constexpr bool kPair = MODE == kCascade;
-  constexpr int WPG = kPair ? 1 : kWaves;
-  constexpr int TPR = D / 16;                  // threads per row
-  const int rows_t = RG * TPR;                 // threads of one group: 64 .. 512
-  const int groups = kCombineWideThreads / rows_t;
-  const int grp = threadIdx.x / rows_t, w = threadIdx.x % rows_t;
-  const int rl = w / TPR, tc = w % TPR;
-  const int64_t row = unit_row<MODE>(a, b, g, rg * RG + rl);
-  auto empty = [&](int k) { return share_start<WPG>(k, T) == share_start<WPG>(k + 1, T); };
-  auto slot_of = [&](int k) { return int64_t(k * 2 + (k == k0)) * (kPair ? 2 : 1) + (kPair ? rg : 0); };
-  float M = -INFINITY, den = 0.f;
-  f32x4 num[4] = {};
-  if (row >= 0) {
-    // this group's shares in batches of KB: every load of a batch is issued before any merge
-    constexpr int KB = 4;
-#pragma unroll 1
-    for (int kb = k0 + grp; kb <= k1; kb += KB * groups) {
-      f32x2 mlv[KB];
-      f32x4 av[KB][4];
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int64_t slot = slot_of(min(kb + u * groups, k1));
-        mlv[u] = *reinterpret_cast<const f32x2*>(a.ws_ml + (slot * RG + rl) * 2);
-        const f32x4* ap = reinterpret_cast<const f32x4*>(a.ws_acc + (slot * RG + rl) * D) + 4 * tc;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) av[u][i] = ap[i];
-      }
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int k = kb + u * groups;
-        if (k > k1 || empty(k) || mlv[u][0] == -INFINITY) continue;
-        const float Mn = fmaxf(M, mlv[u][0]);
-        const float c = exp2_fast(M - Mn), wt = exp2_fast(mlv[u][0] - Mn);  // exp2(-inf) = 0
-        den = den * c + wt * mlv[u][1];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) num[i] = num[i] * c + wt * av[u][i];
-        M = Mn;
-      }
-    }
-  }
-  // the groups' states, merged by group 0 (every thread reaches the barrier)
-  __shared__ float sm[kCombineWideThreads], sden[kCombineWideThreads];
-  __shared__ f32x4 snum[4][kCombineWideThreads];
-  sm[threadIdx.x] = M;
-  sden[threadIdx.x] = den;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) snum[i][threadIdx.x] = num[i];
-  __syncthreads();
-  if (grp != 0 || row < 0) return;
-  for (int j = 1; j < groups; ++j) {
-    const int t = j * rows_t + w;
-    const float mj = sm[t];
-    if (mj == -INFINITY) continue;
-    const float Mn = fmaxf(M, mj);
-    const float c = exp2_fast(M - Mn), wt = exp2_fast(mj - Mn);
-    den = den * c + wt * sden[t];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) num[i] = num[i] * c + wt * snum[i][t];
-    M = Mn;
-  }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  u32x2* o = reinterpret_cast<u32x2*>(a.out + row * D) + 4 * tc;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x4(num[i][0] * inv, num[i][1] * inv, num[i][2] * inv, num[i][3] * inv);
-}
-
-// Merge the partial states of units that cross share boundaries:
-// m* = max m_s, out = sum_s 2^(m_s - m*) acc_s / sum_s 2^(m_s - m*) l_s.
-// Also writes zeros for empty units (softmax over nothing).  A thread takes
-// one row and 16 consecutive head dims (64 contiguous bytes of every share's
-// partial accumulator) and merges shares in one online pass.
-//  - 256 threads per unit: the unit's rows in passes, all its shares per thread.
-//  - WIDE, for calls with few units (each then spans many shares, up to ~75
-//    for a 128K-token session): 1024 threads per unit, i.e. 1024 / (rows*D/16)
-//    groups, group j merging shares k0 + j, k0 + j + groups, ...; the groups'
-//    states are merged through LDS.  Fewer dependent loads per thread.
-template <int D, int MODE, bool WIDE>
-__global__ __launch_bounds__(WIDE ? kCombineWideThreads : 256) void decode_combine_kernel(DecodeArgs a) {
-  const int Hkv = a.pool.num_kv_heads, RGs = a.plan.rowgroups;
-  const int B = MODE == kCascade ? load_uniform(a.ws_units + 3 * a.batch) : a.batch;
-  const int unit = blockIdx.x;  // (gr, b) with b fastest, over the launch's batch
-  const int b = unit % a.batch, gr = unit / a.batch;
-  if (b >= B) return;
-  const int g = gr / RGs, rg = gr % RGs;
-  const int RG = a.plan.rg_rows;
-  const int Ptot = load_uniform(a.ws_cum + B);
-  const int cb0 = load_uniform(a.ws_cum + b);
-  const int npg = load_uniform(a.ws_cum + b + 1) - cb0;
-  // shares: one per wave (plain, private) or per wave pair (cascade: the tile
-  // list is per KV head, and each share's slots are split by row group)
-  constexpr bool kPair = MODE == kCascade;
-  if (npg == 0) {
-    for (int e = threadIdx.x; e < RG * (D / 8); e += blockDim.x) {
-      const int64_t row = unit_row<MODE>(a, b, g, rg * RG + e / (D / 8));
-      if (row < 0) continue;
-      reinterpret_cast<u32x4*>(a.out + row * D)[e % (D / 8)] = u32x4{0u, 0u, 0u, 0u};
-    }
-    return;
-  }
-  const int64_t T = int64_t(Ptot) * Hkv * (kPair ? 1 : RGs);
-  const int64_t s_u = int64_t(kPair ? g : gr) * Ptot + cb0, e_u = s_u + npg;
-  constexpr int WPG = kPair ? 1 : kWaves;  // shares per workgroup of the streaming kernel
-  const int k0 = share_of<WPG>(s_u, T), k1 = share_of<WPG>(e_u - 1, T);
-  if (k0 == k1) return;  // written directly by its wave
-  // shares between k0 and k1 that hold no tile (T < 1024) wrote nothing: skip them
-  auto empty = [&](int k) { return share_start<WPG>(k, T) == share_start<WPG>(k + 1, T); };
-  const float* __restrict__ ml = a.ws_ml;
-  const float* __restrict__ accp = a.ws_acc;
-  if constexpr (WIDE) {
-    combine_wide<D, MODE>(a, b, g, rg, RG, k0, k1, T);
-    return;
-  }
-  // thread: one row, 16 consecutive head dims (D/16 threads per row)
-  constexpr int TPR = D / 16, RPP = 256 / TPR;
-  const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
-  auto slot_of = [&](int k) { return int64_t(k * 2 + (k == k0)) * (kPair ? 2 : 1) + (kPair ? rg : 0); };
-  for (int r0 = 0; r0 < RG; r0 += RPP) {
-    const int rl = r0 + tr;
-    if (rl >= RG) break;
-    const int64_t row = unit_row<MODE>(a, b, g, rg * RG + rl);
-    if (row < 0) continue;
-    float M = -INFINITY, den = 0.f;
-    f32x4 num[4] = {};
-    // shares in batches of 8: every load of a batch is issued before any merge
-    // (a unit of a long session can span dozens of shares)
-    constexpr int KB = 8;
-#pragma unroll 1
-    for (int kb = k0; kb <= k1; kb += KB) {
-      f32x2 mlv[KB];
-      f32x4 av[KB][4];
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int64_t slot = slot_of(min(kb + u, k1));
-        mlv[u] = *reinterpret_cast<const f32x2*>(ml + (slot * RG + rl) * 2);
-        const f32x4* ap = reinterpret_cast<const f32x4*>(accp + (slot * RG + rl) * D) + 4 * tc;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) av[u][i] = ap[i];
-      }
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        // past k1, a share without tiles (nothing written), or one that saw no key of this row
-        if (kb + u > k1 || empty(kb + u) || mlv[u][0] == -INFINITY) continue;
-        const float Mn = fmaxf(M, mlv[u][0]);
-        const float c = exp2_fast(M - Mn), w = exp2_fast(mlv[u][0] - Mn);  // exp2(-inf) = 0
-        den = den * c + w * mlv[u][1];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) num[i] = num[i] * c + w * av[u][i];
-        M = Mn;
-      }
-    }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    u32x2* o = reinterpret_cast<u32x2*>(a.out + row * D) + 4 * tc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x4(num[i][0] * inv, num[i][1] * inv, num[i][2] * inv, num[i][3] * inv);
   }
 }
 
@@ -995,30 +987,15 @@ __global__ __launch_bounds__(1024) void decode_cascade_plan_kernel(DecodeArgs a,
   if (mismatch) flag_error(a.dev_status, KVS_DEV_BAD_PAGE_BIT);
 }
 
-// One combine workgroup per (KV head, row group, session).  With at most 128
-// of them (fewer than the CUs), each unit spans 8 or more of the 1024 shares
-// on average, and the wide variant spreads a unit's shares over 1024 threads.
-template <int D, int MODE>
-hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
-  const int units = a.pool.num_kv_heads * a.plan.rowgroups * a.batch;
-  if (units <= 128)
-    hipLaunchKernelGGL((decode_combine_kernel<D, MODE, true>), dim3(units), dim3(kCombineWideThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_combine_kernel<D, MODE, false>), dim3(units), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
 template <int D, int NB, int MODE, bool APPEND = false>
 hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
   constexpr int S = D == 128 ? 4 : 8;  // 32 KiB of ring per wave
   hipLaunchKernelGGL((decode_stream_kernel<D, NB, S, MODE, APPEND>), dim3(kDecodeBlocks), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_combine<D, MODE>(a, stream);
+  return hipGetLastError();
 }
 
 // Cascade: the plan kernel forms the units, then 4 wave pairs per CU (two waves
-// per SIMD) stream them, then the combine kernel merges split units.
+// per SIMD) stream and merge them.
 template <int D>
 hipError_t launch_decode_cascade(const DecodeArgs& a, hipStream_t stream) {
   constexpr int S = D == 128 ? 4 : 8;  // 32 KiB of ring per pair
@@ -1028,9 +1005,7 @@ hipError_t launch_decode_cascade(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_pair_kernel<D, S>), dim3(1 << kDecodeShareLog2), dim3(128), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_combine<D, kCascade>(a, stream);
+  return hipGetLastError();
 }
 
 template <int D, int NB>
@@ -1040,7 +1015,20 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   return launch_decode_mode<D, NB, kPlain>(a, stream);
 }
 
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, int64_t words) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < words; i += int64_t(gridDim.x) * 256) p[i] = 0u;
+}
+
 }  // namespace
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
+  const int64_t words = int64_t(bytes / 4);
+  if (words == 0) return hipSuccess;
+  const int64_t blocks = (words + 255) / 256;
+  hipLaunchKernelGGL(zero_kernel, dim3(unsigned(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int D = a.pool.head_dim, nb = a.plan.nb;

@@ -36,7 +36,10 @@ constexpr int kDecodeMaxBatch = 4096;
 // groups of 16*nb (one wave holds them all); the (page, KV head, row group)
 // tiles of all sessions are shared out among the 4*blocks waves of a
 // persistent grid (evenly, up to a fixed weight per XCD).  Each wave has two
-// partial-state slots in the workspace.
+// partial-state slots in the workspace, and every unit split between waves
+// has an arrival counter there (zero between calls): counter k0 (or 2*k0 + row
+// group on wave pairs) for the unit that begins in share k0 and ends in a later
+// one, in the fixed kDecodeCounterBytes at the start of every workspace.
 struct DecodePlan {
   int rows;       // N * G query rows per KV head
   int nb;         // 16-row column blocks per wave (1, 2 or 4)
@@ -51,6 +54,8 @@ struct DecodePlan {
 constexpr int kDecodeBlocks = 256;
 constexpr int kDecodeShareLog2 = 10;
 static_assert(kDecodeBlocks * 4 == 1 << kDecodeShareLog2, "share count");
+// Arrival counters: one per share and row group of a wave pair (2 * 2^10 int32).
+constexpr size_t kDecodeCounterBytes = size_t(2) << kDecodeShareLog2 << 2;
 
 // Record a printf-style message for kvs_last_error() and return `status`.
 int set_error(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -84,8 +89,9 @@ struct DecodeArgs {
   // seq_lens[b] - 1 before it is attended
   const uint16_t* k_new;
   const uint16_t* v_new;
+  int* ws_cnt;    // [2 * 1024] arrival counters of split units; zero on entry and on exit
   int* ws_units;  // [3*batch+1] cascade units: first session, count, prefix pages; unit count
-  int* ws_cum;    // [batch+1] page prefix sum, written by the decode kernel
+  int* ws_cum;    // [batch+1] cascade unit tile prefix sum, written by the plan kernel
   float* ws_ml;   // [4*blocks*2][rg_rows][2] partial (m, l)
   float* ws_acc;  // [4*blocks*2][rg_rows][D] partial acc
   DecodePlan plan;
@@ -138,6 +144,9 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_pack(const HandoffArgs& a, bool unpack, hipStream_t stream);
 hipError_t launch_fetch(const FetchArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Zero `bytes` bytes (a multiple of 4) at `p` with a fill kernel (no memset node
+// in a captured graph).
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_extend(const ExtendArgs& a, hipStream_t stream);
 
 }  // namespace kvs

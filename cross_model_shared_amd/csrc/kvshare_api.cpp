@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <string>
 
@@ -59,6 +60,14 @@ kvs::PoolView view(const kvs_pool* p) {
                        p->head_dim};
 }
 
+// A softmax scale must be a positive, finite float.  Tested on the bit pattern,
+// so the check holds whatever floating-point assumptions the compiler makes.
+bool valid_scale(float scale) {
+  uint32_t bits;
+  memcpy(&bits, &scale, sizeof bits);
+  return (bits >> 31) == 0 && ((bits >> 23) & 0xFFu) != 0xFFu && (bits & 0x7FFFFFFFu) != 0;
+}
+
 int launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(KVS_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
   return KVS_OK;
@@ -86,12 +95,14 @@ DecodePlan plan_decode(int batch, int num_decoders, int num_q_heads, int num_kv_
   p.rg_rows = 16 * p.nb;
   p.rowgroups = (p.rows + p.rg_rows - 1) / p.rg_rows;
   p.blocks = kDecodeBlocks;
-  // partial-state slots sized for 64-row groups, so one workspace serves every
-  // decode call with these bounds (a cascade unit may hold up to 64 rows)
+  // arrival counters first, at a fixed size, so that every call on a workspace
+  // finds them in the same place; then the cascade tables and the partial-state
+  // slots, sized for 64-row groups, so one workspace serves every decode call
+  // with these bounds (a cascade unit may hold up to 64 rows)
   const size_t slots = size_t(p.blocks) * 4 * 2, slot_rows = 64;
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };
-  p.cum_offset = 0;
-  p.units_offset = align(size_t(batch + 1) * sizeof(int));
+  p.cum_offset = kDecodeCounterBytes;
+  p.units_offset = p.cum_offset + align(size_t(batch + 1) * sizeof(int));
   p.ml_offset = p.units_offset + align(size_t(3 * batch + 1) * sizeof(int));
   p.acc_offset = p.ml_offset + align(slots * slot_rows * 2 * sizeof(float));
   p.bytes = p.acc_offset + slots * slot_rows * head_dim * sizeof(float);
@@ -142,6 +153,14 @@ size_t shared_kv_decode_workspace_bytes(int32_t batch, int32_t num_decoders, int
   return kvs::plan_decode(batch, num_decoders, num_q_heads, num_kv_heads, head_dim, max_seq_len).bytes;
 }
 
+int shared_kv_decode_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace) return fail(KVS_EINVAL, "shared_kv_decode_workspace_init: workspace is NULL");
+  if (workspace_bytes < kvs::kDecodeCounterBytes)
+    return fail(KVS_EWORKSPACE, "shared_kv_decode_workspace_init: workspace %zu bytes < %zu", workspace_bytes,
+                kvs::kDecodeCounterBytes);
+  return launched(kvs::launch_zero(workspace, kvs::kDecodeCounterBytes, stream), "shared_kv_decode_workspace_init");
+}
+
 }  // extern "C"
 
 namespace {
@@ -163,7 +182,7 @@ int decode_common(const char* name, const kvs_pool* pool, int32_t layer, const v
   if (num_q_heads % pool->num_kv_heads)
     return fail(KVS_EUNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
                 pool->num_kv_heads);
-  if (!(scale > 0.f) || scale != scale) return fail(KVS_EINVAL, "%s: scale must be a positive number", name);
+  if (!valid_scale(scale)) return fail(KVS_EINVAL, "%s: scale must be a positive finite number", name);
   if (batch > kvs::kDecodeMaxBatch)
     return fail(KVS_EUNSUPPORTED, "%s: batch %d above %d", name, batch, kvs::kDecodeMaxBatch);
   kvs::DecodePlan plan = kvs::plan_decode(batch, num_decoders, num_q_heads, pool->num_kv_heads,
@@ -206,7 +225,8 @@ int decode_common(const char* name, const kvs_pool* pool, int32_t layer, const v
                     block_table, bt_stride, seq_lens, batch, num_decoders, num_q_heads, max_seq_len,
                     scale * 1.4426950408889634f, pbt, pbt_stride, plens, max_priv_len, group_id, group_prefix,
                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                    reinterpret_cast<int*>(ws + plan.units_offset), reinterpret_cast<int*>(ws + plan.cum_offset),
+                    reinterpret_cast<int*>(ws), reinterpret_cast<int*>(ws + plan.units_offset),
+                    reinterpret_cast<int*>(ws + plan.cum_offset),
                     reinterpret_cast<float*>(ws + plan.ml_offset),
                     reinterpret_cast<float*>(ws + plan.acc_offset), plan, dev_status};
   return launched(kvs::launch_decode(a, stream), name);
@@ -288,7 +308,7 @@ int extend_common(const char* name, const kvs_pool* pool, int32_t layer, int32_t
   if (num_q_heads % pool->num_kv_heads)
     return fail(KVS_EUNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
                 pool->num_kv_heads);
-  if (!(scale > 0.f) || scale != scale) return fail(KVS_EINVAL, "%s: scale must be a positive number", name);
+  if (!valid_scale(scale)) return fail(KVS_EINVAL, "%s: scale must be a positive finite number", name);
   const int64_t units = int64_t(num_layers) * batch * pool->num_kv_heads;
   if (units > (int64_t(1) << 30))
     return fail(KVS_EUNSUPPORTED, "%s: %lld (layer, session, KV head) units in one call", name, (long long)units);

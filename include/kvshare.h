@@ -15,6 +15,7 @@
  * Three operations:
  *   kv_pool_append         write new K/V rows into pages        (the cache "store")
  *   shared_kv_decode       N decoders x G GQA heads, one KV read (decode attention)
+ *   shared_kv_decode_workspace_init  zero the arrival counters of a new decode workspace
  *   shared_kv_decode_append  the same, writing the step's own token into the
  *                          pool in the same launch (append + decode fused)
  *   shared_kv_decode_private  the same over a shared prefix + per-decoder private suffixes
@@ -143,11 +144,26 @@ int kv_pool_append(const kvs_pool* pool, int32_t layer, const void* k_new, const
                    const int32_t* seq_lens, int32_t batch, int32_t total_new, int32_t max_new,
                    int32_t max_seq_len, int32_t* dev_status, hipStream_t stream);
 
-/* Workspace bytes needed by shared_kv_decode, shared_kv_decode_private and
- * shared_kv_decode_cascade for these bounds. */
+/* Workspace bytes needed by shared_kv_decode, shared_kv_decode_append,
+ * shared_kv_decode_private and shared_kv_decode_cascade for these bounds. */
 size_t shared_kv_decode_workspace_bytes(int32_t batch, int32_t num_decoders, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t max_seq_len);
+
+/*
+ * shared_kv_decode_workspace_init — make a decode workspace ready for its first
+ * call: zero its arrival counters (the first 8 KiB) with a fill kernel on
+ * `stream`.  A workspace whose first 8 KiB are already zero (e.g. allocated
+ * zero-filled) needs no init.
+ *
+ * A decode call splits work on one unit (session, KV head) between several
+ * waves; the last wave to finish a unit merges the others' partial states,
+ * found through a counter that every call leaves at zero again.  So a
+ * workspace needs this once, not per call, as long as only decode calls write
+ * it.  The rest of the workspace needs no init.
+ *  workspace        device buffer, >= 8 KiB (KVS_EWORKSPACE otherwise).
+ */
+int shared_kv_decode_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * shared_kv_decode — one decode step of N decoders over one shared cache.
@@ -168,10 +184,14 @@ size_t shared_kv_decode_workspace_bytes(int32_t batch, int32_t num_decoders, int
  *  max_seq_len   host bound on seq_lens[b]; sizes the launch.
  *  scale         softmax scale (1/sqrt(head_dim) for the usual attention).
  *  workspace     device buffer of >= shared_kv_decode_workspace_bytes(...)
- *                bytes.  Its contents on entry are ignored (every byte the call
- *                reads it wrote earlier in the same call), so a workspace may be
- *                reused by later calls on the same stream; calls that overlap in
- *                time must use different workspaces.
+ *                bytes.  Its first 8 KiB (arrival counters) must be zero when
+ *                the call starts: zero the buffer once, or call
+ *                shared_kv_decode_workspace_init once; every call leaves them
+ *                zero.  The rest of its contents on entry are ignored (every
+ *                other byte the call reads it wrote earlier in the same call), so
+ *                a workspace may be reused by later decode calls on the same
+ *                stream, whatever their shapes; calls that overlap in time must
+ *                use different workspaces.
  */
 int shared_kv_decode(const kvs_pool* pool, int32_t layer, const void* q, void* out,
                      const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,

@@ -50,11 +50,15 @@ def sync():
 
 
 def nan_workspace(nbytes):
-    """A decode workspace whose every float reads as NaN: the library must not
-    read a byte of it that the same call has not written."""
+    """A decode workspace whose every byte past the arrival counters is 0xFF (NaN as
+    floats): the library must not read a byte of it that the same call has not
+    written.  The counters are zeroed by shared_kv_decode_workspace_init, as the
+    header asks before a workspace's first call."""
     import torch
 
-    return torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    binding.decode_workspace_init(ws)
+    return ws
 
 
 def make_decode_case(lens, N, Hkv, G, D, seed, std=1.0, layers=1, layer=0, poison=POISON_BIG,

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(L):
             "shared_kv_decode_cascade",
             "partial_prefill_extend", "partial_prefill_layers",
             "kv_pages_pack", "kv_pages_unpack", "kv_pages_buffer_bytes", "kv_pool_fetch", "kvs_pool_bytes",
-            "shared_kv_decode_workspace_bytes", "kvs_last_error", "kvs_version",
+            "shared_kv_decode_workspace_bytes", "shared_kv_decode_workspace_init", "kvs_last_error", "kvs_version",
             "kvs_prefix_cache_create", "kvs_prefix_cache_admit", "kvs_prefix_cache_publish",
             "kvs_prefix_cache_release", "kvs_prefix_groups"} <= set(names)
     for n in names:
@@ -58,6 +58,21 @@ def test_workspace_bytes_depend_on_bounds_not_device(L):
     assert a >= 64 * 8 * 32 * (128 + 2) * 4
     assert L.shared_kv_decode_workspace_bytes(2, 2, 8, 3, 64, 100) == 0   # 8 % 3 != 0
     assert L.shared_kv_decode_workspace_bytes(0, 2, 8, 2, 64, 100) == 0
+
+
+def test_workspace_init_host_checks(L):
+    # rejected before anything is enqueued: no GPU call is made
+    assert L.shared_kv_decode_workspace_init(None, 1 << 20, None) == binding.KVS_EINVAL
+    assert binding.last_error()
+    assert L.shared_kv_decode_workspace_init(FAKE, 8191, None) == binding.KVS_EWORKSPACE
+    assert "8191" in binding.last_error()
+
+
+def test_workspace_counters_lead_every_layout(L):
+    # the arrival counters sit in the first 8 KiB whatever the bounds, so one workspace
+    # serves calls of any shape: every size holds at least that region
+    for args in [(1, 1, 1, 1, 64, 16), (64, 8, 32, 8, 128, 16384), (4096, 16, 64, 8, 128, 131072)]:
+        assert L.shared_kv_decode_workspace_bytes(*args) > 8192
 
 
 def pool(data=FAKE, layers=1, pages=8, heads=2, dim=64, page=16):
@@ -85,6 +100,10 @@ def call_decode(L, p, layer=0, q=FAKE, out=FAKE, bt=FAKE, stride=4, lens=FAKE, b
     (dict(p=pool(), Hq=7), binding.KVS_EUNSUPPORTED),
     (dict(p=pool(), msl=65), binding.KVS_ERANGE),          # > bt_stride * 16
     (dict(p=pool(), scale=0.0), binding.KVS_EINVAL),
+    (dict(p=pool(), scale=-0.125), binding.KVS_EINVAL),
+    (dict(p=pool(), scale=float("nan")), binding.KVS_EINVAL),
+    (dict(p=pool(), scale=float("inf")), binding.KVS_EINVAL),
+    (dict(p=pool(), scale=float("-inf")), binding.KVS_EINVAL),
     (dict(p=pool(), ws=None), binding.KVS_EWORKSPACE),
     (dict(p=pool(), wsb=16), binding.KVS_EWORKSPACE),
 ])
@@ -187,6 +206,8 @@ def call_extend(L, p, q=FAKE, k=FAKE, v=FAKE, out=FAKE, cu=FAKE, bt=FAKE, stride
     (dict(p=pool(), max_new=0), binding.KVS_EINVAL),
     (dict(p=pool(), msl=1000), binding.KVS_ERANGE),
     (dict(p=pool(), scale=float("nan")), binding.KVS_EINVAL),
+    (dict(p=pool(), scale=float("inf")), binding.KVS_EINVAL),
+    (dict(p=pool(), scale=-1.0), binding.KVS_EINVAL),
     (dict(p=pool(), batch=-3), binding.KVS_EINVAL),
 ])
 def test_extend_host_checks(L, kw, status):

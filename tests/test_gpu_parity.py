@@ -114,12 +114,13 @@ def test_decode_row_layouts_and_splits(D, N, G):
 
 
 @pytest.mark.parametrize("B,Hkv,N,G,D", [
-    (40, 4, 16, 6, 128),   # 320 units of 64-row groups (two per KV head): the 256-thread combine, row passes
-    (48, 2, 8, 4, 64),     # 96 units: the wide combine
-    (3, 2, 16, 6, 64),     # 12 units of 64 rows at D = 64: four share groups per unit
+    (40, 4, 16, 6, 128),   # 320 units of 64-row groups (two per KV head)
+    (48, 2, 8, 4, 64),     # 96 units
+    (3, 2, 16, 6, 64),     # 12 units of 64 rows at D = 64: dozens of shares per unit
 ])
-def test_decode_combine_paths(B, Hkv, N, G, D):
-    """Both combine variants (chosen by the unit count), each with units spanning several shares."""
+def test_decode_split_unit_merges(B, Hkv, N, G, D):
+    """Units split over several waves' shares, merged by the last wave to finish each:
+    many short units, and few long ones that span dozens of shares."""
     rng = np.random.default_rng(B * 7 + D)
     lens = [int(x) for x in rng.integers(1, 400, size=B)]
     lens[0], lens[-1] = 16, 399
@@ -130,6 +131,28 @@ def test_decode_combine_paths(B, Hkv, N, G, D):
     want = oracle.decode_from_logical(case["q"], case["K"], case["V"], 1.0 / math.sqrt(D))
     assert max_err(out, want) <= TOL
     assert int(case["status"].item()) == 0
+
+
+def test_decode_workspace_counters_back_to_zero_across_shapes():
+    """One workspace serves calls of different shapes in a row: every call finds its arrival
+    counters at zero and leaves them so (the first 8 KiB read back as zero), and each
+    result matches the oracle, with the rest of the workspace NaN-poisoned throughout."""
+    import torch
+
+    cases = [gu.make_decode_case([6000, 4100, 33], 16, 2, 6, 64, seed=71, poison=gu.POISON_NAN),
+             gu.make_decode_case([1000, 17, 3001, 16, 2500], 2, 2, 4, 64, seed=72, poison=gu.POISON_NAN)]
+    ws = gu.nan_workspace(max(binding.decode_workspace_bytes(len(c["lens"]), c["N"], c["Hkv"] * c["G"], c["Hkv"],
+                                                             c["D"], max(c["lens"])) for c in cases))
+    for c in cases + cases:
+        B, N, Hq, D = c["q"].shape
+        out = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device="cuda")
+        binding.decode(c["pool"], 0, gu.dev_bf16(c["q"]), out, gu.dev_i32(c["bt"]), gu.dev_i32(c["lens"]),
+                       max(c["lens"]), 1.0 / math.sqrt(D), ws, dev_status=c["status"])
+        gu.sync()
+        want = oracle.decode_from_logical(c["q"], c["K"], c["V"], 1.0 / math.sqrt(D))
+        assert max_err(out, want) <= TOL
+        assert not ws[:8192].cpu().numpy().any(), "arrival counters left non-zero"
+        assert int(c["status"].item()) == 0
 
 
 def test_decode_single_token_returns_v_exactly_and_empty_is_zero():
