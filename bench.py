@@ -67,8 +67,6 @@ def parse():
     ap.add_argument("--only", default=None,
                     help="run one section alone and print its JSON (counter runs): a name in "
                          "CONFIG_DECODE_WORKLOADS, or 'extend'")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=None,
                     help="decode layers per step (default: the workload's 36; fewer only for counter runs)")
@@ -659,28 +657,43 @@ def handoff_section(reps):
     return res
 
 
-def cpu_baseline(wl, q, target_s):
-    """Time the CPU oracle's decode on a bounded sample of sessions of layer 0 (q: its queries, host uint16)."""
-    import torch
-
-    import oracle
-    from cross_model_shared_amd import workload as W
-
+def cpu_host():
+    """Host cores this process may use, the BLAS threads NumPy runs, and the CPU model."""
     try:
         from threadpoolctl import threadpool_info
 
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas_threads = None
+    cpu_model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cores": len(os.sched_getaffinity(0)), "blas_threads": blas_threads, "cpu_model": cpu_model}
+
+
+def cpu_decode_baseline(wl, q, kv_key=(10, 11), layer=0):
+    """The CPU oracle's decode (gather through the pages + float64 softmax), untuned, on every
+    session of one layer of a decode workload: the layer's seeded K/V (the bench's own device
+    draws, copied to the host) appended into a per-session page image by the oracle (untimed),
+    then oracle.decode timed per session.  q: the layer's queries, host uint16 bits."""
+    import torch
+
+    import oracle
+    from cross_model_shared_amd import workload as W
+
     B, N, Hq, Hkv, D = wl.batch, wl.num_decoders, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     lens = wl.lens
-    order = sorted(range(B), key=lambda b: lens[b])[:: max(1, B // 32)]  # spread over the length mix
     cu = np.concatenate([[0], np.cumsum(lens)])
     total = int(cu[-1])
-    k = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 10, 0)).view(total, Hkv, D)
-    v = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, 11, 0)).view(total, Hkv, D)
-    spent, done_bytes, done = 0.0, 0, []
-    for b in order:
+    k = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, kv_key[0], layer)).view(total, Hkv, D)
+    v = W.device_normal_bf16(total * Hkv * D, wl.std, W.mix_seed(wl.seed, kv_key[1], layer)).view(total, Hkv, D)
+    spent, done_bytes = 0.0, 0
+    for b in range(B):
         L = lens[b]
         kb = k[cu[b]:cu[b + 1]].view(torch.int16).cpu().numpy().view(np.uint16)
         vb = v[cu[b]:cu[b + 1]].view(torch.int16).cpu().numpy().view(np.uint16)
@@ -692,22 +705,49 @@ def cpu_baseline(wl, q, target_s):
         oracle.decode(img, shape, 0, q[b:b + 1], bt, [L], wl.scale)
         spent += time.perf_counter() - t0
         done_bytes += decode_bytes([L], 1, N, Hq, Hkv, D)
-        done.append(L)
-        if spent >= target_s:
-            break
     del k, v
-    cpu_model = None
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu_model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
-            "blas_threads": blas_threads, "cpu_model": cpu_model, "kind": "oracle",
-            "sample": f"float64 oracle decode (gather + softmax) of {len(done)} of {B} sessions of layer 0 "
-                      f"(lengths {done}), all {N} decoders x {Hq} heads; {spent:.1f}s CPU time"}
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "kind": "oracle", "seconds": round(spent, 2),
+            "sample": f"{wl.name}: float64 oracle decode (gather + softmax) of all {B} sessions of one layer "
+                      f"({total} tokens), all {N} decoders x {Hq} heads; {spent:.1f}s CPU time", **cpu_host()}
+
+
+def cpu_extend_baseline(ew, sessions=1):
+    """The CPU oracle's partial prefill (append + float64 causal attention), untuned, on the
+    first `sessions` sessions of the extend workload (the bench's seeded device draws for
+    replica 0, copied to the host); TFLOP/s of the algorithmic flops of those sessions."""
+    import torch
+
+    import oracle
+    from cross_model_shared_amd import workload as W
+
+    Hq, Hkv, D = ew.num_q_heads, ew.num_kv_heads, ew.head_dim
+    P, T = sum(ew.prefix), sum(ew.new)
+    host = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    kp = host(W.device_normal_bf16(P * Hkv * D, ew.std, W.mix_seed(ew.seed, 20, 0)).view(P, Hkv, D))
+    vp = host(W.device_normal_bf16(P * Hkv * D, ew.std, W.mix_seed(ew.seed, 21, 0)).view(P, Hkv, D))
+    q = host(W.device_normal_bf16(T * Hq * D, ew.std, W.mix_seed(ew.seed, 22, 0)).view(T, Hq, D))
+    kn = host(W.device_normal_bf16(T * Hkv * D, ew.std, W.mix_seed(ew.seed, 23, 0)).view(T, Hkv, D))
+    vn = host(W.device_normal_bf16(T * Hkv * D, ew.std, W.mix_seed(ew.seed, 24, 0)).view(T, Hkv, D))
+    cup = np.concatenate([[0], np.cumsum(ew.prefix)])
+    cun = np.concatenate([[0], np.cumsum(ew.new)])
+    spent, flops = 0.0, 0
+    for b in range(sessions):
+        Pb, Cb = ew.prefix[b], ew.new[b]
+        npg = (Pb + Cb + 15) // 16
+        shape = oracle.PoolShape(1, npg, Hkv, D)
+        bt = np.arange(npg, dtype=np.int32)[None]
+        img = oracle.append(np.zeros(shape.elems, np.uint16), shape, 0, kp[cup[b]:cup[b + 1]], vp[cup[b]:cup[b + 1]],
+                            [0, Pb], bt, [0])
+        t0 = time.perf_counter()
+        oracle.extend(img, shape, 0, q[cun[b]:cun[b + 1]], kn[cun[b]:cun[b + 1]], vn[cun[b]:cun[b + 1]], [0, Cb], bt,
+                      [Pb], ew.scale)
+        spent += time.perf_counter() - t0
+        flops += extend_flops([Pb], [Cb], Hq, D)
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle", "seconds": round(spent, 2),
+            "sample": f"{ew.name}: float64 oracle partial prefill (append + causal attention) of {sessions} of "
+                      f"{ew.batch} sessions ({ew.prefix[0]} cached + {ew.new[0]} new tokens, {Hq} heads); the "
+                      f"whole batch would take about {ew.batch // sessions}x as long (extrapolated, not run); "
+                      f"{spent:.1f}s CPU time", **cpu_host()}
 
 
 def main():
@@ -821,10 +861,24 @@ def main():
     cascade = None if args.no_cascade else cascade_section(20)
     layer_group = None if args.no_layer_group else layer_group_section(args.layer_group_calls)
 
-    cpu = None
+    cpu, cpus = None, None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, q0_host, args.cpu_seconds)
-        log(f"[bench] cpu baseline {cpu['value']} GB/s")
+        cpu = cpu_decode_baseline(wl, q0_host)
+        cpu["sample"] += f"; the {layers}-layer step would take {layers}x as long (extrapolated, not run)"
+        log(f"[bench] cpu baseline {wl.name} {cpu['value']} GB/s ({cpu['seconds']}s)")
+        cpus = {}
+        if not args.no_decode_configs:
+            for name in CONFIG_DECODE_WORKLOADS:
+                cw_ = W.make_workload(name)
+                qc = W.device_normal_bf16(cw_.batch * cw_.num_decoders * cw_.num_q_heads * cw_.head_dim, cw_.std,
+                                          W.mix_seed(cw_.seed, 12, 0))
+                qc = qc.view(torch.int16).cpu().numpy().view(np.uint16).reshape(
+                    cw_.batch, cw_.num_decoders, cw_.num_q_heads, cw_.head_dim)
+                cpus[name] = cpu_decode_baseline(cw_, qc)
+                log(f"[bench] cpu baseline {name} {cpus[name]['value']} GB/s ({cpus[name]['seconds']}s)")
+        cpus[EXTEND_WORKLOAD] = cpu_extend_baseline(ew, 1)
+        log(f"[bench] cpu baseline {EXTEND_WORKLOAD} {cpus[EXTEND_WORKLOAD]['value']} TFLOP/s "
+            f"({cpus[EXTEND_WORKLOAD]['seconds']}s)")
 
     res = {
         "metric": "shared-KV decode attn KV GB/s (% HBM peak) at N=8 decoders; extend TFLOP/s",
@@ -855,6 +909,7 @@ def main():
             "launches": len(timer.all_ms()),
         },
         "cpu_baseline": cpu,
+        "cpu_baselines_other": cpus,
         "decoder_concat": {"time_N8_over_N1": round(nN_ms / n1_ms, 3), "ms_N8": round(nN_ms, 4),
                            "ms_N1": round(n1_ms, 4)},
         "footprint": {"pool_GB": round(pool_gb, 2), "n_private_copies_GB": round(pool_gb * N, 2),

@@ -53,6 +53,40 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Wait for every outstanding memory access of this wave.  The wait builtin is
+// not a memory access for the compiler, which may move loads and stores across
+// it; the compiler fences on both sides keep them on their side.
+__device__ __forceinline__ void drain() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Direct global -> LDS copy of one 1 KiB slab: 16 bytes per lane, lane l's
+// bytes from `src` + 16 l to LDS byte address `lds` + 16 l (gfx950's
+// global_load_lds_dwordx4; M0 holds the LDS address, and the M0 write needs one
+// wait state before the load reads it).  Written in assembly so that the
+// compiler does not track it: the ring's own waits (wait_ring) order these
+// copies against the LDS reads, and a compiler that tracked them would also
+// wait for the most recent copy before a page's LDS reads whenever it could not
+// tell the ring slots apart.  The copy still counts in vmcnt, so every wait the
+// compiler computes for its own loads only gets stricter.  M0 is set here, right
+// before its one use; no other instruction of these kernels reads M0 (checked
+// in their gfx950 assembly), so clobbering it is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_slab(uint32_t lds, const void* src, int lane) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(lane * 16), "s"(src)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return uint32_t(size_t((__attribute__((address_space(3))) T*)p));
+}
+
 // Wait until at most `pages_after` pages' worth of ring loads are outstanding.
 template <int SLABS, int S>
 __device__ __forceinline__ void wait_ring(int pages_after) {
@@ -244,12 +278,20 @@ __device__ __forceinline__ int64_t unit_row(const DecodeArgs& a, int b, int g, i
 
 // Stream-K share boundaries: 2^10 shares, WPG consecutive shares per
 // workgroup (4 waves in the stream kernel, one wave pair in the cascade), and
-// the hardware places workgroup i on XCD i % 8.  Per-wave timestamps on MI355X
-// show the odd XCDs streaming KV pages about 10% slower than the even ones, so
-// a share on an even XCD weighs 276 and one on an odd XCD 236 (all 1024 weigh
-// 2^18): the waves then finish closer together (calls 2% faster, measured).
-// The weights only move boundaries; any split is correct.
-constexpr int64_t kShareEven = 276, kShareOdd = 236;
+// the hardware places workgroup i on XCD i % 8.  A share on an even XCD weighs
+// kShareEven, one on an odd XCD kShareOdd (all 1024 weigh 2^18).  Per-wave
+// timestamps show the odd XCDs streaming KV pages slower than the even ones, by
+// 4% to 13% depending on the GPU and the workload; 276 / 236 was the fastest
+// split measured on the 8-decoder workload (2% faster than equal shares, calls
+// alternating in one process).  The weights only move boundaries; any split is
+// correct, and a build may set another one.
+#ifndef KVS_RING_PAGES_D128  // LDS ring depth per wave at D = 128 (8 KiB pages)
+#define KVS_RING_PAGES_D128 4
+#endif
+#ifndef KVS_SHARE_EVEN
+#define KVS_SHARE_EVEN 276
+#endif
+constexpr int64_t kShareEven = KVS_SHARE_EVEN, kShareOdd = 512 - KVS_SHARE_EVEN;
 constexpr int kShareTotalLog2 = 18;
 static_assert(512 * (kShareEven + kShareOdd) == int64_t(1) << kShareTotalLog2 && kDecodeShareLog2 == 10,
               "share weights");
@@ -378,78 +420,150 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, const RowStat
   }
 }
 
+// Tiles of the unit [s_u, e_u) that shares p .. q hold.
+template <int WPG>
+__device__ __forceinline__ int range_tiles(int p, int q, int64_t s_u, int64_t e_u, int64_t T) {
+  const int64_t lo = max(s_u, share_start<WPG>(p, T)), hi = min(e_u, share_start<WPG>(q + 1, T));
+  return hi > lo ? int(hi - lo) : 0;
+}
+
+// Merge tree over the shares of a split unit: a node at level lv joins up to
+// 2^kMergeFanLog2 children (shares at level 1, level-(lv-1) nodes above), so a
+// unit spanning dozens of shares is merged by several waves, a level at a time,
+// instead of all by one.
+constexpr int kMergeFanLog2 = 3;
+constexpr int kMergeLevels = 4;  // 8^4 >= 2^10 shares
+// arrival counters per level: (2 * share + x) * 2 + row group < 2^12
+constexpr int kCountersPerLevel = 4 << kDecodeShareLog2;
+static_assert(kMergeLevels * kCountersPerLevel * 4 <= int(kDecodeCounterBytes), "counter region");
+
 // The end of a wave's part of a unit that other shares also hold.  The wave
-// has stored its partial state (m, l, acc) with write_partial; it waits for
-// those stores, then adds its tile count to the unit's arrival counter with a
-// vector atomic; the wave whose addition completes the unit's npg tiles merges
-// the states of all the unit's shares k0..k1, in share order:
-//   m* = max m_s,  out = sum_s 2^(m_s - m*) acc_s / sum_s 2^(m_s - m*) l_s.
-// The order is fixed, so the result does not depend on which wave arrives
-// last.  The merging wave puts the counter back to zero, so every counter is
-// zero again when the call ends.  A share begins at most one unit that it does
-// not finish, so a split unit's counter is indexed by its first share k0:
-// counter k0*mul + add, and share k's partial slot (2k + x)*mul + add, x = 0
-// for the unit a share continues, 1 for the one it begins (mul = 1, add = 0 on
-// the stream kernel; mul = 2, add = the row group on wave pairs).
+// has stored its partial state (m, l, acc) with write_partial.  It then climbs
+// the unit's merge tree: at each node it waits for its stores, adds its
+// subtree's tile count to the node's arrival counter with a vector atomic, and
+// stops unless its addition completes the node's tiles; the wave that completes
+// a node merges the node's children in share order,
+//   m* = max m_c,  acc* = sum_c 2^(m_c - m*) acc_c,  l* = sum_c 2^(m_c - m*) l_c,
+// and writes the result into the slot of the node's first share with tiles
+// (or, at the root, writes out = acc* / l*).  The tree and the order are fixed,
+// so the result does not depend on which waves arrive last.  Each node's last
+// arriver puts the counter back to zero, so every counter is zero again when
+// the call ends.  A share begins at most one unit that it does not finish, and
+// continues at most one, so the node starting at share g of a unit that begins
+// in share k0 uses counter (2g + (g == k0))*mul + add of its level, and share
+// f's state sits in partial slot (2f + (f == k0))*mul + add (mul = 1, add = 0
+// on the stream kernel; mul = 2, add = the row group on wave pairs).
 template <int D, int NB, int MODE, int WPG, int KB>
 __device__ __forceinline__ void finish_split(const DecodeArgs& a, int k, bool before, int mul, int add, int mine,
                                              int npg, int64_t s_u, int64_t T, int b, int g, int rg, int lane) {
+  const int64_t e_u = s_u + npg;
   const int k0 = before ? share_of<WPG>(s_u, T) : k;
-  int* ctr = a.ws_cnt + k0 * mul + add;
-  // the partial state has reached device scope before the arrival does
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  int old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(ctr, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  old = __builtin_amdgcn_readlane(old, 0);
-  if (old + mine != npg) return;
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  const int k1 = share_of<WPG>(s_u + npg - 1, T);
+  const int k1 = share_of<WPG>(e_u - 1, T);
+  auto slot_of = [&](int f) { return int64_t(2 * f + (f == k0 ? 1 : 0)) * mul + add; };
+  // Every share holds at least one tile when T * (the smallest share weight) >= 2^18:
+  // then the unit's shares k0 .. k1 all hold tiles of it, and a range of them
+  // starts with a share holding tiles.  Otherwise, search.
+  const bool dense = T * min(kShareEven, kShareOdd) >= (int64_t(1) << kShareTotalLog2);
+  // the first share of p .. q that holds tiles of the unit (the range has some)
+  auto first_with_tiles = [&](int p) {
+    return dense ? max(p, k0) : share_of<WPG>(max(s_u, share_start<WPG>(p, T)), T);
+  };
   const __amdgpu_buffer_rsrc_t racc = acc_rsrc<D>(a), rml = ml_rsrc(a);
-  // one 16-row column block at a time (fewer live registers); shares in
-  // batches of KB, every load of a batch issued before any merge
+  int child = k, tiles = mine;
+  // the wave's partial state has reached device scope before it arrives anywhere
+  drain();
 #pragma unroll 1
-  for (int cb = 0; cb < NB; ++cb) {
-    float M = -INFINITY, den = 0.f;
-    f32x4 acc[D / 16];
+  for (int lv = 1; lv <= kMergeLevels; ++lv) {
+    const int span = 1 << (kMergeFanLog2 * lv), cspan = span >> kMergeFanLog2;
+    const int g0 = k0 + ((child - k0) >> (kMergeFanLog2 * lv) << (kMergeFanLog2 * lv));
+    const int g1 = min(g0 + span - 1, k1);
+    const int expect = range_tiles<WPG>(g0, g1, s_u, e_u, T);
+    if (expect == tiles) {  // the arriving subtree is the node's only child with tiles
+      child = g0;
+      continue;
+    }
+    int* ctr = a.ws_cnt + (lv - 1) * kCountersPerLevel + (2 * g0 + (g0 == k0 ? 1 : 0)) * mul + add;
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(ctr, tiles, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readlane(old, 0);
+    if (old + tiles != expect) return;
+    if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // every arrival is in
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const bool root = g1 == k1 && g0 == k0;
+    const int64_t dst = root ? 0 : slot_of(first_with_tiles(g0));
+    // the node's children: the slot holding each child's state, or -1 for a
+    // child without tiles of the unit (a level-1 child is a share, which holds
+    // its own state; a higher child's state sits in its first share with tiles)
+    int64_t cslot[1 << kMergeFanLog2];
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < (1 << kMergeFanLog2); ++c) {
+      const int p = g0 + c * cspan, q = min(p + cspan - 1, g1);
+      const bool has = p <= g1 && (dense || range_tiles<WPG>(p, q, s_u, e_u, T) > 0);
+      cslot[c] = !has ? -1 : slot_of(lv == 1 ? p : first_with_tiles(p));
+    }
+    // one 16-row column block at a time (fewer live registers); children in
+    // batches of KB, every load of a batch issued before any merge
 #pragma unroll 1
-    for (int kb = k0; kb <= k1; kb += KB) {
-      f32x2 mlv[KB];
-      f32x4 av[KB][D / 16];
+    for (int cb = 0; cb < NB; ++cb) {
+      float M = -INFINITY, den = 0.f;
+      f32x4 acc[D / 16];
 #pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int kk = min(kb + u, k1);
-        const int64_t slot = int64_t(kk * 2 + (kk == k0 ? 1 : 0)) * mul + add;
-        const u32x2 mlb = __builtin_amdgcn_raw_buffer_load_b64(rml, ml_off<NB>(slot, cb * 16 + (lane & 15)), 0,
-                                                               kDeviceScope);
-        mlv[u] = f32x2{__uint_as_float(mlb[0]), __uint_as_float(mlb[1])};
+      for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c0 = 0; c0 < (1 << kMergeFanLog2); c0 += KB) {
+        bool any = false;  // (a child of only empty shares can sit between children with tiles)
+#pragma unroll
+        for (int u = 0; u < KB; ++u) any |= cslot[c0 + u] >= 0;
+        if (!any) continue;
+        f32x2 mlv[KB];
+        f32x4 av[KB][D / 16];
+        bool use[KB];
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+          const int64_t slot = cslot[c0 + u];
+          use[u] = slot >= 0;
+          mlv[u] = f32x2{-INFINITY, 0.f};
+          if (!use[u]) continue;
+          const u32x2 mlb = __builtin_amdgcn_raw_buffer_load_b64(rml, ml_off<NB>(slot, cb * 16 + (lane & 15)), 0,
+                                                                 kDeviceScope);
+          mlv[u] = f32x2{__uint_as_float(mlb[0]), __uint_as_float(mlb[1])};
+#pragma unroll
+          for (int i = 0; i < D / 16; ++i)
+            av[u][i] = __builtin_amdgcn_raw_buffer_load_b128(racc, lane * 16, acc_soff<D, NB>(slot, cb, i),
+                                                             kDeviceScope);
+        }
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+          if (!use[u] || mlv[u][0] == -INFINITY) continue;  // no child, or a child that saw no key of this row
+          const float Mn = fmaxf(M, mlv[u][0]);
+          const float c = exp2_fast(M - Mn), w = exp2_fast(mlv[u][0] - Mn);  // exp2(-inf) = 0
+          den = den * c + w * mlv[u][1];
+#pragma unroll
+          for (int i = 0; i < D / 16; ++i) acc[i] = acc[i] * c + w * av[u][i];
+          M = Mn;
+        }
+      }
+      if (root) {
+        store_block<D, NB, MODE>(a, acc, den, cb, b, g, rg, lane);
+      } else {
 #pragma unroll
         for (int i = 0; i < D / 16; ++i)
-          av[u][i] = __builtin_amdgcn_raw_buffer_load_b128(racc, lane * 16, acc_soff<D, NB>(slot, cb, i), kDeviceScope);
-      }
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int kk = kb + u;
-        // past k1, a share without tiles (it wrote nothing), or one that saw no key of this row
-        if (kk > k1 || share_start<WPG>(kk, T) == share_start<WPG>(kk + 1, T) || mlv[u][0] == -INFINITY) continue;
-        const float Mn = fmaxf(M, mlv[u][0]);
-        const float c = exp2_fast(M - Mn), w = exp2_fast(mlv[u][0] - Mn);  // exp2(-inf) = 0
-        den = den * c + w * mlv[u][1];
-#pragma unroll
-        for (int i = 0; i < D / 16; ++i) acc[i] = acc[i] * c + w * av[u][i];
-        M = Mn;
+          __builtin_amdgcn_raw_buffer_store_b128(acc[i], racc, lane * 16, acc_soff<D, NB>(dst, cb, i), kDeviceScope);
+        if (lane < 16) {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(M), rml, ml_off<NB>(dst, cb * 16 + lane), 0,
+                                                kDeviceScope);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(den), rml, ml_off<NB>(dst, cb * 16 + lane) + 4, 0,
+                                                kDeviceScope);
+        }
       }
     }
-    store_block<D, NB, MODE>(a, acc, den, cb, b, g, rg, lane);
+    if (root) break;
+    // the merged state has reached device scope before the next arrival
+    drain();
+    child = g0;
+    tiles = expect;
   }
-  if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // Loads of a batch's padding (shares past k1) are never consumed: wait for
-  // them here, or the compiler waits for every outstanding load before the
-  // ring's next LDS read, on every page, to protect their registers.
-  __builtin_amdgcn_s_waitcnt(0);
+  drain();
 }
 
 // Zeros for the rows of units without tiles (softmax over nothing): units
@@ -582,11 +696,9 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       pid = 0;  // stream a harmless in-range page, skip it at compute time
     }
     const u32x4* tile = reinterpret_cast<const u32x4*>(a.pool.data + tile_offset(a.layer, pid, g, num_pages, Hkv, D));
+    const uint32_t dst = lds_addr(&ring[wave][slot][0]);
 #pragma unroll
-    for (int s = 0; s < SLABS; ++s)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + s * 64 + lane),
-                                       (__attribute__((address_space(3))) void*)(&ring[wave][slot][s * 64]),
-                                       16, 0, 0);
+    for (int s = 0; s < SLABS; ++s) dma_slab(dst + s * 1024, tile + s * 64, lane);
     advance<MODE>(a, iw, cum, B);
   };
 
@@ -614,9 +726,9 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
     }
   };
 
-  // Queries (and the step's token) are waited for before the ring (re)starts:
-  // a q load still in flight at the loop head would make the compiler wait for
-  // every outstanding load before each page's first matrix step.
+  // Queries (and the step's token) are waited for before the ring starts: any
+  // non-DMA load still outstanding when the first page's DMA is issued makes
+  // the compiler wait for every outstanding load before each page's LDS reads.
   QFrag<D, NB> qf;
   RowState<D, NB> st;
   st.init();
@@ -679,18 +791,23 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       const bool before = unit_begin < tau0, after = unit_end > tau1;
       if (!before && !after) {
         write_rows<D, NB, MODE>(a, st, cur_b, cur_gr / RGs, cur_gr % RGs, lane);
-      } else {
+      } else {  // split: the share's first unit (continued) or its last one (begun)
         write_partial<D, NB>(a, st, k * 2 + (before ? 0 : 1), lane);
-        finish_split<D, NB, MODE, kWaves, (NB >= 4 ? 1 : 4 / NB)>(a, k, before, 1, 0, int(min(unit_end, tau1) - max(unit_begin, tau0)),
-                                             npg_u, unit_begin, T, cur_b, cur_gr / RGs, cur_gr % RGs, lane);
+        finish_split<D, NB, MODE, kWaves, (NB >= 4 ? 1 : 4 / NB)>(
+            a, k, before, 1, 0, int(min(unit_end, tau1) - max(unit_begin, tau0)), npg_u, unit_begin, T, cur_b,
+            cur_gr / RGs, cur_gr % RGs, lane);
       }
       if (!last) {
         st.init();
         load_q<D, NB, MODE>(qf, a, cw.b, cw.gr / RGs, cw.gr % RGs, lane);
         load_new(cw.b, cw.gr / RGs);
-        __builtin_amdgcn_s_waitcnt(0);  // stores and q loads drained before the ring resumes
         unit_begin = int64_t(cw.gr) * Ptot + cum_s[cw.b];
       }
+      // Stores (their data registers), merge loads and q loads drained before
+      // the ring resumes: whatever the compiler cannot prove complete at the
+      // loop head makes it wait for every outstanding load before each page's
+      // LDS reads.
+      drain();
     }
   }
 }
@@ -748,11 +865,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
       pid = 0;  // stream a harmless in-range page, skip it at compute time
     }
     const u32x4* tile = reinterpret_cast<const u32x4*>(a.pool.data + tile_offset(a.layer, pid, iw.gr, num_pages, Hkv, D));
+    const uint32_t dst = lds_addr(&ring[slot][0]);
 #pragma unroll
     for (int h = 0; h < HALF; ++h) {
       const int s = rg * HALF + h;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + s * 64 + lane),
-                                       (__attribute__((address_space(3))) void*)(&ring[slot][s * 64]), 16, 0, 0);
+      dma_slab(dst + s * 1024, tile + s * 64, lane);
     }
     advance<MODE>(a, iw, cum, B);
   };
@@ -819,9 +936,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
       if (!last) {
         st.init();
         load_q<D, NB, MODE>(qf, a, cw.b, cw.gr, rg, lane);
-        __builtin_amdgcn_s_waitcnt(0);  // stores and q loads drained before the ring resumes
         unit_begin = int64_t(cw.gr) * Ptot + cum(cw.b);
       }
+      drain();  // stores and q loads drained before the ring resumes (see the stream kernel)
     }
   }
 }
@@ -989,7 +1106,7 @@ __global__ __launch_bounds__(1024) void decode_cascade_plan_kernel(DecodeArgs a,
 
 template <int D, int NB, int MODE, bool APPEND = false>
 hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int S = D == 128 ? 4 : 8;  // 32 KiB of ring per wave
+  constexpr int S = D == 128 ? KVS_RING_PAGES_D128 : 8;  // 32 KiB of ring per wave
   hipLaunchKernelGGL((decode_stream_kernel<D, NB, S, MODE, APPEND>), dim3(kDecodeBlocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -37,9 +37,8 @@ constexpr int kDecodeMaxBatch = 4096;
 // tiles of all sessions are shared out among the 4*blocks waves of a
 // persistent grid (evenly, up to a fixed weight per XCD).  Each wave has two
 // partial-state slots in the workspace, and every unit split between waves
-// has an arrival counter there (zero between calls): counter k0 (or 2*k0 + row
-// group on wave pairs) for the unit that begins in share k0 and ends in a later
-// one, in the fixed kDecodeCounterBytes at the start of every workspace.
+// has arrival counters there (zero between calls), in the fixed
+// kDecodeCounterBytes at the start of every workspace.
 struct DecodePlan {
   int rows;       // N * G query rows per KV head
   int nb;         // 16-row column blocks per wave (1, 2 or 4)
@@ -54,8 +53,27 @@ struct DecodePlan {
 constexpr int kDecodeBlocks = 256;
 constexpr int kDecodeShareLog2 = 10;
 static_assert(kDecodeBlocks * 4 == 1 << kDecodeShareLog2, "share count");
-// Arrival counters: one per share and row group of a wave pair (2 * 2^10 int32).
-constexpr size_t kDecodeCounterBytes = size_t(2) << kDecodeShareLog2 << 2;
+// Arrival counters of the split units' merge trees: per tree level (4), two
+// per share and row group of a wave pair (a unit a share begins, one it
+// continues): 4 * 2^12 int32 = 64 KiB.
+constexpr size_t kDecodeCounterBytes = size_t(4) * (size_t(4) << kDecodeShareLog2) * 4;
+
+// Decode workspace layout: arrival counters, then the cascade unit prefix sum
+// [batch+1] and unit tables [3*batch+1], then the partial-state slots (2 per
+// wave, sized for 64-row groups): (m, l) per row, then a D-vector per row.
+constexpr size_t decode_align(size_t x) { return (x + 255) / 256 * 256; }
+constexpr size_t kDecodeSlots = size_t(kDecodeBlocks) * 4 * 2, kDecodeSlotRows = 64;
+constexpr size_t decode_cum_offset() { return kDecodeCounterBytes; }
+constexpr size_t decode_units_offset(int batch) { return decode_cum_offset() + decode_align(size_t(batch + 1) * 4); }
+constexpr size_t decode_ml_offset(int batch) { return decode_units_offset(batch) + decode_align(size_t(3 * batch + 1) * 4); }
+constexpr size_t decode_acc_offset(int batch) {
+  return decode_ml_offset(batch) + decode_align(kDecodeSlots * kDecodeSlotRows * 2 * 4);
+}
+constexpr size_t decode_workspace_size(int batch, int head_dim) {
+  return decode_acc_offset(batch) + kDecodeSlots * kDecodeSlotRows * size_t(head_dim) * 4;
+}
+// The largest workspace any decode call needs (batch <= kDecodeMaxBatch, head_dim <= 128).
+constexpr size_t kDecodeWorkspaceMaxBytes = decode_workspace_size(kDecodeMaxBatch, 128);
 
 // Record a printf-style message for kvs_last_error() and return `status`.
 int set_error(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -89,7 +107,7 @@ struct DecodeArgs {
   // seq_lens[b] - 1 before it is attended
   const uint16_t* k_new;
   const uint16_t* v_new;
-  int* ws_cnt;    // [2 * 1024] arrival counters of split units; zero on entry and on exit
+  int* ws_cnt;    // arrival counters of split units' merge trees; zero on entry and on exit
   int* ws_units;  // [3*batch+1] cascade units: first session, count, prefix pages; unit count
   int* ws_cum;    // [batch+1] cascade unit tile prefix sum, written by the plan kernel
   float* ws_ml;   // [4*blocks*2][rg_rows][2] partial (m, l)

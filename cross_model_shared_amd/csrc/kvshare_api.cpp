@@ -99,13 +99,11 @@ DecodePlan plan_decode(int batch, int num_decoders, int num_q_heads, int num_kv_
   // finds them in the same place; then the cascade tables and the partial-state
   // slots, sized for 64-row groups, so one workspace serves every decode call
   // with these bounds (a cascade unit may hold up to 64 rows)
-  const size_t slots = size_t(p.blocks) * 4 * 2, slot_rows = 64;
-  auto align = [](size_t x) { return (x + 255) / 256 * 256; };
-  p.cum_offset = kDecodeCounterBytes;
-  p.units_offset = p.cum_offset + align(size_t(batch + 1) * sizeof(int));
-  p.ml_offset = p.units_offset + align(size_t(3 * batch + 1) * sizeof(int));
-  p.acc_offset = p.ml_offset + align(slots * slot_rows * 2 * sizeof(float));
-  p.bytes = p.acc_offset + slots * slot_rows * head_dim * sizeof(float);
+  p.cum_offset = decode_cum_offset();
+  p.units_offset = decode_units_offset(batch);
+  p.ml_offset = decode_ml_offset(batch);
+  p.acc_offset = decode_acc_offset(batch);
+  p.bytes = decode_workspace_size(batch, head_dim);
   return p;
 }
 

@@ -140,3 +140,17 @@ def run_decode_private(case, q_bits=None, priv=None, pbt=None, max_priv_len=None
                            dev_i32(pbt), dev_i32(priv), msl, mpl, scale, ws, dev_status=case["status"])
     sync()
     return out
+
+
+# Full-size parity: besides the absolute 2e-2, every sampled session's outputs
+# must satisfy max|gpu - oracle| <= FULLSIZE_REL * max|oracle| (per session).
+# tests/test_fullsize_bound.py shows on the CPU, with the oracle, that one
+# dropped or duplicated 16-token page of an 8K-token context breaks this bound,
+# while an emulation of the kernels' bf16 roundings (weights and outputs) stays
+# well inside it.
+FULLSIZE_REL = 1.0 / 64
+
+
+def session_rel_err(got, want):
+    """max|got - want| / max|want| over one session's outputs (float64 arrays)."""
+    return float(np.max(np.abs(got - want))) / max(float(np.max(np.abs(want))), 1e-30)

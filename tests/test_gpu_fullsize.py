@@ -4,9 +4,12 @@ The GPU path appends device-drawn K/V (torch's seeded generator, the input
 generator for large sizes) into a poisoned pool with kv_pool_append, then runs
 shared_kv_decode / partial_prefill_extend.  The oracle checks a seeded sample of
 sessions (decode: every decoder and head of each sampled session) or rows
-(extend: first, last and boundary rows of sampled sessions) from the same
-logical K/V copied to the host, and compares the sampled sessions' page tiles
-bit for bit against its own append of those K/V.
+(extend: 8 sessions, the ends, middle and two seeded rows of every 128-row
+block) from the same logical K/V copied to the host, and compares the sampled
+sessions' page tiles bit for bit against its own append of those K/V.  Besides
+the absolute tolerance, each sampled session must satisfy the output-scaled
+bound gu.FULLSIZE_REL, which one dropped or doubled page of an 8K-token context
+breaks (tests/test_fullsize_bound.py shows this on the CPU).
 """
 import math
 
@@ -102,8 +105,10 @@ def test_decode_full_size_sampled(name, layers, layer):
         Vs[b] = host_rows(v[cu[b]:cu[b + 1]])
     want = oracle.decode_from_logical(qh, Ks, Vs, wl.scale)
     err = max(float(np.max(np.abs(got[b] - want[b]))) for b in picks)
-    print(f"[fullsize] {name}: sessions {picks} max-abs err {err:.3e}", flush=True)
+    rel = max(gu.session_rel_err(got[b], want[b]) for b in picks)
+    print(f"[fullsize] {name}: sessions {picks} max-abs err {err:.3e}, session-relative {rel:.4f}", flush=True)
     assert err <= TOL
+    assert rel <= gu.FULLSIZE_REL
     for b in sorted(picks, key=lambda b: lens[b])[:2]:   # the two shortest sampled sessions
         check_tiles(pool, bt, layer, b, Ks[b], Vs[b], Hkv, D)
 
@@ -150,8 +155,11 @@ def test_decode_append_full_size_sampled():
         Vs[b] = host_rows(v[cu[b]:cu[b + 1]])
     want = oracle.decode_from_logical(qh, Ks, Vs, wl.scale)
     err = max(float(np.max(np.abs(got[b] - want[b]))) for b in picks)
-    print(f"[fullsize] decode_append: sessions {picks} max-abs err {err:.3e}", flush=True)
+    rel = max(gu.session_rel_err(got[b], want[b]) for b in picks)
+    print(f"[fullsize] decode_append: sessions {picks} max-abs err {err:.3e}, session-relative {rel:.4f}",
+          flush=True)
     assert err <= TOL
+    assert rel <= gu.FULLSIZE_REL
     for b in sorted(picks, key=lambda b: lens[b])[:2]:   # every page, the new token's included
         check_tiles(pool, bt, layer, b, Ks[b], Vs[b], Hkv, D)
 
@@ -184,16 +192,28 @@ def test_extend_full_size_sampled():
     assert int(st.item()) == 0
     got = gu.host_f64(out)
     assert np.all(np.isfinite(got))
-    picks = sample_sessions(full, 3, wl.seed)
+    picks = sample_sessions(full, 8, wl.seed)
+    rng = np.random.default_rng(wl.seed)
     for b in picks:
         C = wl.new[b]
-        rows = sorted(set(list(range(8)) + list(range(C - 8, C)) + [63, 64, 127, 128, 255, 256, 300]))
+        # both ends and the middle of every 128-row block (a workgroup's rows at G = 4), plus two
+        # seeded rows per block
+        rows = set(range(4))
+        for r0 in range(0, C, 128):
+            r1 = min(r0 + 128, C)
+            rows |= {r0, r0 + 1, (r0 + r1) // 2, r1 - 2, r1 - 1}
+            rows |= {int(x) for x in rng.integers(r0, r1, size=2)}
+        rows = sorted(rows)
         kf = np.concatenate([host_rows(kp[cup[b]:cup[b + 1]]), host_rows(kn[cu[b]:cu[b + 1]])])
         vf = np.concatenate([host_rows(vp[cup[b]:cup[b + 1]]), host_rows(vn[cu[b]:cu[b + 1]])])
         want = oracle.extend_from_logical(host_rows(q[cu[b]:cu[b + 1]]), kf, vf, wl.prefix[b], rows, wl.scale)
-        err = float(np.max(np.abs(got[cu[b] + np.array(rows)] - want)))
-        print(f"[fullsize] extend session {b}: {len(rows)} rows, max-abs err {err:.3e}", flush=True)
+        gs = got[cu[b] + np.array(rows)]
+        err = float(np.max(np.abs(gs - want)))
+        rel = gu.session_rel_err(gs, want)
+        print(f"[fullsize] extend session {b}: {len(rows)} rows, max-abs err {err:.3e}, session-relative {rel:.4f}",
+              flush=True)
         assert err <= TOL
+        assert rel <= gu.FULLSIZE_REL
     check_tiles(pool, bt, 0, picks[-1], kf, vf, Hkv, D)  # prefix + appended chunk of the last pick
 
 
@@ -232,7 +252,7 @@ def test_private_decode_full_size_sampled():
     picks = sample_sessions(wl.lens, 8, wl.seed)
     qh = host_rows(q)
     (ks, vs, cus), (kp, vp, cup) = logical
-    err = 0.0
+    err = rel = 0.0
     for b in picks:
         for n in range(N):
             r = b * N + n
@@ -240,8 +260,10 @@ def test_private_decode_full_size_sampled():
             V = np.concatenate([host_rows(vs[cus[b]:cus[b + 1]]), host_rows(vp[cup[r]:cup[r + 1]])])
             want = oracle.decode_from_logical(qh[b:b + 1, n:n + 1], [K], [V], wl.scale)[0]
             err = max(err, float(np.max(np.abs(got[b, n:n + 1] - want))))
-    print(f"[fullsize] private: sessions {picks} max-abs err {err:.3e}", flush=True)
+            rel = max(rel, gu.session_rel_err(got[b, n:n + 1], want))
+    print(f"[fullsize] private: sessions {picks} max-abs err {err:.3e}, session-relative {rel:.4f}", flush=True)
     assert err <= TOL
+    assert rel <= gu.FULLSIZE_REL
 
 
 def test_cascade_decode_full_size_sampled():
@@ -283,12 +305,14 @@ def test_cascade_decode_full_size_sampled():
     picks = sample_sessions(lens, 8, wl.seed)
     qh = host_rows(q)
     (kp, vp, cup), (ko, vo, cuo) = logical
-    err = 0.0
+    err = rel = 0.0
     for b in picks:
         f = firsts.index(max(x for x in firsts if x <= b))
         K = np.concatenate([host_rows(kp[cup[f]:cup[f + 1]]), host_rows(ko[cuo[b]:cuo[b + 1]])])
         V = np.concatenate([host_rows(vp[cup[f]:cup[f + 1]]), host_rows(vo[cuo[b]:cuo[b + 1]])])
         want = oracle.decode_from_logical(qh[b:b + 1], [K], [V], wl.scale)
         err = max(err, float(np.max(np.abs(got[b:b + 1] - want))))
-    print(f"[fullsize] cascade: sessions {picks} max-abs err {err:.3e}", flush=True)
+        rel = max(rel, gu.session_rel_err(got[b:b + 1], want))
+    print(f"[fullsize] cascade: sessions {picks} max-abs err {err:.3e}, session-relative {rel:.4f}", flush=True)
     assert err <= TOL
+    assert rel <= gu.FULLSIZE_REL

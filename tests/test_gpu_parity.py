@@ -133,6 +133,22 @@ def test_decode_split_unit_merges(B, Hkv, N, G, D):
     assert int(case["status"].item()) == 0
 
 
+@pytest.mark.parametrize("lens,Hkv,N,G,D", [
+    ([100000], 1, 1, 1, 64),         # one unit over all 1024 shares: a 4-level merge tree
+    ([70000, 3], 2, 2, 2, 128),      # two long units (3 levels), a short one inside one share
+    ([5000], 1, 3, 1, 64),           # 313 tiles: most shares empty, empty children between full ones
+    ([40, 17, 1], 1, 1, 4, 128),     # a handful of tiles spread over 1024 shares
+])
+def test_decode_merge_tree_depths(lens, Hkv, N, G, D):
+    """Units split over many shares are merged by a tree of nodes of up to 8 children;
+    trees of 1 to 4 levels, with children that hold no tiles, against the oracle."""
+    case = gu.make_decode_case(lens, N, Hkv, G, D, seed=sum(lens) % 1000 + D, poison=gu.POISON_NAN)
+    out = gu.run_decode(case)
+    want = oracle.decode_from_logical(case["q"], case["K"], case["V"], 1.0 / math.sqrt(D))
+    assert max_err(out, want) <= TOL
+    assert int(case["status"].item()) == 0
+
+
 def test_decode_workspace_counters_back_to_zero_across_shapes():
     """One workspace serves calls of different shapes in a row: every call finds its arrival
     counters at zero and leaves them so (the first 8 KiB read back as zero), and each

@@ -131,6 +131,52 @@ def test_groups_match_their_definition():
                 assert (gid[b] == gid[b - 1]) == same
 
 
+# Worked tables for the grouping rule (adjacent sessions holding at least one full page
+# with the same first page form a group; its prefix is the leading entries equal across
+# the group, cut to the full pages every member holds).  Each expected value is worked
+# out by hand from that rule.
+GROUP_CASES = [
+    # sessions 0-2 share page 5; session 2 holds 2 full pages, and entry 1 differs: prefix 1
+    ([[5, 6, 7], [5, 6, 9], [5, 8, 1], [2, 3, 4]], [48, 48, 40, 48], [0, 0, 0, -1], [1, 1, 1, 0]),
+    # session 2 holds no full page: not in the run; sessions 0-1 agree on both full pages
+    ([[1, 2], [1, 2], [1, 3]], [32, 32, 15], [0, 0, -1], [2, 2, 0]),
+    # four sessions with one full page each, all on page 4
+    ([[4], [4], [4], [4]], [16, 16, 17, 31], [0, 0, 0, 0], [1, 1, 1, 1]),
+    # equal first pages that are not adjacent form no group
+    ([[1], [2], [1]], [16, 16, 16], [-1, -1, -1], [0, 0, 0]),
+    # two runs side by side: prefixes 2 and 1
+    ([[1, 9], [1, 9], [2, 8], [2, 8], [2, 7]], [32] * 5, [0, 0, 2, 2, 2], [2, 2, 1, 1, 1]),
+    # a single session never groups
+    ([[3, 3]], [64], [-1], [0]),
+]
+
+
+@pytest.mark.parametrize("bt,lens,gid,pref", GROUP_CASES)
+def test_groups_worked_tables(bt, lens, gid, pref):
+    assert pcm.groups(bt, lens) == (gid, pref)
+
+
+def test_groups_are_complete():
+    """Every maximal run of two or more adjacent sessions that hold a full page and share
+    their first page is one group with a prefix of at least one page (a model that never
+    groups, or splits runs, fails here)."""
+    rng = random.Random(5)
+    for _ in range(200):
+        B = rng.randint(0, 8)
+        bt = [[rng.choice([0, 1]) if p == 0 else rng.randint(0, 3) for p in range(4)] for _ in range(B)]
+        lens = [rng.choice([0, 5, 16, 20, 32, 48, 64]) for _ in range(B)]
+        gid, pref = pcm.groups(bt, lens)
+        b = 0
+        while b < B:
+            e = b + 1
+            if lens[b] >= PAGE:
+                while e < B and lens[e] >= PAGE and bt[e][0] == bt[b][0]:
+                    e += 1
+            if e - b >= 2:
+                assert gid[b:e] == [b] * (e - b) and all(p >= 1 for p in pref[b:e]), (bt, lens, gid, pref)
+            b = e
+
+
 MODEL_SRC = open(pcm.__file__).read()
 MUTANTS = {
     "reuse_skips_a_missing_block": ("            if key not in self.page_of_entry:\n                break",
@@ -142,6 +188,33 @@ MUTANTS = {
     "publishes_partial_block": ("full = len(tokens) // PAGE\n        for i in range(full):\n            if not",
                                 "full = -(-len(tokens) // PAGE)\n        for i in range(full):\n            if not"),
 }
+
+
+GROUP_MUTANTS = {
+    "never_groups": ("        if e - b >= 2:\n", "        if e - b >= 99:\n"),
+    "groups_pairs_only": ("            while e < B and seq_lens[e] >= PAGE",
+                          "            while e < b + 2 and e < B and seq_lens[e] >= PAGE"),
+    "ignores_partial_members": ("full = min(seq_lens[m] // PAGE for m in range(b, e))",
+                                "full = max(seq_lens[m] // PAGE for m in range(b, e))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GROUP_MUTANTS))
+def test_group_pins_catch_mutant(name, monkeypatch):
+    old, new = GROUP_MUTANTS[name]
+    assert MODEL_SRC.count(old) == 1, name
+    ns = {"__name__": "prefix_cache_mutant"}
+    exec(compile(MODEL_SRC.replace(old, new), "<mutant>", "exec"), ns)
+    monkeypatch.setattr(pcm, "groups", ns["groups"])
+    failed = 0
+    pins = [lambda c=c: test_groups_worked_tables(*c) for c in GROUP_CASES] + [test_groups_are_complete,
+                                                                                 test_groups_match_their_definition]
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, IndexError):
+            failed += 1
+    assert failed, f"mutant {name} survived every grouping pin"
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
