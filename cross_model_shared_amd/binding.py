@@ -41,6 +41,8 @@ _SIGNATURES = {
     "shared_kv_decode_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
     "shared_kv_decode": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                         _f, _vp, _sz, _vp, _vp]),
+    "shared_kv_decode_noalloc": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                                _f, _vp, _vp]),
     "shared_kv_decode_append": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                                _i32, _i32, _f, _vp, _sz, _vp, _vp]),
     "shared_kv_decode_private": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32,
@@ -204,6 +206,20 @@ def decode(pool: Pool, layer, q, out, block_table, seq_lens, max_seq_len, scale,
         _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
         _ptr(seq_lens, "seq_lens", torch.int32, B), B, N, Hq, max_seq_len, float(scale),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True), _stream(stream)))
+
+
+def decode_noalloc(pool: Pool, layer, q, out, block_table, seq_lens, max_seq_len, scale, dev_status=None,
+                   stream=None):
+    """decode() with the library's static scratch instead of a workspace (allocates nothing)."""
+    torch = _torch()
+    B, N, Hq, D = q.shape
+    if D != pool.head_dim or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q/out shape does not match the pool")
+    _check(load().shared_kv_decode_noalloc(
+        pool.struct, layer, _ptr(q, "q", torch.bfloat16), _ptr(out, "out", torch.bfloat16),
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
+        _ptr(seq_lens, "seq_lens", torch.int32, B), B, N, Hq, max_seq_len, float(scale),
         _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True), _stream(stream)))
 
 

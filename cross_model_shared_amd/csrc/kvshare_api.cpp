@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/kvshare.h"
@@ -242,6 +243,72 @@ int shared_kv_decode(const kvs_pool* pool, int32_t layer, const void* q, void* o
   return decode_common("shared_kv_decode", pool, layer, q, out, block_table, bt_stride, seq_lens, nullptr, 0,
                        nullptr, nullptr, nullptr, batch, num_decoders, num_q_heads, max_seq_len, 0, scale,
                        workspace, workspace_bytes, dev_status, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of shared_kv_decode_noalloc: a decode workspace for the largest call
+// the library accepts (batch <= 4096, head_dim <= 128), in device memory the
+// code object itself holds, so the entry point allocates nothing.  In host code
+// `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+constexpr size_t kNoAllocScratchBytes = kvs::kDecodeWorkspaceMaxBytes;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's scratch address.  At its first use on a device it also
+// zeroes the arrival counters (with a fill kernel on `stream`); every decode
+// call leaves them zero again.
+int noalloc_scratch(void** out, hipStream_t stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVS_EHIP, "shared_kv_decode_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KVS_EUNSUPPORTED, "shared_kv_decode_noalloc: device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(KVS_EHIP, "shared_kv_decode_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    e = kvs::launch_zero(ptr, kvs::kDecodeCounterBytes, stream);
+    if (e != hipSuccess)
+      return fail(KVS_EHIP, "shared_kv_decode_noalloc: clearing the scratch counters: %s", hipGetErrorString(e));
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return KVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int shared_kv_decode_noalloc(const kvs_pool* pool, int32_t layer, const void* q, void* out,
+                             const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                             int32_t batch, int32_t num_decoders, int32_t num_q_heads, int32_t max_seq_len,
+                             float scale, int32_t* dev_status, hipStream_t stream) {
+  const char* name = "shared_kv_decode_noalloc";
+  if (!pool) return fail(KVS_EINVAL, "%s: pool is NULL", name);
+  if (batch > kvs::kDecodeMaxBatch)
+    return fail(KVS_EUNSUPPORTED, "%s: batch %d above %d", name, batch, kvs::kDecodeMaxBatch);
+  if (batch > 0 && pool->head_dim > 0 && pool->head_dim <= 128) {
+    const size_t need = kvs::decode_workspace_size(batch, pool->head_dim);
+    if (need > kNoAllocScratchBytes)
+      return fail(KVS_EWORKSPACE, "%s: the call needs %zu bytes of scratch, above the static %zu", name, need,
+                  kNoAllocScratchBytes);
+  }
+  void* ws = nullptr;
+  int s = noalloc_scratch(&ws, stream);
+  if (s) return s;
+  return decode_common(name, pool, layer, q, out, block_table, bt_stride, seq_lens, nullptr, 0, nullptr, nullptr,
+                       nullptr, batch, num_decoders, num_q_heads, max_seq_len, 0, scale, ws, kNoAllocScratchBytes,
+                       dev_status, stream);
 }
 
 int shared_kv_decode_append(const kvs_pool* pool, int32_t layer, const void* k_new, const void* v_new,

@@ -16,6 +16,7 @@
  *   kv_pool_append         write new K/V rows into pages        (the cache "store")
  *   shared_kv_decode       N decoders x G GQA heads, one KV read (decode attention)
  *   shared_kv_decode_workspace_init  zero the arrival counters of a new decode workspace
+ *   shared_kv_decode_noalloc  shared_kv_decode on a static scratch (allocates nothing)
  *   shared_kv_decode_append  the same, writing the step's own token into the
  *                          pool in the same launch (append + decode fused)
  *   shared_kv_decode_private  the same over a shared prefix + per-decoder private suffixes
@@ -198,6 +199,32 @@ int shared_kv_decode(const kvs_pool* pool, int32_t layer, const void* q, void* o
                      int32_t batch, int32_t num_decoders, int32_t num_q_heads,
                      int32_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
                      int32_t* dev_status, hipStream_t stream);
+
+/*
+ * shared_kv_decode_noalloc — shared_kv_decode without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments, results and device checks as shared_kv_decode, minus
+ * `workspace` / `workspace_bytes`.  The workspace is a scratch array of
+ * 68,289,024 bytes (the size shared_kv_decode_workspace_bytes gives for
+ * batch 4096, head_dim 128, the largest call the library accepts) that the
+ * library's code object holds in device memory; each GPU the library runs on
+ * holds its own copy until the process ends.  The call allocates nothing (no
+ * hipMalloc, no hipFree, no allocating library routine).  On its first call on
+ * a device it looks up that device's scratch address and zeroes the scratch's
+ * arrival counters with a fill kernel on `stream`; every call leaves them zero.
+ *  - The stream must belong to the current device.
+ *  - Every call on a GPU uses that GPU's one scratch array: calls that overlap in
+ *    time on one GPU (other streams, other threads) race and give wrong
+ *    results.  Serialize them.
+ *  - A call needing more scratch than the array holds returns KVS_EWORKSPACE
+ *    (no call within the documented bounds does).
+ */
+int shared_kv_decode_noalloc(const kvs_pool* pool, int32_t layer, const void* q, void* out,
+                             const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                             int32_t batch, int32_t num_decoders, int32_t num_q_heads,
+                             int32_t max_seq_len, float scale, int32_t* dev_status, hipStream_t stream);
 
 /*
  * shared_kv_decode_append — kv_pool_append of one token per session followed by
