@@ -82,6 +82,17 @@ __device__ __forceinline__ void dma_slab(uint32_t lds, const void* src, int lane
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
+// The kernel's argument block (its only argument, at offset 0 of the kernarg
+// segment) through a pointer the compiler cannot look through.  Fields read
+// through it are loaded where they are used: the code at a unit's end reads
+// its pointers this way, so they do not sit in scalar registers across the
+// page loop (the scalar file is full there, and what does not fit is spilled
+// into vector-register lanes and reloaded on every page).
+__device__ __forceinline__ const DecodeArgs& args_late() {
+  uint64_t p = uint64_t(__builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+s"(p));
+  return *(const DecodeArgs*)(const __attribute__((address_space(4))) DecodeArgs*)p;
+}
 template <class T>
 __device__ __forceinline__ uint32_t lds_addr(T* p) {
   return uint32_t(size_t((__attribute__((address_space(3))) T*)p));
@@ -491,16 +502,18 @@ __device__ __forceinline__ void finish_split(const DecodeArgs& a, int k, bool be
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const bool root = g1 == k1 && g0 == k0;
     const int64_t dst = root ? 0 : slot_of(first_with_tiles(g0));
-    // the node's children: the slot holding each child's state, or -1 for a
-    // child without tiles of the unit (a level-1 child is a share, which holds
-    // its own state; a higher child's state sits in its first share with tiles)
-    int64_t cslot[1 << kMergeFanLog2];
-#pragma unroll
-    for (int c = 0; c < (1 << kMergeFanLog2); ++c) {
-      const int p = g0 + c * cspan, q = min(p + cspan - 1, g1);
-      const bool has = p <= g1 && (dense || range_tiles<WPG>(p, q, s_u, e_u, T) > 0);
-      cslot[c] = !has ? -1 : slot_of(lv == 1 ? p : first_with_tiles(p));
+    // the node's children, child c on lane c: the slot holding its state, or -1
+    // for a child without tiles of the unit (a level-1 child is a share, which
+    // holds its own state; a higher child's state sits in its first share with
+    // tiles).  One vector register instead of eight scalar pairs: scalar
+    // registers live here would be spilled inside the page loop.
+    int cslot = -1;
+    {
+      const int p = g0 + lane * cspan, q = min(p + cspan - 1, g1);
+      if (lane < (1 << kMergeFanLog2) && p <= g1 && (dense || range_tiles<WPG>(p, q, s_u, e_u, T) > 0))
+        cslot = int(slot_of(lv == 1 ? p : first_with_tiles(p)));
     }
+    const uint64_t has_child = __ballot(cslot >= 0);
     // one 16-row column block at a time (fewer live registers); children in
     // batches of KB, every load of a batch issued before any merge
 #pragma unroll 1
@@ -511,16 +524,14 @@ __device__ __forceinline__ void finish_split(const DecodeArgs& a, int k, bool be
       for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c0 = 0; c0 < (1 << kMergeFanLog2); c0 += KB) {
-        bool any = false;  // (a child of only empty shares can sit between children with tiles)
-#pragma unroll
-        for (int u = 0; u < KB; ++u) any |= cslot[c0 + u] >= 0;
-        if (!any) continue;
+        // (a child of only empty shares can sit between children with tiles)
+        if (((has_child >> c0) & ((1u << KB) - 1)) == 0) continue;
         f32x2 mlv[KB];
         f32x4 av[KB][D / 16];
         bool use[KB];
 #pragma unroll
         for (int u = 0; u < KB; ++u) {
-          const int64_t slot = cslot[c0 + u];
+          const int slot = __builtin_amdgcn_readlane(cslot, c0 + u);
           use[u] = slot >= 0;
           mlv[u] = f32x2{-INFINITY, 0.f};
           if (!use[u]) continue;
@@ -789,17 +800,18 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       const int npg_u = cum_s[cur_b + 1] - cum_s[cur_b];
       const int64_t unit_end = unit_begin + npg_u;
       const bool before = unit_begin < tau0, after = unit_end > tau1;
+      const DecodeArgs& al = args_late();
       if (!before && !after) {
-        write_rows<D, NB, MODE>(a, st, cur_b, cur_gr / RGs, cur_gr % RGs, lane);
+        write_rows<D, NB, MODE>(al, st, cur_b, cur_gr / RGs, cur_gr % RGs, lane);
       } else {  // split: the share's first unit (continued) or its last one (begun)
-        write_partial<D, NB>(a, st, k * 2 + (before ? 0 : 1), lane);
+        write_partial<D, NB>(al, st, k * 2 + (before ? 0 : 1), lane);
         finish_split<D, NB, MODE, kWaves, (NB >= 4 ? 1 : 4 / NB)>(
-            a, k, before, 1, 0, int(min(unit_end, tau1) - max(unit_begin, tau0)), npg_u, unit_begin, T, cur_b,
+            al, k, before, 1, 0, int(min(unit_end, tau1) - max(unit_begin, tau0)), npg_u, unit_begin, T, cur_b,
             cur_gr / RGs, cur_gr % RGs, lane);
       }
       if (!last) {
         st.init();
-        load_q<D, NB, MODE>(qf, a, cw.b, cw.gr / RGs, cw.gr % RGs, lane);
+        load_q<D, NB, MODE>(qf, al, cw.b, cw.gr / RGs, cw.gr % RGs, lane);
         load_new(cw.b, cw.gr / RGs);
         unit_begin = int64_t(cw.gr) * Ptot + cum_s[cw.b];
       }
@@ -926,16 +938,17 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
       const int npg_u = cum(cur_b + 1) - cum(cur_b);
       const int64_t unit_end = unit_begin + npg_u;
       const bool before = unit_begin < tau0, after = unit_end > tau1;
+      const DecodeArgs& al = args_late();
       if (!before && !after) {
-        write_rows<D, NB, MODE>(a, st, cur_b, cur_gr, rg, lane);
+        write_rows<D, NB, MODE>(al, st, cur_b, cur_gr, rg, lane);
       } else {  // each wave of the pair merges its own row group
-        write_partial<D, NB>(a, st, (k * 2 + (before ? 0 : 1)) * 2 + rg, lane);
-        finish_split<D, NB, MODE, 1, 1>(a, k, before, 2, rg, int(min(unit_end, tau1) - max(unit_begin, tau0)),
+        write_partial<D, NB>(al, st, (k * 2 + (before ? 0 : 1)) * 2 + rg, lane);
+        finish_split<D, NB, MODE, 1, 1>(al, k, before, 2, rg, int(min(unit_end, tau1) - max(unit_begin, tau0)),
                                         npg_u, unit_begin, T, cur_b, cur_gr, rg, lane);
       }
       if (!last) {
         st.init();
-        load_q<D, NB, MODE>(qf, a, cw.b, cw.gr, rg, lane);
+        load_q<D, NB, MODE>(qf, al, cw.b, cw.gr, rg, lane);
         unit_begin = int64_t(cw.gr) * Ptot + cum(cw.b);
       }
       drain();  // stores and q loads drained before the ring resumes (see the stream kernel)
