@@ -31,6 +31,7 @@ namespace {
 constexpr int kXcds = 8;
 constexpr float kLazy = 8.0f;                // rescaling path: max moves when it grows by > 2^8
 constexpr float kSafeSum = 1.0e18f;          // ~2^60: fixed-reference sums stay below this
+constexpr int kExtendPairRounds = 4;         // paired grid >= this many full rounds of resident workgroups
 
 template <int VM>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -233,7 +234,7 @@ __device__ __forceinline__ void softmax_rescale(ExtendState<D, NB>& st, const f3
 // buffers); otherwise each block runs QK^T, softmax, PV in turn (fewer registers,
 // so more waves per SIMD can hide each other's latency).
 template <int D, int NB, int WAVES, int kStages, int kLook, int BLOCKS_PER_CU, bool PIPE>
-__global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(ExtendArgs a, int row_blocks) {
+__global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(ExtendArgs a, int row_blocks, int pairs) {
   static_assert(kStages >= kLook + 2, "a stage is rewritten only after every wave has left it");
   constexpr int THREADS = 64 * WAVES;
   constexpr int kRowsPerWave = 16 * NB;
@@ -246,10 +247,16 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
 
   const int Hkv = a.pool.num_kv_heads;
   const int units = a.num_layers * a.batch * Hkv;  // (layer, session, KV head), KV head fastest
+  // Workgroup slots per unit: one per row block, heaviest (longest key walk)
+  // first; or, with pairs, one per pair of row blocks rb and row_blocks-1-rb,
+  // run one after the other.  In a causal chunk the key walk grows by one block
+  // per row block, so every pair walks the same number of key blocks and the
+  // workgroups get equal work.
+  const int slots = pairs ? (row_blocks + 1) / 2 : row_blocks;
   const int xcd = blockIdx.x % kXcds;
   const int kk = blockIdx.x / kXcds;
-  const int unit = (kk / row_blocks) * kXcds + xcd;
-  const int rb = row_blocks - 1 - kk % row_blocks;  // heaviest (longest-key) row blocks first
+  const int unit = (kk / slots) * kXcds + xcd;
+  const int slot = kk % slots;
   if (unit >= units) return;
   const int l = unit / (a.batch * Hkv), b = (unit / Hkv) % a.batch, g = unit % Hkv;
   const int layer = a.layer + l;
@@ -263,10 +270,11 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
   const int c0 = load_uniform(a.cu_new + b), c1 = load_uniform(a.cu_new + b + 1);
   const int C = c1 - c0;
   if (P < 0 || C < 0 || C > a.max_new || P + C > a.max_seq_len || c0 < 0 || c1 > a.total_new) {
-    if (threadIdx.x == 0 && rb == 0) flag_error(a.dev_status, KVS_DEV_BAD_LEN_BIT);
+    if (threadIdx.x == 0 && slot == 0) flag_error(a.dev_status, KVS_DEV_BAD_LEN_BIT);
     return;
   }
   const int rows = C * G;
+  auto row_block = [&](const int rb) {
   const int rbase = rb * kRowsPerBlock;
   if (rbase >= rows) return;  // whole workgroup: uniform
   const int total = P + C;
@@ -561,6 +569,15 @@ __global__ __launch_bounds__(64 * WAVES, BLOCKS_PER_CU) void extend_kernel(Exten
       *reinterpret_cast<u32x2*>(o + 16 * i + 4 * (ln >> 4)) = pack_bf16x4(v[0], v[1], v[2], v[3]);
     }
   }
+  };  // row_block
+
+  row_block(row_blocks - 1 - slot);
+  if (pairs && slot != row_blocks - 1 - slot) {
+    // every wave has consumed its last ring reads (their results fed the output
+    // rows) before the next row block loads into the ring
+    block_barrier();
+    row_block(slot);
+  }
 }
 
 template <int D, int NB, int WAVES, int STAGES, int LOOK, int PER_CU, bool PIPE>
@@ -570,10 +587,14 @@ hipError_t launch_extend_t(const ExtendArgs& a, hipStream_t stream) {
   const int row_blocks = (a.max_new * G + kRowsPerBlock - 1) / kRowsPerBlock;
   const int64_t units = int64_t(a.num_layers) * a.batch * a.pool.num_kv_heads;
   const int64_t unit_rounds = (units + kXcds - 1) / kXcds;
-  const int64_t blocks = unit_rounds * row_blocks * kXcds;
+  // Pair row blocks when the halved grid still holds several rounds of
+  // workgroups for the chip: short walks then share a workgroup with long ones.
+  const int64_t resident = int64_t(device_cu_count()) * PER_CU;
+  const int pairs = row_blocks >= 2 && unit_rounds * kXcds * ((row_blocks + 1) / 2) >= kExtendPairRounds * resident;
+  const int64_t blocks = unit_rounds * (pairs ? (row_blocks + 1) / 2 : row_blocks) * kXcds;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((extend_kernel<D, NB, WAVES, STAGES, LOOK, PER_CU, PIPE>), dim3(unsigned(blocks)), dim3(64 * WAVES), 0,
-                     stream, a, row_blocks);
+                     stream, a, row_blocks, pairs);
   return hipGetLastError();
 }
 

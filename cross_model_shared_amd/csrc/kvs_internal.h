@@ -75,6 +75,10 @@ constexpr size_t decode_workspace_size(int batch, int head_dim) {
 // The largest workspace any decode call needs (batch <= kDecodeMaxBatch, head_dim <= 128).
 constexpr size_t kDecodeWorkspaceMaxBytes = decode_workspace_size(kDecodeMaxBatch, 128);
 
+// Compute units of the current device (read once per device, then cached;
+// 256, MI355X's count, if the query fails).
+int device_cu_count();
+
 // Record a printf-style message for kvs_last_error() and return `status`.
 int set_error(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 

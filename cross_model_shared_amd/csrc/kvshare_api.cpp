@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -78,6 +79,18 @@ int launched(hipError_t e, const char* what) {
 }  // namespace
 
 namespace kvs {
+
+int device_cu_count() {
+  constexpr int kDevices = 64, kFallback = 256;
+  static std::atomic<int> cached[kDevices];  // 0: not read yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return kFallback;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = kFallback;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 int set_error(int status, const char* fmt, ...) {
   va_list ap;
