@@ -31,6 +31,13 @@ COMMON = [
 # Kernel sources only: no NaN canonicalization around max/min (masked scores
 # are -inf, never NaN).  The host-side C ABI checks keep IEEE NaN semantics.
 KERNEL_FLAGS = ["-fno-honor-nans"]
+# Per-source device flags.  decode.hip: matrix-core steps read and write their
+# accumulators in ordinary vector registers.  Otherwise the compiler gives the
+# decode accumulators an accumulation-register home for the matrix steps and a
+# vector-register home for the online-softmax rescale, and copies all of them
+# both ways on every page (measured: the 8-decoder layer 1% faster, the
+# 64-row groups 28% faster, outputs bit-identical; extend is unchanged by it).
+SOURCE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -46,7 +53,7 @@ def _compile(src: str) -> str:
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     else:
-        cmd[1:1] = KERNEL_FLAGS
+        cmd[1:1] = KERNEL_FLAGS + SOURCE_FLAGS.get(src, [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)  # host pass does not know the feature
