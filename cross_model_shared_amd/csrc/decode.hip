@@ -978,6 +978,14 @@ __device__ __forceinline__ int block_scan(int x, int* buf) {
   return x;
 }
 
+// 64-bit finalizer of the splitmix64 generator (Steele, Lea and Flood, "Fast
+// splittable pseudorandom number generators", OOPSLA 2014).
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
 // Cascade plan.  Sessions with equal, non-negative group ids that are adjacent in
 // the batch share their first group_prefix[b] pages.  Runs of such sessions are
 // cut into units of at most `per_unit` sessions (all rows of a unit fit one
@@ -987,6 +995,13 @@ __device__ __forceinline__ int block_scan(int x, int* buf) {
 // Flags: members whose group_prefix differs from the unit's first session's
 // (BAD_LEN), and shared-prefix block-table entries that differ from the first
 // session's (BAD_PAGE); the prefix read is always the first session's.
+//
+// The tables depend only on the batch, the sessions per unit, the length bound
+// and every session's length, group id and prefix claim, which the layers of a
+// decode step share.  A 64-bit fingerprint of those inputs is stored with the
+// tables; a call whose inputs hash to the stored fingerprint finds its tables
+// already in the workspace and returns at once, so a step plans once for all
+// its layers (the block-table checks run when the tables are rebuilt).
 __global__ __launch_bounds__(1024) void decode_cascade_plan_kernel(DecodeArgs a, int per_unit) {
   constexpr int E = 4;
   __shared__ int buf[1024];
@@ -995,7 +1010,32 @@ __global__ __launch_bounds__(1024) void decode_cascade_plan_kernel(DecodeArgs a,
   __shared__ int first_s[kDecodeMaxBatch];
   __shared__ int pref_s[kDecodeMaxBatch];
   __shared__ int voff_s[kDecodeMaxBatch + 1];
+  __shared__ uint64_t fp_s[16];
   const int B = a.batch, tid = threadIdx.x;
+  {
+    uint64_t h = 0;
+    for (int i = 0; i < E; ++i) {
+      const int b = tid * E + i;
+      if (b < B) {
+        const uint64_t lg = (uint64_t(uint32_t(a.seq_lens[b])) << 32) | uint32_t(a.group_id[b]);
+        h ^= mix64(mix64(lg ^ (uint64_t(b) << 20)) ^ uint64_t(uint32_t(a.group_prefix[b])));
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t lo = __shfl_xor(uint32_t(h), off), hi = __shfl_xor(uint32_t(h >> 32), off);
+      h ^= (uint64_t(hi) << 32) | lo;
+    }
+    if ((tid & 63) == 0) fp_s[tid >> 6] = h;
+    __syncthreads();
+    h = mix64((uint64_t(uint32_t(B)) << 40) ^ (uint64_t(uint32_t(per_unit)) << 32) ^ uint32_t(a.max_seq_len));
+#pragma unroll
+    for (int w = 0; w < 16; ++w) h ^= fp_s[w];
+    const uint32_t* stored = reinterpret_cast<const uint32_t*>(a.ws_units + 3 * B + 1);
+    if (stored[0] == uint32_t(h) && stored[1] == uint32_t(h >> 32)) return;  // whole workgroup: uniform
+    __syncthreads();  // every thread has compared before thread 0 rewrites the fingerprint below
+    if (tid == 0) fp_s[0] = h;
+  }
   int L[E], us[E];
   for (int i = 0; i < E; ++i) {
     const int b = tid * E + i;
@@ -1075,6 +1115,12 @@ __global__ __launch_bounds__(1024) void decode_cascade_plan_kernel(DecodeArgs a,
   if (tid == 0) {
     a.ws_cum[nu] = total;
     a.ws_units[3 * B] = nu;
+  }
+  __syncthreads();  // every table entry written before the fingerprint that vouches for them
+  if (tid == 0) {
+    const uint64_t h = fp_s[0];
+    a.ws_units[3 * B + 1] = int(uint32_t(h));
+    a.ws_units[3 * B + 2] = int(uint32_t(h >> 32));
   }
   // 5. check the shared-prefix entries of every non-first session
   const int incl_v = block_scan<false>(v, buf);

@@ -59,13 +59,15 @@ static_assert(kDecodeBlocks * 4 == 1 << kDecodeShareLog2, "share count");
 constexpr size_t kDecodeCounterBytes = size_t(4) * (size_t(4) << kDecodeShareLog2) * 4;
 
 // Decode workspace layout: arrival counters, then the cascade unit prefix sum
-// [batch+1] and unit tables [3*batch+1], then the partial-state slots (2 per
+// [batch+1] and unit tables [3*batch+3] (first session, count and prefix per
+// unit; the unit count; a 64-bit fingerprint of the inputs the tables were
+// built from), then the partial-state slots (2 per
 // wave, sized for 64-row groups): (m, l) per row, then a D-vector per row.
 constexpr size_t decode_align(size_t x) { return (x + 255) / 256 * 256; }
 constexpr size_t kDecodeSlots = size_t(kDecodeBlocks) * 4 * 2, kDecodeSlotRows = 64;
 constexpr size_t decode_cum_offset() { return kDecodeCounterBytes; }
 constexpr size_t decode_units_offset(int batch) { return decode_cum_offset() + decode_align(size_t(batch + 1) * 4); }
-constexpr size_t decode_ml_offset(int batch) { return decode_units_offset(batch) + decode_align(size_t(3 * batch + 1) * 4); }
+constexpr size_t decode_ml_offset(int batch) { return decode_units_offset(batch) + decode_align(size_t(3 * batch + 3) * 4); }
 constexpr size_t decode_acc_offset(int batch) {
   return decode_ml_offset(batch) + decode_align(kDecodeSlots * kDecodeSlotRows * 2 * 4);
 }
@@ -112,7 +114,7 @@ struct DecodeArgs {
   const uint16_t* k_new;
   const uint16_t* v_new;
   int* ws_cnt;    // arrival counters of split units' merge trees; zero on entry and on exit
-  int* ws_units;  // [3*batch+1] cascade units: first session, count, prefix pages; unit count
+  int* ws_units;  // [3*batch+3] cascade units: first session, count, prefix pages; unit count; fingerprint
   int* ws_cum;    // [batch+1] cascade unit tile prefix sum, written by the plan kernel
   float* ws_ml;   // [4*blocks*2][rg_rows][2] partial (m, l)
   float* ws_acc;  // [4*blocks*2][rg_rows][D] partial acc

@@ -312,6 +312,13 @@ int shared_kv_decode_private(const kvs_pool* pool, int32_t layer, const void* q,
  *                prefix is also cut to whole pages every member holds.
  *  Needs num_decoders * (num_q_heads / num_kv_heads) <= 64.  Other arguments
  *  and the workspace as for shared_kv_decode.
+ *
+ * The units are planned by a first kernel into the workspace, with a 64-bit
+ * fingerprint of what they depend on (batch, sessions per unit, max_seq_len,
+ * and every session's seq_lens, group_id and group_prefix_pages).  A call whose
+ * inputs have the stored fingerprint reuses the planned units, so the layers of
+ * a decode step that share a workspace plan once; any change to those inputs
+ * plans again.  The block-table checks above run when the units are planned.
  */
 int shared_kv_decode_cascade(const kvs_pool* pool, int32_t layer, const void* q, void* out,
                              const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,

@@ -174,3 +174,42 @@ def test_cascade_over_allocator_tables():
     print(f"[cascade] allocator tables: max-abs err {err:.3e}", flush=True)
     assert err <= TOL
     assert int(st.item()) == 0
+
+
+def test_cascade_tables_reused_only_for_the_same_inputs():
+    """One workspace serves a sequence of cascade calls: repeated calls with the same
+    inputs find their tables already built (the plan kernel returns at once), and any
+    change to a length, a group id or a prefix claim rebuilds them.  Every call must
+    equal the same call on a fresh workspace, bit for bit."""
+    import torch
+
+    groups = [(64, [100, 64, 300]), (0, [17]), (32, [33, 48])]
+    c = make_case(groups, 8, 2, 4, 128, seed=91)
+    B, N, Hq, D = c["q"].shape
+    msl = max(max(c["lens"]), 1)
+    nbytes = binding.decode_workspace_bytes(B, N, Hq, c["Hkv"], D, msl)
+    shared = gu.nan_workspace(nbytes)
+
+    def call(ws, lens, gid, pref):
+        out = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device="cuda")
+        binding.decode_cascade(c["pool"], 0, gu.dev_bf16(c["q"]), out, gu.dev_i32(c["bt"]), gu.dev_i32(lens),
+                               gu.dev_i32(gid), gu.dev_i32(pref), msl, 1.0 / math.sqrt(D), ws,
+                               dev_status=c["status"])
+        gu.sync()
+        return out
+
+    lens, gid, pref = list(c["lens"]), list(c["gid"]), list(c["pref"])
+    shorter = list(lens)
+    shorter[1] -= 1                      # one session one token shorter (its last token dropped)
+    split = list(gid)
+    split[2] = -1                        # the group's third member no longer shares
+    claim = list(pref)
+    claim[0] = claim[1] = 2              # the first group claims 2 of its 4 prefix pages
+    seq = [(lens, gid, pref), (lens, gid, pref), (shorter, gid, pref), (lens, gid, pref),
+           (lens, split, pref), (lens, gid, claim), (lens, gid, pref)]
+    for i, (l_, g_, p_) in enumerate(seq):
+        print(f"[cascade reuse] call {i}", flush=True)
+        got = call(shared, l_, g_, p_)
+        want = call(gu.nan_workspace(nbytes), l_, g_, p_)
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), i
+    assert int(c["status"].item()) == 0
