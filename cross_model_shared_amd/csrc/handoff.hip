@@ -20,31 +20,37 @@ namespace kvs {
 
 namespace {
 
+#ifndef KVS_PACK_PIECE_KIB
+#define KVS_PACK_PIECE_KIB 16
+#endif
+// One workgroup copies one PIECE-KiB part of a (layer, page) chunk: every thread
+// loads all its 16-byte pieces of the part before storing any.
 template <bool UNPACK>
-__global__ __launch_bounds__(256) void pack_kernel(HandoffArgs a) {
-  const int i = blockIdx.x;        // entry of the page list
+__global__ __launch_bounds__(256) void pack_kernel(HandoffArgs a, int parts) {
+  constexpr int kPer = KVS_PACK_PIECE_KIB * 1024 / 16 / 256;  // 16-byte pieces per thread
+  const int i = blockIdx.x / parts;  // entry of the page list
+  const int part = blockIdx.x % parts;
   const int li = blockIdx.y;       // layer within the range
   const int Hkv = a.pool.num_kv_heads, D = a.pool.head_dim;
   const int pid = a.page_ids[i];
   if (pid < 0 || pid >= a.pool.num_pages) {
-    if (threadIdx.x == 0 && li == 0) flag_error(a.dev_status, KVS_DEV_BAD_PAGE_BIT);
+    if (threadIdx.x == 0 && li == 0 && part == 0) flag_error(a.dev_status, KVS_DEV_BAD_PAGE_BIT);
     return;
   }
   const int64_t chunk = int64_t(Hkv) * 32 * D;   // elements: every head's tile of one page
   uint16_t* pool_chunk = a.pool.data + tile_offset(a.layer_begin + li, pid, 0, a.pool.num_pages, Hkv, D);
   uint16_t* buf_chunk = a.buf + (int64_t(li) * a.num_ids + i) * chunk;
+  const int n = int(chunk / 8);    // 16-byte pieces of the chunk
+  const int p0 = part * kPer * 256, p1 = min(n, p0 + kPer * 256);
   const u32x4* src = reinterpret_cast<const u32x4*>(UNPACK ? buf_chunk : pool_chunk);
   u32x4* dst = reinterpret_cast<u32x4*>(UNPACK ? pool_chunk : buf_chunk);
-  const int n = int(chunk / 8);    // 16-byte pieces, a multiple of 256
-  for (int e0 = 0; e0 < n; e0 += 4 * 256) {
-    u32x4 v[4];
+  u32x4 v[kPer];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (e0 + j * 256 < n) v[j] = src[e0 + j * 256 + threadIdx.x];
+  for (int j = 0; j < kPer; ++j)
+    if (p0 + j * 256 < p1) v[j] = src[p0 + j * 256 + threadIdx.x];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (e0 + j * 256 < n) dst[e0 + j * 256 + threadIdx.x] = v[j];
-  }
+  for (int j = 0; j < kPer; ++j)
+    if (p0 + j * 256 < p1) dst[p0 + j * 256 + threadIdx.x] = v[j];
 }
 
 template <int D>
@@ -97,9 +103,12 @@ __global__ __launch_bounds__(256) void fetch_kernel(FetchArgs a) {
 
 hipError_t launch_pack(const HandoffArgs& a, bool unpack, hipStream_t stream) {
   if (a.num_ids == 0) return hipSuccess;
-  dim3 grid(a.num_ids, a.num_layers);
-  if (unpack) hipLaunchKernelGGL(pack_kernel<true>, grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(pack_kernel<false>, grid, dim3(256), 0, stream, a);
+  const int64_t chunk_bytes = int64_t(a.pool.num_kv_heads) * 32 * a.pool.head_dim * 2;
+  const int parts = int((chunk_bytes + KVS_PACK_PIECE_KIB * 1024 - 1) / (KVS_PACK_PIECE_KIB * 1024));
+  if (int64_t(a.num_ids) * parts > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  dim3 grid(a.num_ids * parts, a.num_layers);
+  if (unpack) hipLaunchKernelGGL(pack_kernel<true>, grid, dim3(256), 0, stream, a, parts);
+  else hipLaunchKernelGGL(pack_kernel<false>, grid, dim3(256), 0, stream, a, parts);
   return hipGetLastError();
 }
 
