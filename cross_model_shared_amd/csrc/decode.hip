@@ -287,49 +287,60 @@ __device__ __forceinline__ int64_t unit_row(const DecodeArgs& a, int b, int g, i
   return (int64_t(b) * a.num_decoders + r / G) * a.num_q_heads + g * G + r % G;
 }
 
-// Stream-K share boundaries: 2^10 shares, WPG consecutive shares per
-// workgroup (4 waves in the stream kernel, one wave pair in the cascade), and
-// the hardware places workgroup i on XCD i % 8.  A share on an even XCD weighs
-// kShareEven, one on an odd XCD kShareOdd (all 1024 weigh 2^18).  Per-wave
-// timestamps show the odd XCDs streaming KV pages slower than the even ones, by
-// 4% to 13% depending on the GPU and the workload; 276 / 236 was the fastest
-// split measured on the 8-decoder workload (2% faster than equal shares, calls
-// alternating in one process).  The weights only move boundaries; any split is
-// correct, and a build may set another one.
+// Stream-K share boundaries.  A call cuts its tile list into n shares, WPG
+// consecutive shares per workgroup (4 waves in the stream kernel, one wave pair
+// in the cascade), n = 4 x the grid's workgroups (the device's CU count, at most
+// 256; the host plans it), and the hardware places workgroup i on XCD i % 8.  A
+// share on an even XCD weighs `even`, one on an odd XCD 512 - even, so all n
+// weigh n * 256.  On MI355X (256 CUs) per-wave timestamps show the odd XCDs
+// streaming KV pages slower than the even ones, by 4% to 13% depending on the
+// GPU and the workload; 276 / 236 was the fastest split measured on the
+// 8-decoder workload (2% faster than equal shares, calls alternating in one
+// process), and other devices get equal shares.  The weights only move
+// boundaries; any split is correct.
+//
+// The weight before share k is scaled to a whole of 2^18 by the multiplier
+// mult = floor(2^26 / n) (exactly 2^16 at n = 1024), W(k) = (weight * mult) >>
+// 16, so that a boundary is a multiply and a shift, no division:
+// share_start(k) = (W(k) * T) >> 18, and share_start(n) = T.  W is
+// non-decreasing and W(n) <= 2^18, so the shares tile 0 .. T in order.
 #ifndef KVS_RING_PAGES_D128  // LDS ring depth per wave at D = 128 (8 KiB pages)
 #define KVS_RING_PAGES_D128 4
 #endif
-#ifndef KVS_SHARE_EVEN
-#define KVS_SHARE_EVEN 276
-#endif
-constexpr int64_t kShareEven = KVS_SHARE_EVEN, kShareOdd = 512 - KVS_SHARE_EVEN;
-constexpr int kShareTotalLog2 = 18;
-static_assert(512 * (kShareEven + kShareOdd) == int64_t(1) << kShareTotalLog2 && kDecodeShareLog2 == 10,
-              "share weights");
+constexpr int kShareWholeLog2 = 18;
+struct Shares {
+  int n;     // shares of the call: a multiple of 8 * WPG, at most 2^kDecodeShareLog2
+  int even;  // weight of a share on an even XCD (1 .. 511)
+  int mult;  // floor(2^26 / n)
+};
+__device__ __forceinline__ Shares call_shares(const DecodeArgs& a) {
+  return Shares{4 * a.plan.blocks, a.plan.share_even, a.plan.share_mult};
+}
 
-// weight of shares 0 .. k-1
+// weight of shares 0 .. k-1, scaled to a whole of 2^18
 template <int WPG>
-__device__ __forceinline__ int64_t share_weight_before(int k) {
+__device__ __forceinline__ int64_t share_weight_before(int k, const Shares& sh) {
   static_assert(WPG == 1 || WPG == 4, "shares per workgroup");
   constexpr int kPer = 8 * WPG;  // shares of one round of 8 workgroups
+  const int even = sh.even, odd = 512 - even;
   const int r = k % kPer, g = r / WPG;  // workgroup within the round = its XCD
-  const int64_t prev = ((g + 1) >> 1) * kShareEven + (g >> 1) * kShareOdd;  // XCDs 0 .. g-1
-  return int64_t(k / kPer) * WPG * 4 * (kShareEven + kShareOdd) + WPG * prev +
-         int64_t(r % WPG) * ((g & 1) ? kShareOdd : kShareEven);
+  const int prev = ((g + 1) >> 1) * even + (g >> 1) * odd;  // XCDs 0 .. g-1
+  const int raw = (k / kPer) * WPG * 4 * 512 + WPG * prev + (r % WPG) * ((g & 1) ? odd : even);
+  return (int64_t(raw) * sh.mult) >> 16;
 }
 template <int WPG>
-__device__ __forceinline__ int64_t share_start(int k, int64_t T) {
-  return (share_weight_before<WPG>(k) * T) >> kShareTotalLog2;
+__device__ __forceinline__ int64_t share_start(int k, int64_t T, const Shares& sh) {
+  return k >= sh.n ? T : (share_weight_before<WPG>(k, sh) * T) >> kShareWholeLog2;
 }
-// the share holding tile t: the largest k with share_start(k) <= t, i.e. with
-// share_weight_before(k) * T < (t + 1) * 2^18
+// the share holding tile t < T: the largest k < n with share_start(k) <= t, i.e.
+// with W(k) * T < (t + 1) * 2^18
 template <int WPG>
-__device__ __forceinline__ int share_of(int64_t t, int64_t T) {
-  const int64_t lim = (t + 1) << kShareTotalLog2;
-  int lo = 0, hi = 1 << kDecodeShareLog2;
+__device__ __forceinline__ int share_of(int64_t t, int64_t T, const Shares& sh) {
+  const int64_t lim = (t + 1) << kShareWholeLog2;
+  int lo = 0, hi = sh.n;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (share_weight_before<WPG>(mid) * T < lim) lo = mid;
+    if (share_weight_before<WPG>(mid, sh) * T < lim) lo = mid;
     else hi = mid;
   }
   return lo;
@@ -433,8 +444,8 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, const RowStat
 
 // Tiles of the unit [s_u, e_u) that shares p .. q hold.
 template <int WPG>
-__device__ __forceinline__ int range_tiles(int p, int q, int64_t s_u, int64_t e_u, int64_t T) {
-  const int64_t lo = max(s_u, share_start<WPG>(p, T)), hi = min(e_u, share_start<WPG>(q + 1, T));
+__device__ __forceinline__ int range_tiles(int p, int q, int64_t s_u, int64_t e_u, int64_t T, const Shares& sh) {
+  const int64_t lo = max(s_u, share_start<WPG>(p, T, sh)), hi = min(e_u, share_start<WPG>(q + 1, T, sh));
   return hi > lo ? int(hi - lo) : 0;
 }
 
@@ -467,17 +478,19 @@ static_assert(kMergeLevels * kCountersPerLevel * 4 <= int(kDecodeCounterBytes), 
 template <int D, int NB, int MODE, int WPG, int KB>
 __device__ __forceinline__ void finish_split(const DecodeArgs& a, int k, bool before, int mul, int add, int mine,
                                              int npg, int64_t s_u, int64_t T, int b, int g, int rg, int lane) {
+  const Shares sh = call_shares(a);
   const int64_t e_u = s_u + npg;
-  const int k0 = before ? share_of<WPG>(s_u, T) : k;
-  const int k1 = share_of<WPG>(e_u - 1, T);
+  const int k0 = before ? share_of<WPG>(s_u, T, sh) : k;
+  const int k1 = share_of<WPG>(e_u - 1, T, sh);
   auto slot_of = [&](int f) { return int64_t(2 * f + (f == k0 ? 1 : 0)) * mul + add; };
-  // Every share holds at least one tile when T * (the smallest share weight) >= 2^18:
+  // Every share holds at least one tile when T * (the smallest scaled share
+  // weight) >= 2^18 (a share's scaled weight is at least floor(its weight x mult / 2^16)):
   // then the unit's shares k0 .. k1 all hold tiles of it, and a range of them
   // starts with a share holding tiles.  Otherwise, search.
-  const bool dense = T * min(kShareEven, kShareOdd) >= (int64_t(1) << kShareTotalLog2);
+  const bool dense = T * ((min(sh.even, 512 - sh.even) * int64_t(sh.mult)) >> 16) >= (int64_t(1) << kShareWholeLog2);
   // the first share of p .. q that holds tiles of the unit (the range has some)
   auto first_with_tiles = [&](int p) {
-    return dense ? max(p, k0) : share_of<WPG>(max(s_u, share_start<WPG>(p, T)), T);
+    return dense ? max(p, k0) : share_of<WPG>(max(s_u, share_start<WPG>(p, T, sh)), T, sh);
   };
   const __amdgpu_buffer_rsrc_t racc = acc_rsrc<D>(a), rml = ml_rsrc(a);
   int child = k, tiles = mine;
@@ -488,7 +501,7 @@ __device__ __forceinline__ void finish_split(const DecodeArgs& a, int k, bool be
     const int span = 1 << (kMergeFanLog2 * lv), cspan = span >> kMergeFanLog2;
     const int g0 = k0 + ((child - k0) >> (kMergeFanLog2 * lv) << (kMergeFanLog2 * lv));
     const int g1 = min(g0 + span - 1, k1);
-    const int expect = range_tiles<WPG>(g0, g1, s_u, e_u, T);
+    const int expect = range_tiles<WPG>(g0, g1, s_u, e_u, T, sh);
     if (expect == tiles) {  // the arriving subtree is the node's only child with tiles
       child = g0;
       continue;
@@ -510,7 +523,7 @@ __device__ __forceinline__ void finish_split(const DecodeArgs& a, int k, bool be
     int cslot = -1;
     {
       const int p = g0 + lane * cspan, q = min(p + cspan - 1, g1);
-      if (lane < (1 << kMergeFanLog2) && p <= g1 && (dense || range_tiles<WPG>(p, q, s_u, e_u, T) > 0))
+      if (lane < (1 << kMergeFanLog2) && p <= g1 && (dense || range_tiles<WPG>(p, q, s_u, e_u, T, sh) > 0))
         cslot = int(slot_of(lv == 1 ? p : first_with_tiles(p)));
     }
     const uint64_t has_child = __ballot(cslot >= 0);
@@ -673,14 +686,15 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
 
   const int Ptot = cum_s[B];
   const int64_t T = int64_t(Ptot) * Hkv * RGs;
-  const int k = blockIdx.x * kWaves + wave;  // the grid is kDecodeBlocks workgroups
-  zero_empty_units<D, NB, MODE>(a, Hkv * RGs * B, B, RGs, -1, k, kWaves * kDecodeBlocks,
+  const int k = blockIdx.x * kWaves + wave;  // the grid is a.plan.blocks workgroups
+  const Shares sh = call_shares(a);
+  zero_empty_units<D, NB, MODE>(a, Hkv * RGs * B, B, RGs, -1, k, sh.n,
                                 [&](int b) { return cum_s[b + 1] == cum_s[b]; }, lane);
   // Nothing outstanding before the ring starts.  (Without this wait the
   // compiler also waits for every outstanding load before a ring page's LDS
   // reads, on every page.)
   __builtin_amdgcn_s_waitcnt(0);
-  const int64_t tau0 = share_start<kWaves>(k, T), tau1 = share_start<kWaves>(k + 1, T);
+  const int64_t tau0 = share_start<kWaves>(k, T, sh), tau1 = share_start<kWaves>(k + 1, T, sh);
   if (tau0 >= tau1) return;  // no barriers follow
   const int n = int(tau1 - tau0);
 
@@ -850,9 +864,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int64_t T = int64_t(Ptot) * Hkv;
   const int k = blockIdx.x;  // the grid is one pair per share
   // each wave zeroes its own rows of units without tiles
-  zero_empty_units<D, NB, MODE>(a, Hkv * B, B, 1, rg, k, 1 << kDecodeShareLog2,
+  const Shares sh = call_shares(a);
+  zero_empty_units<D, NB, MODE>(a, Hkv * B, B, 1, rg, k, sh.n,
                                 [&](int u) { return cum(u + 1) == cum(u); }, lane);
-  const int64_t tau0 = share_start<1>(k, T), tau1 = share_start<1>(k + 1, T);
+  const int64_t tau0 = share_start<1>(k, T, sh), tau1 = share_start<1>(k + 1, T, sh);
   if (tau0 >= tau1) return;  // both waves alike: no barriers follow
   const int n = int(tau1 - tau0);
 
@@ -1166,7 +1181,7 @@ __global__ __launch_bounds__(1024) void decode_cascade_plan_kernel(DecodeArgs a,
 template <int D, int NB, int MODE, bool APPEND = false>
 hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
   constexpr int S = D == 128 ? KVS_RING_PAGES_D128 : 8;  // 32 KiB of ring per wave
-  hipLaunchKernelGGL((decode_stream_kernel<D, NB, S, MODE, APPEND>), dim3(kDecodeBlocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_stream_kernel<D, NB, S, MODE, APPEND>), dim3(a.plan.blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1180,7 +1195,7 @@ hipError_t launch_decode_cascade(const DecodeArgs& a, hipStream_t stream) {
                      a.plan.rows / (a.num_decoders * G));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_pair_kernel<D, S>), dim3(1 << kDecodeShareLog2), dim3(128), 0, stream, a);
+  hipLaunchKernelGGL((decode_pair_kernel<D, S>), dim3(4 * a.plan.blocks), dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 

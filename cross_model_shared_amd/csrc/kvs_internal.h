@@ -44,12 +44,15 @@ struct DecodePlan {
   int nb;         // 16-row column blocks per wave (1, 2 or 4)
   int rg_rows;    // 16 * nb
   int rowgroups;  // ceil(rows / rg_rows)
-  int blocks;     // workgroups of the persistent grid (one per CU)
+  int blocks;     // 4-wave workgroups of the persistent grid: a multiple of 8, 8 .. kDecodeBlocks
+  int share_even; // stream-K weight of a share on an even XCD (odd XCDs: 512 - share_even)
+  int share_mult; // floor(2^26 / (4 * blocks)): scales the share weights to a whole of 2^18
   size_t cum_offset, units_offset, ml_offset, acc_offset, bytes;
 };
 
-// Persistent decode grid: one 4-wave workgroup per CU of an MI355X (256 CUs),
-// so 1024 = 2^10 stream-K shares (waves, or wave pairs in the cascade).
+// Persistent decode grid: one 4-wave workgroup per CU, at most 256 (an
+// MI355X), so at most 1024 = 2^10 stream-K shares (waves, or wave pairs in the
+// cascade).  The workspace is sized for the maximum, whatever the device.
 constexpr int kDecodeBlocks = 256;
 constexpr int kDecodeShareLog2 = 10;
 static_assert(kDecodeBlocks * 4 == 1 << kDecodeShareLog2, "share count");

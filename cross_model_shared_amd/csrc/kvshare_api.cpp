@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <string>
@@ -108,7 +109,20 @@ DecodePlan plan_decode(int batch, int num_decoders, int num_q_heads, int num_kv_
   p.nb = p.rows <= 16 ? 1 : (p.rows <= 32 ? 2 : 4);
   p.rg_rows = 16 * p.nb;
   p.rowgroups = (p.rows + p.rg_rows - 1) / p.rg_rows;
-  p.blocks = kDecodeBlocks;
+  // One workgroup per CU, in whole rounds of 8 so that every XCD holds the same
+  // number of workgroups.  On a 256-CU part the shares on even XCDs weigh 276 and
+  // those on odd XCDs 236 (the odd XCDs stream KV pages slower there); any other
+  // grid gets equal weights.  KVS_DECODE_WORKGROUPS and KVS_DECODE_SHARE_EVEN,
+  // read at every call, override both (clamped to their ranges): they let the
+  // tests run the general share arithmetic on any device.
+  const int cus = device_cu_count();
+  p.blocks = std::min(kDecodeBlocks, std::max(8, cus / 8 * 8));
+  if (const char* e = std::getenv("KVS_DECODE_WORKGROUPS"))
+    p.blocks = std::min(kDecodeBlocks, std::max(8, std::atoi(e) / 8 * 8));
+  p.share_even = (p.blocks == 256 && cus == 256) ? 276 : 256;
+  if (const char* e = std::getenv("KVS_DECODE_SHARE_EVEN"))
+    p.share_even = std::min(511, std::max(1, std::atoi(e)));
+  p.share_mult = (1 << 26) / (4 * p.blocks);
   // arrival counters first, at a fixed size, so that every call on a workspace
   // finds them in the same place; then the cascade tables and the partial-state
   // slots, sized for 64-row groups, so one workspace serves every decode call
