@@ -701,15 +701,16 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
   const int num_pages = a.pool.num_pages;
   uint32_t bad = 0;  // ring slots whose page id was out of range
 
-  // decoder of each of the lane's rows (private mode: one row group per KV head)
-  int row_owner[NB];
+  // private mode: the unit's row (within its KV head) of the lane's row in
+  // column block 0 (column block cb adds 16 cb); decoder n holds rows nG .. nG+G-1
+  int row_base = 0;
   const int G = a.num_q_heads / Hkv;
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb) row_owner[cb] = (cb * 16 + (lane & 15)) / G;
+  auto set_owners = [&](int rg) { row_base = rg * 16 * NB + (lane & 15); };
 
   const LdsCum cum{cum_s};
   Walker iw = seek<MODE>(a, cum, B, Ptot, tau0);
   Walker cw = iw;
+  if (MODE == kPrivate) set_owners(cw.gr % RGs);
   auto issue = [&](int slot) {
     const int g = iw.gr / RGs;
     int pid = page_id<MODE>(a, iw);
@@ -792,10 +793,13 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
       int lim[NB], nvalid;
       bool masked;
       if (MODE == kPrivate && cw.page >= cw.nsh) {
-        // a private page of decoder pn: only its rows see it
+        // a private page of decoder pn: only its rows see it (with several row
+        // groups every row group walks all private pages of the session, and a
+        // group holding no row of decoder pn masks the whole page)
         nvalid = min(kPage, cw.plen - cw.pp * kPage);
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) lim[cb] = (row_owner[cb] == cw.pn) ? nvalid : 0;
+        for (int cb = 0; cb < NB; ++cb)
+          lim[cb] = uint32_t(row_base + cb * 16 - cw.pn * G) < uint32_t(G) ? nvalid : 0;
         masked = true;
       } else {
         const int L = seq_len(a, cw.b);
@@ -827,6 +831,7 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
         st.init();
         load_q<D, NB, MODE>(qf, al, cw.b, cw.gr / RGs, cw.gr % RGs, lane);
         load_new(cw.b, cw.gr / RGs);
+        if (MODE == kPrivate) set_owners(cw.gr % RGs);
         unit_begin = int64_t(cw.gr) * Ptot + cum_s[cw.b];
       }
       // Stores (their data registers), merge loads and q loads drained before

@@ -213,13 +213,14 @@ int decode_common(const char* name, const kvs_pool* pool, int32_t layer, const v
     return fail(KVS_EUNSUPPORTED, "%s: batch %d above %d", name, batch, kvs::kDecodeMaxBatch);
   kvs::DecodePlan plan = kvs::plan_decode(batch, num_decoders, num_q_heads, pool->num_kv_heads,
                                           pool->head_dim, max_seq_len);
+  // A cascade unit holds as many whole sessions as fit 64 rows, split into two
+  // 32-row groups, one per wave of a pair.  With more than 64 rows per session a
+  // unit would hold one session, whose pages plain decode reads the same way
+  // (once for all its rows, in 64-row groups): such calls run plain decode over
+  // the same block tables, and group_id / group_prefix_pages are not read.
+  if (group_id && num_decoders * (num_q_heads / pool->num_kv_heads) > 64) group_id = group_prefix = nullptr;
   if (group_id) {
-    // a unit holds as many whole sessions as fit 64 rows (at least one), split
-    // into two 32-row groups, one per wave of a pair
     const int ng = num_decoders * (num_q_heads / pool->num_kv_heads);
-    if (ng > 64)
-      return fail(KVS_EUNSUPPORTED, "%s: %d query rows per KV head and session (num_decoders * group) above 64",
-                  name, ng);
     const int per_unit = 64 / ng;
     kvs::DecodePlan full = kvs::plan_decode(batch, per_unit * num_decoders, num_q_heads, pool->num_kv_heads,
                                             pool->head_dim, max_seq_len);
@@ -239,9 +240,6 @@ int decode_common(const char* name, const kvs_pool* pool, int32_t layer, const v
     if (int64_t(max_priv_len) > int64_t(pbt_stride) * 16)
       return fail(KVS_ERANGE, "%s: max_priv_len %d exceeds private block-table capacity %lld", name,
                   max_priv_len, (long long)pbt_stride * 16);
-    if (plan.rowgroups != 1)
-      return fail(KVS_EUNSUPPORTED, "%s: %d query rows per KV head (num_decoders * group) above 64", name,
-                  plan.rows);
   }
   if (!workspace || workspace_bytes < plan.bytes)
     return fail(KVS_EWORKSPACE, "%s: workspace %zu bytes < required %zu", name,

@@ -276,9 +276,12 @@ int shared_kv_decode_append(const kvs_pool* pool, int32_t layer, const void* k_n
  *                    kv_pool_append using this table, row b*N + n as a session).
  *  priv_lens         int32 [batch*num_decoders], private tokens per decoder.
  *  max_priv_len      host bound on priv_lens entries, <= priv_bt_stride * 16.
- *  Other arguments as for shared_kv_decode (same workspace size).  Needs
- *  num_decoders * (num_q_heads / num_kv_heads) <= 64 (all rows of a KV head in
- *  one wave); larger row counts return KVS_EUNSUPPORTED.
+ *  Other arguments as for shared_kv_decode (same workspace size).  Up to 64
+ *  query rows per KV head (num_decoders * num_q_heads / num_kv_heads) one wave
+ *  holds them all and every private page is read once.  Above 64 the rows run
+ *  in 64-row groups, as in shared_kv_decode: each group reads the shared pages
+ *  and the session's private pages, and attends the private pages of the
+ *  decoders whose rows it holds.
  */
 int shared_kv_decode_private(const kvs_pool* pool, int32_t layer, const void* q, void* out,
                              const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
@@ -310,8 +313,11 @@ int shared_kv_decode_private(const kvs_pool* pool, int32_t layer, const void* q,
  *                session's, is reported (KVS_DEV_BAD_LEN / KVS_DEV_BAD_PAGE);
  *                the prefix pages read are always the first session's.  The
  *                prefix is also cut to whole pages every member holds.
- *  Needs num_decoders * (num_q_heads / num_kv_heads) <= 64.  Other arguments
- *  and the workspace as for shared_kv_decode.
+ *  Other arguments and the workspace as for shared_kv_decode.  With more than
+ *  64 query rows per session (num_decoders * num_q_heads / num_kv_heads) a unit
+ *  would hold one session and share nothing: the call then runs shared_kv_decode
+ *  over the same block tables (same result, bit for bit), and group_id and
+ *  group_prefix_pages are not read.
  *
  * The units are planned by a first kernel into the workspace, with a 64-bit
  * fingerprint of what they depend on (batch, sessions per unit, max_seq_len,

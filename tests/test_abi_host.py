@@ -144,7 +144,7 @@ def call_decode_private(L, p, q=FAKE, bt=FAKE, pbt=FAKE, pstride=2, plens=FAKE, 
     (dict(p=pool(), pstride=0), binding.KVS_EINVAL),
     (dict(p=pool(), mpl=-1), binding.KVS_EINVAL),
     (dict(p=pool(), mpl=33), binding.KVS_ERANGE),            # > priv_bt_stride * 16
-    (dict(p=pool(), N=17), binding.KVS_EUNSUPPORTED),        # 17 * 4 rows per KV head > 64
+    (dict(p=pool(), N=17, wsb=16), binding.KVS_EWORKSPACE),  # 68 rows per KV head: accepted (row groups)
     (dict(p=pool(), msl=65), binding.KVS_ERANGE),
     (dict(p=pool(), wsb=16), binding.KVS_EWORKSPACE),
 ])
@@ -157,7 +157,7 @@ def test_decode_private_host_checks(L, kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(gid=None), binding.KVS_EINVAL),
     (dict(pref=None), binding.KVS_EINVAL),
-    (dict(N=17), binding.KVS_EUNSUPPORTED),           # 17 decoders x 4 heads per KV head > 64 rows
+    (dict(N=17, wsb=16), binding.KVS_EWORKSPACE),     # 68 rows per session: accepted (plain decode)
     (dict(msl=65), binding.KVS_ERANGE),
     (dict(wsb=16), binding.KVS_EWORKSPACE),
 ])

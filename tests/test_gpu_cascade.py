@@ -106,6 +106,23 @@ def test_no_groups_is_shared_decode():
     assert float(np.max(np.abs(casc - want))) <= TOL
 
 
+def test_cascade_above_64_rows_per_session_is_shared_decode():
+    """With more than 64 query rows per session a unit would hold one session:
+    the call runs the plain decode over the same tables, bit for bit, and the
+    group arguments are not read."""
+    groups = [(64, [100, 80, 90]), (0, [33])]
+    c = make_case(groups, 12, 1, 8, 128, seed=74)      # 96 rows per session
+    casc = gu.host_bits(run_cascade(c))
+    plain = gu.host_bits(gu.run_decode(c, q_bits=c["q"], lens=c["lens"], bt=c["bt"]))
+    assert np.array_equal(casc, plain)
+    want = oracle.decode_from_logical(c["q"], c["K"], c["V"], 1.0 / math.sqrt(128))
+    assert float(np.max(np.abs(gu.host_f64(run_cascade(c)) - want))) <= TOL
+    pref = c["pref"].copy()
+    pref[1] = 2                                        # inconsistent, and not read
+    run_cascade(c, pref=pref)
+    assert int(c["status"].item()) == 0
+
+
 def test_cascade_reports_inconsistent_groups_without_faulting():
     groups = [(64, [100, 80, 90])]
     c = make_case(groups, 8, 2, 4, 128, seed=73)

@@ -61,6 +61,33 @@ def test_private_decode_matches_oracle(lens, N, G, D, pmax):
     assert int(case["status"].item()) == 0
 
 
+@pytest.mark.parametrize("lens,N,G,D,pmax", [
+    ([300, 17, 900], 16, 8, 128, 60),    # 128 rows per KV head: two 64-row groups
+    ([555, 0, 130], 20, 4, 64, 40),      # 80 rows: a full and a partial row group
+    ([1000, 48], 5, 16, 128, 200),       # 80 rows, decoder 4 split over both row groups
+])
+def test_private_decode_above_64_rows_matches_oracle(lens, N, G, D, pmax):
+    """More than 64 query rows per KV head run in 64-row groups; each group walks
+    the session's private pages and attends those of its own decoders."""
+    rng = np.random.default_rng(len(lens) * 1000 + N * G + D)
+    priv = [int(x) for x in rng.integers(0, pmax, size=len(lens) * N, endpoint=True)]
+    priv[1] = 0
+    print(f"[private>64] lens={lens} N={N} G={G} D={D}", flush=True)
+    case = gu.make_private_case(lens, priv, N, 1, G, D, seed=N * G + D)
+    out = gu.run_decode_private(case)
+    want = oracle_from_logical(case)
+    err = float(np.max(np.abs(gu.host_f64(out) - want)))
+    print(f"[private>64] max-abs err {err:.3e}", flush=True)
+    assert err <= TOL
+    assert int(case["status"].item()) == 0
+    # without suffixes it is the plain decode, bit for bit
+    nopriv = [0] * len(priv)
+    a = gu.host_bits(gu.run_decode_private(case, priv=nopriv, max_priv_len=0))
+    b = gu.host_bits(gu.run_decode(dict(pool=case["pool"], Hkv=1, layer=0, status=case["status"]),
+                                   q_bits=case["q"], lens=lens, bt=case["bt"]))
+    assert np.array_equal(a, b)
+
+
 def test_private_decode_pool_path_matches_oracle_pool_path():
     """The oracle's own pool walk (both block tables) on the pool the GPU built."""
     lens, priv, N = [45, 210], [3, 0, 17, 64], 2
