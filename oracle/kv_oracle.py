@@ -137,6 +137,49 @@ def append(pool: np.ndarray, shape: PoolShape, layer: int, k_new: np.ndarray, v_
     return out
 
 
+def append_aliasing(block_table: np.ndarray, seq_lens, cu_new, num_pages: int, max_new: int,
+                    max_seq_len: int) -> bool:
+    """True when an append would write one physical slot for two logical slots.
+
+    Pages hold a session's positions in blocks (PrefillShare, section 3.3), and
+    full, block-aligned prefix blocks may be mapped into several sessions' tables
+    (Prefill-as-a-Service, component 3), so one physical slot may be *live* for
+    several sessions: that is sharing, not a fault.  A write is a fault when the
+    physical slot (page, slot) of a new token of the call
+      - is also the slot of another new token of the call, or
+      - holds a live token of a session of the batch: position q < seq_lens[c]
+        of any session c (the writing session included).
+    Slots whose page id lies outside [0, num_pages), and sessions whose lengths
+    the append rejects, write nothing and are left out, as the append leaves them.
+    """
+    B = len(seq_lens)
+    live = set()
+    for c in range(B):
+        L = int(seq_lens[c])
+        if L < 0 or L > max_seq_len:
+            continue
+        for q in range(L):
+            page = int(block_table[c, q // PAGE])
+            if 0 <= page < num_pages:
+                live.add((page, q % PAGE))
+    written = set()
+    total_new = int(cu_new[B])
+    for b in range(B):
+        P, c0, c1 = int(seq_lens[b]), int(cu_new[b]), int(cu_new[b + 1])
+        n = c1 - c0
+        if P < 0 or n < 0 or n > max_new or P + n > max_seq_len or c0 < 0 or c1 > total_new:
+            continue
+        for p in range(P, P + n):
+            page = int(block_table[b, p // PAGE])
+            if not 0 <= page < num_pages:
+                continue
+            key = (page, p % PAGE)
+            if key in written or key in live:
+                return True
+            written.add(key)
+    return False
+
+
 # ---------------------------------------------------------------------------
 # Gather a session's logical K/V from its pages
 # ---------------------------------------------------------------------------
