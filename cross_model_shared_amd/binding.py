@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvshare.so")
 
 KVS_OK, KVS_EINVAL, KVS_ERANGE, KVS_EWORKSPACE, KVS_EUNSUPPORTED, KVS_EHIP, KVS_ENOSPACE = 0, -1, -2, -3, -4, -5, -6
-DEV_BAD_PAGE, DEV_BAD_LEN = 1, 2
+DEV_BAD_PAGE, DEV_BAD_LEN, DEV_ALIAS = 1, 2, 4
 PAGE = 16
 
 
@@ -37,6 +37,9 @@ _SIGNATURES = {
     "kvs_pool_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "kv_pool_append": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                       _i32, _vp, _vp]),
+    "kv_pool_append_check_bytes": (_sz, [_i32]),
+    "kv_pool_append_check": (ctypes.c_int, [_pool_p, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp,
+                                            _vp]),
     "shared_kv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "shared_kv_decode_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
     "shared_kv_decode": (ctypes.c_int, [_pool_p, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
@@ -171,6 +174,23 @@ def append(pool: Pool, layer, k_new, v_new, cu_new, block_table, seq_lens, max_n
         _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
         _ptr(seq_lens, "seq_lens", torch.int32), batch, total, max_new, max_seq_len,
         _ptr(dev_status, "dev_status", torch.int32, 1, allow_none=True), _stream(stream)))
+
+
+def append_check(pool: Pool, cu_new, block_table, seq_lens, total_new, max_new, max_seq_len, scratch,
+                 dev_status, stream=None):
+    """kv_pool_append_check: OR KVS_DEV_ALIAS into dev_status when the append with these
+    arguments would write one physical slot for two logical slots."""
+    torch = _torch()
+    batch = seq_lens.numel()
+    _check(load().kv_pool_append_check(
+        pool.struct, _ptr(cu_new, "cu_new", torch.int32, batch + 1), _ptr(block_table, "block_table", torch.int32),
+        block_table.shape[1], _ptr(seq_lens, "seq_lens", torch.int32), batch, total_new, max_new, max_seq_len,
+        _ptr(scratch, "scratch"), scratch.numel() * scratch.element_size(),
+        _ptr(dev_status, "dev_status", torch.int32, 1), _stream(stream)))
+
+
+def append_check_bytes(num_pages) -> int:
+    return load().kv_pool_append_check_bytes(num_pages)
 
 
 def decode_workspace_bytes(batch, num_decoders, num_q_heads, num_kv_heads, head_dim, max_seq_len) -> int:

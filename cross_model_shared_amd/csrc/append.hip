@@ -7,6 +7,8 @@
 // tile is stored with 8 slots of one head-dim value side by side, so a thread
 // gathers those 8 slots and writes them as one 16-byte run when all 8 are new,
 // and slot by slot otherwise (slots not being appended are never touched).
+#include <algorithm>
+
 #include "kvs_device.h"
 #include "kvs_internal.h"
 
@@ -101,7 +103,72 @@ hipError_t launch_append_t(const AppendArgs& a, hipStream_t stream) {
   return hipSuccess;
 }
 
+// ---- kv_pool_append_check: the append's write-aliasing rule ----------------
+//
+// One 32-bit word per physical page: bit s is set when a new token of the call
+// goes to slot s, bit 16 + s when slot s holds a live token of a session of the
+// batch (a position below its seq_lens).  A first kernel marks every live slot;
+// a second marks every new token's slot with an atomic OR and reports aliasing
+// when the slot's word already had either bit: a second new token, or a live
+// token (sessions may share full prefix pages, so live-live is allowed).  The
+// kernels are separate launches on one stream, so every live bit is in before
+// the first new token looks.  Work is a grid-stride loop over (session, page).
+
+constexpr int kAliasThreads = 256, kAliasMaxBlocks = 4096;
+
+__device__ __forceinline__ uint32_t slot_bits(int lo, int hi) {  // slots lo .. hi-1 of a page
+  return ((hi >= 32 ? 0u : (1u << hi)) - 1u) & ~((1u << lo) - 1u);
+}
+
+__global__ __launch_bounds__(kAliasThreads) void alias_live_kernel(AliasArgs a, int pages_per_session) {
+  const int64_t total = int64_t(a.batch) * pages_per_session;
+  for (int64_t i = int64_t(blockIdx.x) * kAliasThreads + threadIdx.x; i < total;
+       i += int64_t(gridDim.x) * kAliasThreads) {
+    const int b = int(i / pages_per_session), pi = int(i % pages_per_session);
+    const int L = a.seq_lens[b];
+    if (L < 0 || L > a.max_seq_len || pi * kPage >= L) continue;
+    const int pid = a.bt[int64_t(b) * a.bt_stride + pi];
+    if (pid < 0 || pid >= a.num_pages) continue;
+    atomicOr(a.words + pid, slot_bits(0, min(kPage, L - pi * kPage)) << 16);
+  }
+}
+
+__global__ __launch_bounds__(kAliasThreads) void alias_new_kernel(AliasArgs a, int windows) {
+  const int64_t total = int64_t(a.batch) * windows;
+  for (int64_t i = int64_t(blockIdx.x) * kAliasThreads + threadIdx.x; i < total;
+       i += int64_t(gridDim.x) * kAliasThreads) {
+    const int b = int(i / windows), w = int(i % windows);
+    const int P = a.seq_lens[b], c0 = a.cu_new[b], c1 = a.cu_new[b + 1], n = c1 - c0;
+    // lengths the append rejects write nothing (the append reports them)
+    if (P < 0 || n <= 0 || n > a.max_new || P + n > a.max_seq_len || c0 < 0 || c1 > a.total_new) continue;
+    const int lp = P / kPage + w;
+    const int t0 = max(lp * kPage, P), t1 = min(lp * kPage + kPage, P + n);
+    if (t0 >= t1) continue;
+    const int pid = a.bt[int64_t(b) * a.bt_stride + lp];
+    if (pid < 0 || pid >= a.num_pages) continue;
+    const uint32_t mine = slot_bits(t0 - lp * kPage, t1 - lp * kPage);
+    const uint32_t old = atomicOr(a.words + pid, mine);
+    if ((old & mine) || ((old >> 16) & mine)) flag_error(a.dev_status, KVS_DEV_ALIAS_BIT);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append_check(const AliasArgs& a, hipStream_t stream) {
+  hipError_t e = launch_zero(a.words, size_t(a.num_pages) * 4, stream);
+  if (e != hipSuccess) return e;
+  const int pages = (a.max_seq_len + kPage - 1) / kPage;
+  const int windows = (a.max_new + 2 * kPage - 2) / kPage;
+  auto blocks = [](int64_t work) {
+    return unsigned(std::min<int64_t>(kAliasMaxBlocks, std::max<int64_t>(1, (work + kAliasThreads - 1) / kAliasThreads)));
+  };
+  hipLaunchKernelGGL(alias_live_kernel, dim3(blocks(int64_t(a.batch) * pages)), dim3(kAliasThreads), 0, stream, a,
+                     pages);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(alias_new_kernel, dim3(blocks(int64_t(a.batch) * windows)), dim3(kAliasThreads), 0, stream, a,
+                     windows);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   if (a.pool.head_dim == 128) return launch_append_t<128>(a, stream);

@@ -21,6 +21,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // bits OR-ed into the caller's device status word (values of the C ABI enum)
 constexpr int KVS_DEV_BAD_PAGE_BIT = 1;
 constexpr int KVS_DEV_BAD_LEN_BIT = 2;
+constexpr int KVS_DEV_ALIAS_BIT = 4;
 
 // Element offset of the (layer, page, head) tile: K part (16*D) then V part (16*D).
 __device__ __forceinline__ int64_t tile_offset(int layer, int page, int head, int num_pages,

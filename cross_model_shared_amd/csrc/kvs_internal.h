@@ -167,7 +167,19 @@ struct FetchArgs {
   int32_t* dev_status;
 };
 
+// kv_pool_append_check: the append's destinations, and one scratch word per page
+struct AliasArgs {
+  const int32_t* cu_new;
+  const int32_t* bt;
+  int bt_stride;
+  const int32_t* seq_lens;
+  int batch, total_new, max_new, max_seq_len, num_pages;
+  uint32_t* words;
+  int32_t* dev_status;
+};
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_append_check(const AliasArgs& a, hipStream_t stream);
 hipError_t launch_pack(const HandoffArgs& a, bool unpack, hipStream_t stream);
 hipError_t launch_fetch(const FetchArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -170,6 +170,31 @@ int kv_pool_append(const kvs_pool* pool, int32_t layer, const void* k_new, const
   return launched(kvs::launch_append(a, stream), "kv_pool_append");
 }
 
+size_t kv_pool_append_check_bytes(int32_t num_pages) { return num_pages > 0 ? size_t(num_pages) * 4 : 0; }
+
+int kv_pool_append_check(const kvs_pool* pool, const int32_t* cu_new, const int32_t* block_table,
+                         int32_t bt_stride, const int32_t* seq_lens, int32_t batch, int32_t total_new,
+                         int32_t max_new, int32_t max_seq_len, void* scratch, size_t scratch_bytes,
+                         int32_t* dev_status, hipStream_t stream) {
+  int s = check_pool(pool, 0);
+  if (s) return s;
+  if (!cu_new || !block_table || !seq_lens || !dev_status)
+    return fail(KVS_EINVAL, "kv_pool_append_check: a required pointer is NULL");
+  if ((s = check_table(batch, bt_stride, max_seq_len))) return s;
+  if (max_new <= 0 || total_new < 0)
+    return fail(KVS_EINVAL, "kv_pool_append_check: max_new %d must be >= 1, total_new %d >= 0", max_new,
+                total_new);
+  if (max_new > max_seq_len)
+    return fail(KVS_ERANGE, "kv_pool_append_check: max_new %d exceeds max_seq_len %d", max_new, max_seq_len);
+  const size_t need = kv_pool_append_check_bytes(pool->num_pages);
+  if (!scratch || scratch_bytes < need)
+    return fail(KVS_EWORKSPACE, "kv_pool_append_check: scratch %zu bytes < required %zu",
+                scratch ? scratch_bytes : size_t(0), need);
+  kvs::AliasArgs a{cu_new, block_table, bt_stride, seq_lens, batch, total_new, max_new, max_seq_len,
+                   pool->num_pages, static_cast<uint32_t*>(scratch), dev_status};
+  return launched(kvs::launch_append_check(a, stream), "kv_pool_append_check");
+}
+
 size_t shared_kv_decode_workspace_bytes(int32_t batch, int32_t num_decoders, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t max_seq_len) {

@@ -105,6 +105,7 @@ enum {
 enum {
   KVS_DEV_BAD_PAGE = 1,  /* block-table entry outside [0, num_pages)          */
   KVS_DEV_BAD_LEN = 2,   /* seq_lens / cu_new beyond the host-given bounds    */
+  KVS_DEV_ALIAS = 4,     /* (kv_pool_append_check) a write would alias a slot  */
 };
 
 typedef struct kvs_pool {
@@ -138,12 +139,46 @@ size_t kvs_pool_bytes(int32_t num_layers, int32_t num_pages, int32_t num_kv_head
  *  max_new       host bound on cu_new[b+1]-cu_new[b] (>= 1).
  *  max_seq_len   host bound on seq_lens[b] + new tokens of b (<= bt_stride*16).
  *  Only the destination slots are written; every other pool byte is unchanged.
- *  Two new rows must never map to the same physical slot (caller's duty).
+ *  Two new rows must never map to the same physical slot (caller's duty;
+ *  kv_pool_append_check verifies it in debug runs).
  */
 int kv_pool_append(const kvs_pool* pool, int32_t layer, const void* k_new, const void* v_new,
                    const int32_t* cu_new, const int32_t* block_table, int32_t bt_stride,
                    const int32_t* seq_lens, int32_t batch, int32_t total_new, int32_t max_new,
                    int32_t max_seq_len, int32_t* dev_status, hipStream_t stream);
+
+/* Scratch bytes kv_pool_append_check needs for a pool of num_pages pages
+ * (4 per page; 0 if num_pages <= 0). */
+size_t kv_pool_append_check_bytes(int32_t num_pages);
+
+/*
+ * kv_pool_append_check — debug check of a kv_pool_append call's destinations,
+ * made with the same arguments before the call (the K/V rows are not needed).
+ *
+ * Pages hold a session's positions in blocks (PrefillShare, section 3.3) and
+ * full, block-aligned prefix blocks may sit in several sessions' tables
+ * (Prefill-as-a-Service, component 3): a physical slot may be live for several
+ * sessions, and reading it through each is sharing.  A write aliases when the
+ * physical slot (page, slot) of a new token of the call
+ *   - is also the slot of another new token of the call, or
+ *   - holds a live token of a session of the batch (position q < seq_lens[c]
+ *     of some session c, the writing session included);
+ * then KVS_DEV_ALIAS is OR-ed into *dev_status.  Sessions outside the batch are
+ * not known to the call.  Slots that kv_pool_append would not write (page ids
+ * out of range, lengths it rejects) are left out; the append reports those.
+ *
+ *  scratch       device buffer of kv_pool_append_check_bytes(pool->num_pages)
+ *                bytes, cleared by the call with a fill kernel on `stream`
+ *                (KVS_EWORKSPACE when smaller or NULL); its contents after the
+ *                call are unspecified.
+ *  dev_status    required (KVS_EINVAL when NULL).
+ *  Other arguments and host checks as for kv_pool_append (the pool's layers are
+ *  not read).
+ */
+int kv_pool_append_check(const kvs_pool* pool, const int32_t* cu_new, const int32_t* block_table,
+                         int32_t bt_stride, const int32_t* seq_lens, int32_t batch, int32_t total_new,
+                         int32_t max_new, int32_t max_seq_len, void* scratch, size_t scratch_bytes,
+                         int32_t* dev_status, hipStream_t stream);
 
 /* Workspace bytes needed by shared_kv_decode, shared_kv_decode_append,
  * shared_kv_decode_private and shared_kv_decode_cascade for these bounds. */
@@ -153,8 +188,8 @@ size_t shared_kv_decode_workspace_bytes(int32_t batch, int32_t num_decoders, int
 
 /*
  * shared_kv_decode_workspace_init — make a decode workspace ready for its first
- * call: zero its arrival counters (the first 8 KiB) with a fill kernel on
- * `stream`.  A workspace whose first 8 KiB are already zero (e.g. allocated
+ * call: zero its arrival counters (the first 64 KiB) with a fill kernel on
+ * `stream`.  A workspace whose first 64 KiB are already zero (e.g. allocated
  * zero-filled) needs no init.
  *
  * A decode call splits work on one unit (session, KV head) between several
@@ -162,7 +197,7 @@ size_t shared_kv_decode_workspace_bytes(int32_t batch, int32_t num_decoders, int
  * found through a counter that every call leaves at zero again.  So a
  * workspace needs this once, not per call, as long as only decode calls write
  * it.  The rest of the workspace needs no init.
- *  workspace        device buffer, >= 8 KiB (KVS_EWORKSPACE otherwise).
+ *  workspace        device buffer, >= 64 KiB (KVS_EWORKSPACE otherwise).
  */
 int shared_kv_decode_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -185,7 +220,7 @@ int shared_kv_decode_workspace_init(void* workspace, size_t workspace_bytes, hip
  *  max_seq_len   host bound on seq_lens[b]; sizes the launch.
  *  scale         softmax scale (1/sqrt(head_dim) for the usual attention).
  *  workspace     device buffer of >= shared_kv_decode_workspace_bytes(...)
- *                bytes.  Its first 8 KiB (arrival counters) must be zero when
+ *                bytes.  Its first 64 KiB (arrival counters) must be zero when
  *                the call starts: zero the buffer once, or call
  *                shared_kv_decode_workspace_init once; every call leaves them
  *                zero.  The rest of its contents on entry are ignored (every

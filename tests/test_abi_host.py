@@ -192,6 +192,33 @@ def test_append_host_checks(L, kw, status):
     assert call_append(L, p, **kw) == status
 
 
+def call_append_check(L, p, cu=FAKE, bt=FAKE, stride=4, lens=FAKE, batch=2, total=10, max_new=8, msl=64,
+                      scratch=FAKE, sbytes=1 << 20, status=FAKE):
+    return L.kv_pool_append_check(ctypes.byref(p), cu, bt, stride, lens, batch, total, max_new, msl, scratch,
+                                  sbytes, status, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=pool(page=8)), binding.KVS_EUNSUPPORTED),
+    (dict(p=pool(), cu=None), binding.KVS_EINVAL),
+    (dict(p=pool(), status=None), binding.KVS_EINVAL),       # the check reports through dev_status only
+    (dict(p=pool(), max_new=0), binding.KVS_EINVAL),
+    (dict(p=pool(), max_new=65), binding.KVS_ERANGE),
+    (dict(p=pool(), msl=100), binding.KVS_ERANGE),
+    (dict(p=pool(), scratch=None), binding.KVS_EWORKSPACE),
+    (dict(p=pool(pages=8), sbytes=31), binding.KVS_EWORKSPACE),  # 4 bytes per page
+])
+def test_append_check_host_checks(L, kw, status):
+    p = kw.pop("p")
+    assert call_append_check(L, p, **kw) == status
+    assert binding.last_error()
+
+
+def test_append_check_bytes(L):
+    assert L.kv_pool_append_check_bytes(8) == 32
+    assert L.kv_pool_append_check_bytes(0) == 0
+
+
 def call_extend(L, p, q=FAKE, k=FAKE, v=FAKE, out=FAKE, cu=FAKE, bt=FAKE, stride=4, lens=FAKE, batch=2,
                 Hq=8, total=10, max_new=8, msl=64, scale=0.125):
     return L.partial_prefill_extend(ctypes.byref(p), 0, q, k, v, out, cu, bt, stride, lens, batch, Hq, total,
