@@ -642,6 +642,8 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
   const int B = a.batch;
 
   // ---- pages per session and their exclusive prefix sum (every workgroup) ----
+  // Each thread counts the pages of a run of sessions into cum_s, then turns its
+  // run into an exclusive prefix sum in place once the runs' totals are scanned.
   const int chunk = (B + 255) / 256;
   int local = 0;
   for (int i = 0; i < chunk; ++i) {
@@ -649,8 +651,10 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
     if (b < B) {
       const int L = a.seq_lens[b];
       if ((L < 0 || L > a.max_seq_len) && blockIdx.x == 0) flag_error(a.dev_status, KVS_DEV_BAD_LEN_BIT);
-      local += (clamp_len(L, a.max_seq_len) + kPage - 1) / kPage;
-      if (MODE == kPrivate) local += priv_pages(a, b);
+      int pages = (clamp_len(L, a.max_seq_len) + kPage - 1) / kPage;
+      if (MODE == kPrivate) pages += priv_pages(a, b);
+      cum_s[b] = pages;
+      local += pages;
     }
   }
   part_s[tid] = local;
@@ -675,9 +679,9 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
     for (int i = 0; i < chunk; ++i) {
       const int b = tid * chunk + i;
       if (b < B) {
+        const int pages = cum_s[b];
         cum_s[b] = run;
-        run += (clamp_len(a.seq_lens[b], a.max_seq_len) + kPage - 1) / kPage;
-        if (MODE == kPrivate) run += priv_pages(a, b);
+        run += pages;
       }
     }
     if (tid == 255) cum_s[B] = run;
@@ -752,9 +756,13 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
     }
   };
 
-  // Queries (and the step's token) are waited for before the ring starts: any
-  // non-DMA load still outstanding when the first page's DMA is issued makes
-  // the compiler wait for every outstanding load before each page's LDS reads.
+  // The first ring pages are issued before the queries (and the step's token)
+  // are loaded, so that the two latencies overlap.  Both are waited for before
+  // the page loop (vector-memory loads complete in order): any non-DMA load
+  // still outstanding at the loop makes the compiler wait for every outstanding
+  // load before each page's LDS reads.
+#pragma unroll 1
+  for (int j = 0; j < S - 1 && j < n; ++j) issue(j);
   QFrag<D, NB> qf;
   RowState<D, NB> st;
   st.init();
@@ -762,9 +770,6 @@ __global__ __launch_bounds__(256, 1) void decode_stream_kernel(DecodeArgs a) {
   load_new(cw.b, cw.gr / RGs);
   __builtin_amdgcn_s_waitcnt(0);
   int64_t unit_begin = int64_t(cw.gr) * Ptot + cum_s[cw.b];  // first tile of the current unit
-
-#pragma unroll 1
-  for (int j = 0; j < S - 1 && j < n; ++j) issue(j);
 
 #pragma unroll 1
   for (int j = 0; j < n; ++j) {
