@@ -228,6 +228,15 @@ int shared_kv_decode_workspace_init(void* workspace, size_t workspace_bytes, hip
  *                a workspace may be reused by later decode calls on the same
  *                stream, whatever their shapes; calls that overlap in time must
  *                use different workspaces.
+ *
+ * Launch plan: one 4-wave workgroup per CU of the current device (its CU count
+ * rounded down to a multiple of 8, at most 256), each wave streaming one
+ * contiguous share of the (KV head, session, page) list; on a 256-CU part the
+ * shares on even XCDs are 276/236 the size of those on odd ones.  The result
+ * depends on the split only through rounding, and for one plan it is the same
+ * bits on every call.  Testing hooks, read at every call: KVS_DECODE_WORKGROUPS
+ * sets the workgroup count (rounded down to a multiple of 8, in 8 .. 256) and
+ * KVS_DECODE_SHARE_EVEN the even-XCD weight (1 .. 511, of 512 per XCD pair).
  */
 int shared_kv_decode(const kvs_pool* pool, int32_t layer, const void* q, void* out,
                      const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
