@@ -911,15 +911,16 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void d
     advance<MODE>(a, iw, cum, B);
   };
 
+  // the first ring pages before the queries, so that the two latencies overlap
+  // (both are waited for before the page loop, as in the stream kernel)
+#pragma unroll 1
+  for (int j = 0; j < S - 1 && j < n; ++j) issue(j);
   QFrag<D, NB> qf;
   RowState<D, NB> st;
   st.init();
   load_q<D, NB, MODE>(qf, a, cw.b, cw.gr, rg, lane);
   __builtin_amdgcn_s_waitcnt(0);
   int64_t unit_begin = int64_t(cw.gr) * Ptot + cum(cw.b);  // first tile of the current unit
-
-#pragma unroll 1
-  for (int j = 0; j < S - 1 && j < n; ++j) issue(j);
 
 #pragma unroll 1
   for (int j = 0; j < n; ++j) {
