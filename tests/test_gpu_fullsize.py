@@ -217,6 +217,61 @@ def test_extend_full_size_sampled():
     check_tiles(pool, bt, 0, picks[-1], kf, vf, Hkv, D)  # prefix + appended chunk of the last pick
 
 
+def test_layer_group_full_size_sampled():
+    """partial_prefill_layers at the bench's size and launch (layers [12, 16) of a 32-layer pool,
+    8 prompts of 4096 tokens, no cached prefix; paired causal row blocks): in every layer one of two
+    sampled prompts, its first, last and two tokens (the block's last and a seeded one) of every
+    workgroup's 128-row block, all heads, against the oracle; plus that prompt's appended tiles.""" 
+    import torch
+
+    wl = W.make_workload("llama8b_layer_group")
+    B, Hq, Hkv, D = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    lb, nl = wl.layer_group
+    full = wl.total_lens()
+    print(f"[fullsize] layer group: B={B} new={wl.new[0]} layers [{lb}, {lb + nl}) of {wl.num_layers}", flush=True)
+    bt, num_pages = W.build_block_table(full, wl.seed)
+    pool = binding.Pool(wl.num_layers, num_pages, Hkv, D, fill=np.int16(np.uint16(gu.POISON_NAN).view(np.int16)))
+    btd = torch.from_numpy(bt).cuda()
+    st = gu.status_tensor()
+    T = sum(wl.new)
+    q = W.device_normal_bf16(nl * T * Hq * D, wl.std, W.mix_seed(wl.seed, 70)).view(nl, T, Hq, D)
+    kn = W.device_normal_bf16(nl * T * Hkv * D, wl.std, W.mix_seed(wl.seed, 71)).view(nl, T, Hkv, D)
+    vn = W.device_normal_bf16(nl * T * Hkv * D, wl.std, W.mix_seed(wl.seed, 72)).view(nl, T, Hkv, D)
+    out = torch.empty_like(q)
+    cu = np.concatenate([[0], np.cumsum(wl.new)]).astype(np.int32)
+    binding.extend_layers(pool, lb, q, kn, vn, out, gu.dev_i32(cu), btd, gu.dev_i32(wl.prefix), max(wl.new),
+                          max(full), wl.scale, dev_status=st)
+    gu.sync()
+    assert int(st.item()) == 0
+    picks = sample_sessions(full, 2, wl.seed + 3)
+    rng = np.random.default_rng(wl.seed + 3)
+    for li in range(nl):
+        got = gu.host_f64(out[li])
+        assert np.all(np.isfinite(got))
+        for b in picks[li % 2:li % 2 + 1]:   # one prompt per layer, both prompts over the group
+            C = wl.new[b]
+            rows = {0, 1, C - 1}
+            for r0 in range(0, C, 32):   # a workgroup's 128 rows are 32 tokens at G = 4
+                r1 = min(r0 + 32, C)
+                rows |= {r1 - 1, int(rng.integers(r0, r1))}
+            rows = sorted(rows)
+            kf = host_rows(kn[li, cu[b]:cu[b + 1]])
+            vf = host_rows(vn[li, cu[b]:cu[b + 1]])
+            want = oracle.extend_from_logical(host_rows(q[li, cu[b]:cu[b + 1]]), kf, vf, 0, rows, wl.scale)
+            gs = got[cu[b] + np.array(rows)]
+            err = float(np.max(np.abs(gs - want)))
+            rel = gu.session_rel_err(gs, want)
+            print(f"[fullsize] layer {lb + li} prompt {b}: {len(rows)} tokens, max-abs err {err:.3e}, "
+                  f"session-relative {rel:.4f}", flush=True)
+            assert err <= TOL
+            assert rel <= gu.FULLSIZE_REL
+        b = picks[li % 2]
+        check_tiles(pool, bt, lb + li, b, host_rows(kn[li, cu[b]:cu[b + 1]]), host_rows(vn[li, cu[b]:cu[b + 1]]),
+                    Hkv, D)
+    del pool, q, kn, vn, out
+    torch.cuda.empty_cache()
+
+
 def test_private_decode_full_size_sampled():
     """qwen3_8b_n8_private at full size (64 sessions, 8 decoders, private suffixes up to
     2048 tokens), in the bench's launch configuration; 8 sampled sessions, every
