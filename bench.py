@@ -434,7 +434,7 @@ def private_section(calls):
     def call():
         binding.decode_private(pool, 0, q, out, d_bt, d_lens, d_pbt, d_priv, maxL, maxU, wl.scale, ws)
 
-    for _ in range(5):
+    for _ in range(30):                              # about 25 ms of calls: the clock settles first
         call()
     torch.cuda.synchronize()
     t = EventTimer()
@@ -497,20 +497,26 @@ def cascade_section(calls):
     d_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
     d_gid, d_pref = torch.from_numpy(gid).cuda(), torch.from_numpy(pref).cuda()
 
-    def timed(fn):
-        for _ in range(5):
-            fn()
-        torch.cuda.synchronize()
-        t = EventTimer()
-        for _ in range(calls):
+    def cascade():
+        binding.decode_cascade(pool, 0, q, out, d_bt, d_lens, d_gid, d_pref, maxL, wl.scale, ws)
+
+    def plain():
+        binding.decode(pool, 0, q, out, d_bt, d_lens, maxL, wl.scale, ws)
+
+    # the two entry points alternate, each call between its own events, after a warm-up long
+    # enough (about 25 ms of calls) that the first timed calls run at the settled clock
+    for _ in range(30):
+        cascade()
+        plain()
+    torch.cuda.synchronize()
+    tc, tp = EventTimer(), EventTimer()
+    for _ in range(calls):
+        for fn, t in ((cascade, tc), (plain, tp)):
             e = t.start()
             fn()
             t.stop(e)
-        torch.cuda.synchronize()
-        return float(np.median(t.all_ms()))
-
-    ms_c = timed(lambda: binding.decode_cascade(pool, 0, q, out, d_bt, d_lens, d_gid, d_pref, maxL, wl.scale, ws))
-    ms_p = timed(lambda: binding.decode(pool, 0, q, out, d_bt, d_lens, maxL, wl.scale, ws))
+    torch.cuda.synchronize()
+    ms_c, ms_p = float(np.median(tc.all_ms())), float(np.median(tp.all_ms()))
     # unique KV bytes: every group's prefix once (units of 64 / (N G) = 2 sessions hold whole pairs here)
     uniq_tokens = sum(pre + sum(L - pre for L in ls) for pre, ls in wl.groups)
     nbytes = uniq_tokens * Hkv * D * 4 + 2 * B * N * Hq * D * 2 + 4 * (num_pages + 3 * B)
